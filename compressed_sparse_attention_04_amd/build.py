@@ -1,0 +1,98 @@
+"""Build libcsa.so (the C-ABI library) from the HIP sources in csrc/.
+
+Every .hip file is compiled for gfx950 with hipcc into an object, and the
+objects are linked into one shared library against the HIP runtime that torch
+itself loads, so that a process holding torch tensors and this library runs a
+single HIP runtime (torch's libamdhip64.so carries no SONAME; linking it as
+``-l:libamdhip64.so`` makes the library's dependency resolve to the copy torch
+has already loaded).
+"""
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB_NAME = "libcsa.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+CLANG = os.path.join(ROCM, "llvm", "bin", "clang++")
+
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+    # packed-FP32 VALU ops stay off in every kernel of this library
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-munsafe-fp-atomics",
+]
+
+
+def torch_lib_dir():
+    import importlib.util
+    spec = importlib.util.find_spec("torch")
+    if spec is None or not spec.origin:
+        return None
+    d = os.path.join(os.path.dirname(spec.origin), "lib")
+    return d if os.path.exists(os.path.join(d, "libamdhip64.so")) else None
+
+
+def _compile(src, obj, extra):
+    cmd = [HIPCC] + HIP_FLAGS + ["-I" + INCLUDE, "-I" + CSRC] + extra + ["-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass warns that it does not know the packed-fp32 feature; drop that noise
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    return r.returncode, " ".join(cmd), err
+
+
+def build(verbose=False, extra_flags=None, jobs=None):
+    """Compile every csrc/*.hip and link libcsa.so; returns the library path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    extra = list(extra_flags or [])
+    srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+    if not srcs:
+        raise RuntimeError("no HIP sources found in " + CSRC)
+    objs = []
+    jobs = jobs or min(8, len(srcs))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        futs = {}
+        for s in srcs:
+            obj = os.path.join(BUILD_DIR, s[:-4] + ".o")
+            objs.append(obj)
+            futs[ex.submit(_compile, os.path.join(CSRC, s), obj, extra)] = s
+        failed = []
+        for f in cf.as_completed(futs):
+            rc, cmd, err = f.result()
+            if verbose or rc != 0:
+                print(cmd)
+                if err.strip():
+                    print(err)
+            if rc != 0:
+                failed.append(futs[f])
+    if failed:
+        raise RuntimeError("HIP compile failed: " + ", ".join(sorted(failed)))
+    tdir = torch_lib_dir()
+    link = [CLANG, "-shared", "-fPIC", "-o", LIB_PATH + ".tmp"] + objs
+    if tdir:
+        link += ["-L" + tdir, "-l:libamdhip64.so", "-Wl,-rpath," + tdir]
+    else:
+        link += ["-L" + os.path.join(ROCM, "lib"), "-lamdhip64",
+                 "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    link += ["-Wl,--no-undefined", "-lstdc++"]
+    r = subprocess.run(link, capture_output=True, text=True)
+    if verbose or r.returncode != 0:
+        print(" ".join(link))
+        print(r.stderr)
+    if r.returncode != 0:
+        raise RuntimeError("link failed")
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,401 @@
+// C-ABI entry points of libcsa: host-side validation, workspace layout and
+// launch sequencing.  No entry point allocates, frees or synchronizes; every
+// check runs before the first launch, so an error enqueues nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace csa;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+csa_status fail(csa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+csa_status fail(csa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+csa_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return CSA_OK;
+  return fail(CSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+#define CHECK_PTR(p)                                                                   \
+  do {                                                                                 \
+    if ((p) == nullptr) return fail(CSA_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);    \
+  } while (0)
+#define CHECK_ALIGN(p, a)                                                              \
+  do {                                                                                 \
+    if (!aligned((p), (a)))                                                            \
+      return fail(CSA_ERR_ALIGNMENT, "%s: %s is not %d-byte aligned", fn, #p, (int)(a)); \
+  } while (0)
+#define CHECK(cond, status, ...)                                                       \
+  do {                                                                                 \
+    if (!(cond)) return fail((status), __VA_ARGS__);                                   \
+  } while (0)
+
+// Workspace plan of a layer call: offsets of its scratch buffers.
+struct LayerPlan {
+  int64_t Q = 0, ncols = 0, nblk = 0;
+  size_t off_scores = 0, off_bm = 0, off_sel = 0, off_attn = 0, total = 0;
+  bool pooled = false;
+};
+
+LayerPlan plan_layer(int32_t mode, const csa_layer_args* a) {
+  LayerPlan p;
+  p.Q = a->n_seq * a->q_per_seq;
+  size_t off = 0;
+  if (mode == CSA_MODE_FULL || mode == CSA_MODE_REINDEX) {
+    p.pooled = (mode == CSA_MODE_REINDEX) && a->pool_blocks != nullptr;
+    p.ncols = p.pooled ? (int64_t)CSA_BLOCK * a->n_pool_blocks : a->n_entries;
+    p.off_scores = off;
+    off += round_up((size_t)(p.Q * p.ncols) * sizeof(float));
+    size_t sel = topk_workspace_bytes(p.Q, p.ncols, a->top_k);
+    if (mode == CSA_MODE_FULL && a->build_pool) {
+      p.nblk = (p.ncols + 7) / 8;
+      p.off_bm = off;
+      off += round_up((size_t)(p.Q * p.nblk) * sizeof(float));
+      size_t pool_ws = block_pool_workspace_bytes(p.Q, p.nblk, 1, a->n_pool_blocks);
+      sel = sel > pool_ws ? sel : pool_ws;
+    }
+    p.off_sel = off;
+    off += round_up(sel);
+  }
+  p.off_attn = off;
+  off += round_up(attn_workspace_bytes(p.Q, a->top_k));
+  p.total = off;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa_status_string(csa_status s) {
+  switch (s) {
+    case CSA_OK: return "ok";
+    case CSA_ERR_INVALID_ARG: return "invalid argument";
+    case CSA_ERR_UNSUPPORTED: return "unsupported size";
+    case CSA_ERR_ALIGNMENT: return "misaligned pointer";
+    case CSA_ERR_WORKSPACE: return "workspace too small";
+    case CSA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* csa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t csa_version(void) { return 100; }
+
+// ------------------------------------------------------------------ a2 ----
+csa_status csa_quantize(const float* e, int64_t n, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const char* fn = "csa_quantize";
+  CHECK(n >= 0, CSA_ERR_INVALID_ARG, "%s: n < 0", fn);
+  if (n == 0) return CSA_OK;
+  CHECK_PTR(e); CHECK_PTR(codes); CHECK_PTR(scales);
+  CHECK_ALIGN(e, 16); CHECK_ALIGN(codes, 16); CHECK_ALIGN(scales, 16);
+  return hip_status(launch_quantize(e, n, codes, scales, stream), fn);
+}
+
+csa_status csa_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t n, float* out,
+                          hipStream_t stream) {
+  const char* fn = "csa_dequantize";
+  CHECK(n >= 0, CSA_ERR_INVALID_ARG, "%s: n < 0", fn);
+  if (n == 0) return CSA_OK;
+  CHECK_PTR(codes); CHECK_PTR(scales); CHECK_PTR(out);
+  CHECK_ALIGN(codes, 16); CHECK_ALIGN(scales, 16); CHECK_ALIGN(out, 16);
+  return hip_status(launch_dequantize(codes, scales, n, out, stream), fn);
+}
+
+// ------------------------------------------------------------- a1 + a2 ----
+size_t csa_compress_quant_workspace_size(int64_t n_entries) {
+  return n_entries <= 0 ? 0 : compress_workspace_bytes(n_entries);
+}
+
+csa_status csa_compress_quant(const float* x, int64_t n_seq, int64_t n_per_seq, int64_t x_seq_stride,
+                              const float* w, const float* rope_cs, int32_t rope_dim, float eps,
+                              uint8_t* codes, uint8_t* scales, int64_t out_seq_stride, float* e_out,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "csa_compress_quant";
+  CHECK(n_seq >= 0 && n_per_seq >= 0, CSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  int64_t n = n_seq * n_per_seq;
+  if (n == 0) return CSA_OK;
+  CHECK_PTR(x); CHECK_PTR(w); CHECK_PTR(codes); CHECK_PTR(scales);
+  CHECK(rope_dim >= 0 && rope_dim <= D && rope_dim % 2 == 0, CSA_ERR_UNSUPPORTED,
+        "%s: rope_dim must be even and in [0, 512] (got %d)", fn, rope_dim);
+  CHECK(rope_dim == 0 || rope_cs != nullptr, CSA_ERR_INVALID_ARG, "%s: rope_cs is NULL", fn);
+  CHECK(std::isfinite(eps) && eps >= 0.f, CSA_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+  CHECK(n_seq == 1 || x_seq_stride >= n_per_seq * 4 * D, CSA_ERR_INVALID_ARG,
+        "%s: x_seq_stride overlaps the previous sequence", fn);
+  CHECK(x_seq_stride % 4 == 0, CSA_ERR_ALIGNMENT, "%s: x_seq_stride must be a multiple of 4", fn);
+  CHECK(n_seq == 1 || out_seq_stride >= n_per_seq, CSA_ERR_INVALID_ARG,
+        "%s: out_seq_stride must be >= n_per_seq", fn);
+  CHECK_ALIGN(x, 16); CHECK_ALIGN(w, 16); CHECK_ALIGN(codes, 16); CHECK_ALIGN(scales, 16);
+  if (rope_cs) CHECK_ALIGN(rope_cs, 4);
+  if (e_out) CHECK_ALIGN(e_out, 16);
+  size_t need = compress_workspace_bytes(n);
+  CHECK(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  CHECK_ALIGN(ws, 16);
+  return hip_status(launch_compress_quant(x, n_seq, n_per_seq, x_seq_stride, w, rope_cs, rope_dim, eps,
+                                          codes, scales, out_seq_stride, e_out, ws, stream), fn);
+}
+
+// ------------------------------------------------------------------ a9 ----
+csa_status csa_window_append(const float* x, int64_t n_seq, int64_t n_tok, int64_t x_seq_stride,
+                             const int32_t* pos0, uint8_t* win, int64_t win_cap, hipStream_t stream) {
+  const char* fn = "csa_window_append";
+  CHECK(n_seq >= 0 && n_tok >= 0, CSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (n_seq * n_tok == 0) return CSA_OK;
+  CHECK_PTR(x); CHECK_PTR(pos0); CHECK_PTR(win);
+  CHECK(win_cap >= NWIN, CSA_ERR_UNSUPPORTED, "%s: win_cap must be >= 128", fn);
+  CHECK(n_tok <= win_cap, CSA_ERR_INVALID_ARG, "%s: n_tok exceeds win_cap", fn);
+  CHECK(x_seq_stride % 4 == 0, CSA_ERR_ALIGNMENT, "%s: x_seq_stride must be a multiple of 4", fn);
+  CHECK(n_seq == 1 || x_seq_stride >= n_tok * D, CSA_ERR_INVALID_ARG, "%s: x_seq_stride too small", fn);
+  CHECK_ALIGN(x, 16); CHECK_ALIGN(pos0, 4); CHECK_ALIGN(win, 16);
+  return hip_status(launch_window_append(x, n_seq, n_tok, x_seq_stride, pos0, win, win_cap, stream), fn);
+}
+
+// ------------------------------------------------------------------ a3 ----
+static csa_status check_score(const char* fn, const ScoreArgs& s) {
+  CHECK(s.n_seq >= 0 && s.q_per_seq >= 0, CSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  CHECK_PTR(s.q_fp8); CHECK_PTR(s.w); CHECK_PTR(s.q_pos); CHECK_PTR(s.k_fp8);
+  CHECK(s.n_entries >= 0 && s.n_entries <= s.k_rows, CSA_ERR_INVALID_ARG,
+        "%s: need 0 <= n_entries <= k_rows (%lld, %lld)", fn, (long long)s.n_entries, (long long)s.k_rows);
+  CHECK(s.n_entries < (int64_t)1 << 30, CSA_ERR_UNSUPPORTED, "%s: n_entries too large", fn);
+  if (s.pool) {
+    CHECK(s.n_pool_blocks >= 1 && s.n_pool_blocks <= 65536, CSA_ERR_UNSUPPORTED,
+          "%s: n_pool_blocks out of range", fn);
+    CHECK(s.block_max == nullptr, CSA_ERR_INVALID_ARG, "%s: block_max is for dense mode only", fn);
+    CHECK_ALIGN(s.pool, 4);
+  }
+  CHECK(s.scores != nullptr || s.block_max != nullptr, CSA_ERR_INVALID_ARG,
+        "%s: scores and block_max are both NULL", fn);
+  CHECK_ALIGN(s.q_fp8, 16); CHECK_ALIGN(s.k_fp8, 16); CHECK_ALIGN(s.w, 4); CHECK_ALIGN(s.q_pos, 4);
+  if (s.scores) CHECK_ALIGN(s.scores, 4);
+  if (s.block_max) CHECK_ALIGN(s.block_max, 4);
+  return CSA_OK;
+}
+
+csa_status csa_index_score(const uint8_t* q_fp8, const float* w, const int32_t* q_pos, int64_t n_seq,
+                           int64_t q_per_seq, const uint8_t* k_fp8, int64_t k_seq_stride,
+                           int64_t n_entries, const int32_t* pool_blocks, int32_t n_pool_blocks,
+                           float* scores, float* block_max, hipStream_t stream) {
+  const char* fn = "csa_index_score";
+  ScoreArgs s{q_fp8, w, q_pos, n_seq, q_per_seq, k_fp8, k_seq_stride, n_entries, pool_blocks,
+              n_pool_blocks, scores, block_max};
+  if (n_seq * q_per_seq == 0 && n_seq >= 0 && q_per_seq >= 0) return CSA_OK;
+  csa_status st = check_score(fn, s);
+  if (st != CSA_OK) return st;
+  return hip_status(launch_index_score(s, stream), fn);
+}
+
+// ------------------------------------------------------------------ a4 ----
+size_t csa_topk_workspace_size(int64_t Q, int64_t ncols, int32_t k) {
+  if (Q <= 0 || ncols <= 0 || k <= 0) return 0;
+  return topk_workspace_bytes(Q, ncols, k);
+}
+
+csa_status csa_topk(const float* scores, int64_t Q, int64_t ncols, const int32_t* col_blocks, int32_t k,
+                    int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "csa_topk";
+  CHECK(Q >= 0, CSA_ERR_INVALID_ARG, "%s: Q < 0", fn);
+  if (Q == 0) return CSA_OK;
+  CHECK(ncols >= 1 && ncols < ((int64_t)1 << 31), CSA_ERR_UNSUPPORTED, "%s: ncols out of range", fn);
+  CHECK(k >= 1 && k <= 4096, CSA_ERR_UNSUPPORTED, "%s: k must be in [1, 4096]", fn);
+  CHECK(col_blocks == nullptr || ncols % 8 == 0, CSA_ERR_INVALID_ARG,
+        "%s: pooled columns must be a multiple of 8", fn);
+  CHECK_PTR(scores); CHECK_PTR(idx);
+  CHECK_ALIGN(scores, 4); CHECK_ALIGN(idx, 4);
+  if (col_blocks) CHECK_ALIGN(col_blocks, 4);
+  size_t need = topk_workspace_bytes(Q, ncols, k);
+  CHECK(need == 0 || (ws != nullptr && ws_bytes >= need), CSA_ERR_WORKSPACE,
+        "%s: workspace needs %zu bytes", fn, need);
+  if (need) CHECK_ALIGN(ws, 16);
+  return hip_status(launch_topk(scores, Q, ncols, col_blocks, k, idx, ws, stream), fn);
+}
+
+// ------------------------------------------------------------------ a5 ----
+size_t csa_block_pool_workspace_size(int64_t Q, int64_t ncols, int32_t is_block_max, int32_t nb) {
+  if (Q <= 0 || ncols <= 0 || nb <= 0) return 0;
+  return block_pool_workspace_bytes(Q, ncols, is_block_max, nb);
+}
+
+csa_status csa_block_pool(const float* values, int32_t is_block_max, int64_t Q, int64_t ncols,
+                          int32_t n_pool_blocks, int32_t* pool_blocks, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  const char* fn = "csa_block_pool";
+  CHECK(Q >= 0, CSA_ERR_INVALID_ARG, "%s: Q < 0", fn);
+  if (Q == 0) return CSA_OK;
+  CHECK(is_block_max == 0 || is_block_max == 1, CSA_ERR_INVALID_ARG, "%s: is_block_max must be 0 or 1", fn);
+  CHECK(ncols >= 1 && ncols < ((int64_t)1 << 31), CSA_ERR_UNSUPPORTED, "%s: ncols out of range", fn);
+  CHECK(n_pool_blocks >= 1 && n_pool_blocks <= 4096, CSA_ERR_UNSUPPORTED,
+        "%s: n_pool_blocks must be in [1, 4096]", fn);
+  CHECK_PTR(values); CHECK_PTR(pool_blocks);
+  CHECK_ALIGN(values, 4); CHECK_ALIGN(pool_blocks, 4);
+  size_t need = block_pool_workspace_bytes(Q, ncols, is_block_max, n_pool_blocks);
+  CHECK(need == 0 || (ws != nullptr && ws_bytes >= need), CSA_ERR_WORKSPACE,
+        "%s: workspace needs %zu bytes", fn, need);
+  if (need) CHECK_ALIGN(ws, 256);
+  return hip_status(launch_block_pool(values, is_block_max, Q, ncols, n_pool_blocks, pool_blocks, ws, stream),
+                    fn);
+}
+
+// ------------------------------------------------------------------ a7 ----
+size_t csa_sparse_attn_workspace_size(int64_t Q, int32_t k) {
+  if (Q <= 0 || k <= 0) return 0;
+  return attn_workspace_bytes(Q, k);
+}
+
+static csa_status check_attn(const char* fn, const float* q, const int32_t* q_pos, int64_t n_seq,
+                             int64_t q_per_seq, const uint8_t* codes, const uint8_t* scales,
+                             int64_t kv_rows, const int32_t* idx, int32_t k, const uint8_t* win,
+                             int64_t win_cap, float sm_scale, float* out, void* ws, size_t ws_bytes) {
+  CHECK(n_seq >= 0 && q_per_seq >= 0, CSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  CHECK(k >= 1 && k <= 4096, CSA_ERR_UNSUPPORTED, "%s: k must be in [1, 4096]", fn);
+  CHECK(kv_rows >= 0 && kv_rows < ((int64_t)1 << 31), CSA_ERR_UNSUPPORTED, "%s: kv_rows out of range", fn);
+  CHECK(win_cap >= NWIN, CSA_ERR_UNSUPPORTED, "%s: win_cap must be >= 128", fn);
+  CHECK(std::isfinite(sm_scale), CSA_ERR_INVALID_ARG, "%s: sm_scale must be finite", fn);
+  CHECK_PTR(q); CHECK_PTR(q_pos); CHECK_PTR(codes); CHECK_PTR(scales); CHECK_PTR(idx);
+  CHECK_PTR(win); CHECK_PTR(out);
+  CHECK_ALIGN(q, 16); CHECK_ALIGN(q_pos, 4); CHECK_ALIGN(codes, 16); CHECK_ALIGN(scales, 16);
+  CHECK_ALIGN(idx, 4); CHECK_ALIGN(win, 16); CHECK_ALIGN(out, 16);
+  size_t need = attn_workspace_bytes(n_seq * q_per_seq, k);
+  CHECK(need == 0 || (ws != nullptr && ws_bytes >= need), CSA_ERR_WORKSPACE,
+        "%s: workspace needs %zu bytes", fn, need);
+  if (need) CHECK_ALIGN(ws, 16);
+  return CSA_OK;
+}
+
+csa_status csa_sparse_attn(const float* q, const int32_t* q_pos, int64_t n_seq, int64_t q_per_seq,
+                           const uint8_t* codes, const uint8_t* scales, int64_t kv_rows, const int32_t* idx,
+                           int32_t k, const uint8_t* win, int64_t win_cap, float sm_scale, float* out,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "csa_sparse_attn";
+  if (n_seq * q_per_seq == 0 && n_seq >= 0 && q_per_seq >= 0) return CSA_OK;
+  csa_status st = check_attn(fn, q, q_pos, n_seq, q_per_seq, codes, scales, kv_rows, idx, k, win, win_cap,
+                             sm_scale, out, ws, ws_bytes);
+  if (st != CSA_OK) return st;
+  return hip_status(launch_sparse_attn(q, q_pos, n_seq, q_per_seq, codes, scales, kv_rows, idx, k, win,
+                                       win_cap, sm_scale, out, ws, stream),
+                    fn);
+}
+
+// ------------------------------------------------------------- a6 + a8 ----
+size_t csa_layer_workspace_size(int32_t mode, const csa_layer_args* a) {
+  if (a == nullptr || mode < CSA_MODE_FULL || mode > CSA_MODE_REUSE) return 0;
+  return plan_layer(mode, a).total;
+}
+
+static csa_status check_layer(const char* fn, int32_t mode, const csa_layer_args* a, LayerPlan* plan) {
+  CHECK(a != nullptr, CSA_ERR_INVALID_ARG, "%s: args is NULL", fn);
+  CHECK(a->n_seq >= 0 && a->q_per_seq >= 0, CSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  CHECK(a->top_k >= 1 && a->top_k <= 4096, CSA_ERR_UNSUPPORTED, "%s: top_k must be in [1, 4096]", fn);
+  CHECK(a->n_entries >= 0 && a->n_entries <= a->kv_rows, CSA_ERR_INVALID_ARG,
+        "%s: n_entries must be <= kv_rows", fn);
+  CHECK_PTR(a->idx); CHECK_PTR(a->out);
+  if (mode != CSA_MODE_REUSE) {
+    CHECK_PTR(a->q_idx); CHECK_PTR(a->w_idx); CHECK_PTR(a->k_fp8);
+    CHECK(a->n_entries <= a->k_rows, CSA_ERR_INVALID_ARG, "%s: n_entries must be <= k_rows", fn);
+    CHECK(a->n_entries >= 1, CSA_ERR_INVALID_ARG, "%s: n_entries must be >= 1", fn);
+  }
+  bool uses_pool = (mode == CSA_MODE_FULL && a->build_pool) || (mode == CSA_MODE_REINDEX && a->pool_blocks);
+  if (mode == CSA_MODE_FULL && a->build_pool) CHECK_PTR(a->pool_blocks);
+  if (uses_pool) {
+    CHECK(a->n_pool_blocks >= 1 && a->n_pool_blocks <= 4096, CSA_ERR_UNSUPPORTED,
+          "%s: n_pool_blocks must be in [1, 4096]", fn);
+    CHECK_ALIGN(a->pool_blocks, 4);
+  }
+  *plan = plan_layer(mode, a);
+  CHECK(plan->total == 0 || (a->ws != nullptr && a->ws_bytes >= plan->total), CSA_ERR_WORKSPACE,
+        "%s: workspace needs %zu bytes", fn, plan->total);
+  if (plan->total) CHECK_ALIGN(a->ws, 256);
+  if (mode != CSA_MODE_REUSE && plan->Q > 0) {
+    ScoreArgs s{a->q_idx, a->w_idx, a->q_pos, a->n_seq, a->q_per_seq, a->k_fp8, a->k_rows, a->n_entries,
+                plan->pooled ? a->pool_blocks : nullptr, a->n_pool_blocks, reinterpret_cast<float*>(1),
+                nullptr};
+    csa_status st = check_score(fn, s);
+    if (st != CSA_OK) return st;
+  }
+  if (plan->Q > 0) {
+    void* aws = reinterpret_cast<char*>(a->ws) + plan->off_attn;
+    csa_status st = check_attn(fn, a->q_attn, a->q_pos, a->n_seq, a->q_per_seq, a->codes, a->scales,
+                               a->kv_rows, a->idx, a->top_k, a->win, a->win_cap, a->sm_scale, a->out,
+                               plan->total ? aws : nullptr, plan->total ? plan->total - plan->off_attn : 0);
+    if (st != CSA_OK) return st;
+  }
+  return CSA_OK;
+}
+
+static csa_status run_attention(const char* fn, const csa_layer_args* a, const LayerPlan& p, hipStream_t st) {
+  void* aws = reinterpret_cast<char*>(a->ws) + p.off_attn;
+  return hip_status(launch_sparse_attn(a->q_attn, a->q_pos, a->n_seq, a->q_per_seq, a->codes, a->scales,
+                                       a->kv_rows, a->idx, a->top_k, a->win, a->win_cap, a->sm_scale,
+                                       a->out, aws, st),
+                    fn);
+}
+
+static csa_status run_index(const char* fn, int32_t mode, const csa_layer_args* a, const LayerPlan& p,
+                            hipStream_t st) {
+  char* ws = reinterpret_cast<char*>(a->ws);
+  float* scores = reinterpret_cast<float*>(ws + p.off_scores);
+  float* bm = (mode == CSA_MODE_FULL && a->build_pool) ? reinterpret_cast<float*>(ws + p.off_bm) : nullptr;
+  ScoreArgs s{a->q_idx, a->w_idx, a->q_pos, a->n_seq, a->q_per_seq, a->k_fp8, a->k_rows, a->n_entries,
+              p.pooled ? a->pool_blocks : nullptr, a->n_pool_blocks, scores, bm};
+  csa_status r = hip_status(launch_index_score(s, st), fn);
+  if (r != CSA_OK) return r;
+  r = hip_status(launch_topk(scores, p.Q, p.ncols, p.pooled ? a->pool_blocks : nullptr, a->top_k, a->idx,
+                             ws + p.off_sel, st),
+                 fn);
+  if (r != CSA_OK) return r;
+  if (bm) {
+    r = hip_status(launch_block_pool(bm, 1, p.Q, p.nblk, a->n_pool_blocks, a->pool_blocks, ws + p.off_sel, st),
+                   fn);
+  }
+  return r;
+}
+
+csa_status csa_layer_full(const csa_layer_args* a, hipStream_t stream) {
+  const char* fn = "csa_layer_full";
+  LayerPlan p;
+  csa_status st = check_layer(fn, CSA_MODE_FULL, a, &p);
+  if (st != CSA_OK || p.Q == 0) return st;
+  st = run_index(fn, CSA_MODE_FULL, a, p, stream);
+  if (st != CSA_OK) return st;
+  return run_attention(fn, a, p, stream);
+}
+
+csa_status csa_layer_reindex(const csa_layer_args* a, hipStream_t stream) {
+  const char* fn = "csa_layer_reindex";
+  LayerPlan p;
+  csa_status st = check_layer(fn, CSA_MODE_REINDEX, a, &p);
+  if (st != CSA_OK || p.Q == 0) return st;
+  st = run_index(fn, CSA_MODE_REINDEX, a, p, stream);
+  if (st != CSA_OK) return st;
+  return run_attention(fn, a, p, stream);
+}
+
+csa_status csa_layer_reuse(const csa_layer_args* a, hipStream_t stream) {
+  const char* fn = "csa_layer_reuse";
+  LayerPlan p;
+  csa_status st = check_layer(fn, CSA_MODE_REUSE, a, &p);
+  if (st != CSA_OK || p.Q == 0) return st;
+  return run_attention(fn, a, p, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,290 @@
+// MXFP4 store path: quantize / dequantize, window append, and the fused
+// compress (4 tokens -> 1 entry) + RMSNorm + RoPE + quantize chain.
+//
+// P3 §02 (sequence compression), P2 §2.1 (4:1), P3 §03 (E2M1 values with an
+// E4M3 scale per 16 channels, RMSNorm before, quantize after RoPE; SWA KV in
+// FP8).
+#include "common.h"
+#include "kernels.h"
+
+namespace csa {
+
+// ---------------------------------------------------------------------------
+// Quantize: 16 lanes per entry, 32 channels (two scale groups) per lane.
+// Each lane stores its 16 code bytes with one 16-byte store (an entry's 256
+// code bytes are one contiguous 256-byte run) and its two scale bytes.
+__device__ __forceinline__ void quantize32_store(const float* v, uint8_t* codes_row,
+                                                 uint8_t* scales_row, int lane16) {
+  uint32_t c0[2], c1[2];
+  uint32_t s0 = mxfp4_group(v, c0);
+  uint32_t s1 = mxfp4_group(v + 16, c1);
+  uint4 cw = make_uint4(c0[0], c0[1], c1[0], c1[1]);
+  *reinterpret_cast<uint4*>(codes_row + 16 * lane16) = cw;
+  *reinterpret_cast<uint16_t*>(scales_row + 2 * lane16) = (uint16_t)(s0 | (s1 << 8));
+}
+
+__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ e, int64_t n,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales) {
+  int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t entry = t >> 4;
+  int lane16 = (int)(t & 15);
+  if (entry >= n) return;
+  const float4* src = reinterpret_cast<const float4*>(e + entry * D + 32 * lane16);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float4 f = src[i];
+    v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+  }
+  quantize32_store(v, codes + entry * CODE_BYTES, scales + entry * SCALE_BYTES, lane16);
+}
+
+__global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restrict__ codes,
+                                                         const uint8_t* __restrict__ scales,
+                                                         int64_t n, float* __restrict__ out) {
+  int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t entry = t >> 4;
+  int lane16 = (int)(t & 15);
+  if (entry >= n) return;
+  uint4 cw = *reinterpret_cast<const uint4*>(codes + entry * CODE_BYTES + 16 * lane16);
+  uint16_t sw = *reinterpret_cast<const uint16_t*>(scales + entry * SCALE_BYTES + 2 * lane16);
+  float s0 = e4m3_code_value(sw & 0x7Fu), s1 = e4m3_code_value((sw >> 8) & 0x7Fu);
+  uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+  float4* dst = reinterpret_cast<float4*>(out + entry * D + 32 * lane16);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float s = i < 4 ? s0 : s1;
+    uint32_t word = w[i >> 1] >> (16 * (i & 1));
+    float f[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t c = (word >> (4 * j)) & 0xFu;
+      float m = e2m1_value(c) * s;
+      f[j] = (c & 8u) ? -m : m;
+    }
+    dst[i] = make_float4(f[0], f[1], f[2], f[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Window append: 32 lanes per token, 16 channels per lane, one 16-byte store.
+__global__ __launch_bounds__(256) void window_append_kernel(const float* __restrict__ x,
+                                                            int64_t n_seq, int64_t n_tok,
+                                                            int64_t x_seq_stride,
+                                                            const int32_t* __restrict__ pos0,
+                                                            uint8_t* __restrict__ win,
+                                                            int64_t win_cap) {
+  int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t tok = t >> 5;
+  int lane = (int)(t & 31);
+  if (tok >= n_seq * n_tok) return;
+  int64_t s = tok / n_tok, i = tok % n_tok;
+  int64_t p = (int64_t)pos0[s] + i;
+  if (p < 0) return;
+  const float4* src = reinterpret_cast<const float4*>(x + s * x_seq_stride + i * D + 16 * lane);
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float4 f = src[k];
+    w[k] = e4m3_encode(f.x) | (e4m3_encode(f.y) << 8) | (e4m3_encode(f.z) << 16) |
+           (e4m3_encode(f.w) << 24);
+  }
+  uint8_t* dst = win + (s * win_cap + p % win_cap) * D + 16 * lane;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Compression GEMM on the fp32 matrix cores: Y[i, o] = sum_k Xc[i, k] Wc[o, k]
+// with Xc[i] = the 4 token rows of entry i (2048 contiguous floats) and
+// Wc[o, i*512 + c] = W_i[o, c].  Tile 32 entries x 64 outputs, k-chunks of 32;
+// optional split-K over blockIdx.z writes partial sums to ypart[z].
+constexpr int CG_BM = 32, CG_BN = 64, CG_BK = 32, CG_PITCH = CG_BK + 1;
+
+__global__ __launch_bounds__(256) void compress_gemm_kernel(const float* __restrict__ x,
+                                                            int64_t n_seq, int64_t n_per_seq,
+                                                            int64_t x_seq_stride,
+                                                            const float* __restrict__ w,
+                                                            float* __restrict__ ypart,
+                                                            int k_per_split) {
+  __shared__ float As[CG_BM][CG_PITCH];
+  __shared__ float Bs[CG_BN][CG_PITCH];
+  const int64_t n = n_seq * n_per_seq;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int o0 = blockIdx.x * CG_BN;
+  const int64_t r0 = (int64_t)blockIdx.y * CG_BM;
+  const int kbeg = blockIdx.z * k_per_split;
+  const int kend = kbeg + k_per_split;
+  // A loads: one float4 per thread (32 rows x 8 float4)
+  const int a_row = tid >> 3, a_k4 = (tid & 7) * 4;
+  const int64_t a_entry = r0 + a_row;
+  const float* a_src = nullptr;
+  if (a_entry < n) {
+    int64_t s = a_entry / n_per_seq, r = a_entry % n_per_seq;
+    a_src = x + s * x_seq_stride + r * (4 * D);
+  }
+  const int wr = (wave >> 1) * 16;          // wave's row offset in the tile
+  const int wc = (wave & 1) * 32;           // wave's column offset
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = kbeg; k0 < kend; k0 += CG_BK) {
+    float4 av = a_src ? *reinterpret_cast<const float4*>(a_src + k0 + a_k4)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int ti = k0 / D, c0 = k0 % D;     // token slot and channel of this chunk
+    float4 bv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      int idx = tid + 256 * u;
+      int row = idx >> 3, k4 = (idx & 7) * 4;
+      bv[u] = *reinterpret_cast<const float4*>(w + (int64_t)ti * D * D + (int64_t)(o0 + row) * D +
+                                               c0 + k4);
+    }
+    __syncthreads();
+    As[a_row][a_k4] = av.x; As[a_row][a_k4 + 1] = av.y;
+    As[a_row][a_k4 + 2] = av.z; As[a_row][a_k4 + 3] = av.w;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      int idx = tid + 256 * u;
+      int row = idx >> 3, k4 = (idx & 7) * 4;
+      Bs[row][k4] = bv[u].x; Bs[row][k4 + 1] = bv[u].y;
+      Bs[row][k4 + 2] = bv[u].z; Bs[row][k4 + 3] = bv[u].w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < CG_BK; kk += 4) {
+      float a = As[wr + (lane & 15)][kk + (lane >> 4)];
+      float b0 = Bs[wc + (lane & 15)][kk + (lane >> 4)];
+      float b1 = Bs[wc + 16 + (lane & 15)][kk + (lane >> 4)];
+      acc0 = mfma_f32_16x16x4(a, b0, acc0);
+      acc1 = mfma_f32_16x16x4(a, b1, acc1);
+    }
+  }
+  float* yp = ypart + (int64_t)blockIdx.z * n * D;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    int64_t row = r0 + wr + 4 * (lane >> 4) + r;
+    if (row < n) {
+      yp[row * D + o0 + wc + (lane & 15)] = acc0[r];
+      yp[row * D + o0 + wc + 16 + (lane & 15)] = acc1[r];
+    }
+  }
+}
+
+// RMSNorm + RoPE + quantize + packed store.  16 lanes per entry (32 channels
+// per lane), 16 entries per 256-thread block.  Sums the split-K partials in a
+// fixed order.
+__global__ __launch_bounds__(256) void compress_epilogue_kernel(
+    const float* __restrict__ ypart, int n_split, int64_t n_seq, int64_t n_per_seq,
+    const float* __restrict__ rope_cs, int rope_dim, float eps, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, int64_t out_seq_stride, float* __restrict__ e_out) {
+  const int64_t n = n_seq * n_per_seq;
+  int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t entry = t >> 4;
+  int lane16 = (int)(t & 15);
+  bool live = entry < n;
+  int64_t ent = live ? entry : 0;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = 0.f;
+  for (int z = 0; z < n_split; ++z) {
+    const float4* src = reinterpret_cast<const float4*>(ypart + ((int64_t)z * n + ent) * D + 32 * lane16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float4 f = src[i];
+      v[4 * i] += f.x; v[4 * i + 1] += f.y; v[4 * i + 2] += f.z; v[4 * i + 3] += f.w;
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) ss = fmaf(v[i], v[i], ss);
+  // reduce over the 16 lanes of this entry
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 16);
+  float inv = 1.0f / sqrtf(ss * (1.0f / (float)D) + eps);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] *= inv;
+  const int c_lane = 32 * lane16;
+  const int c0 = D - rope_dim;
+  if (rope_dim > 0 && c_lane + 32 > c0) {
+    const float* cs = rope_cs + ent * (int64_t)rope_dim;   // [rope_dim/2][2]
+#pragma unroll
+    for (int i = 0; i < 32; i += 2) {
+      int c = c_lane + i;
+      if (c >= c0) {
+        int pi = (c - c0) >> 1;
+        float cs_c = cs[2 * pi], cs_s = cs[2 * pi + 1];
+        float x0 = v[i], x1 = v[i + 1];
+        v[i] = x0 * cs_c - x1 * cs_s;
+        v[i + 1] = x0 * cs_s + x1 * cs_c;
+      }
+    }
+  }
+  if (!live) return;
+  if (e_out) {
+    float4* dst = reinterpret_cast<float4*>(e_out + entry * D + c_lane);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  }
+  int64_t s = entry / n_per_seq, r = entry % n_per_seq;
+  int64_t row = s * out_seq_stride + r;
+  quantize32_store(v, codes + row * CODE_BYTES, scales + row * SCALE_BYTES, lane16);
+}
+
+// ------------------------------------------------------------- launchers --
+hipError_t launch_quantize(const float* e, int64_t n, uint8_t* codes, uint8_t* scales,
+                           hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n * 16 + 255) / 256;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, e, n, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t n, float* out,
+                             hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n * 16 + 255) / 256;
+  hipLaunchKernelGGL(dequantize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, codes, scales, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_append(const float* x, int64_t n_seq, int64_t n_tok, int64_t x_seq_stride,
+                                const int32_t* pos0, uint8_t* win, int64_t win_cap, hipStream_t st) {
+  int64_t tokens = n_seq * n_tok;
+  if (tokens == 0) return hipSuccess;
+  int64_t blocks = (tokens * 32 + 255) / 256;
+  hipLaunchKernelGGL(window_append_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, n_seq, n_tok,
+                     x_seq_stride, pos0, win, win_cap);
+  return hipGetLastError();
+}
+
+int compress_split_k(int64_t n) {
+  int64_t tiles = (int64_t)(D / CG_BN) * ((n + CG_BM - 1) / CG_BM);
+  int split = 1;
+  // spread small batches over more blocks: K = 2048 split into up to 16 parts
+  while (split < 16 && tiles * split < 512) split *= 2;
+  return split;
+}
+
+size_t compress_workspace_bytes(int64_t n) {
+  return (size_t)compress_split_k(n) * (size_t)n * D * sizeof(float);
+}
+
+hipError_t launch_compress_quant(const float* x, int64_t n_seq, int64_t n_per_seq,
+                                 int64_t x_seq_stride, const float* w, const float* rope_cs,
+                                 int rope_dim, float eps, uint8_t* codes, uint8_t* scales,
+                                 int64_t out_seq_stride, float* e_out, void* ws, hipStream_t st) {
+  int64_t n = n_seq * n_per_seq;
+  if (n == 0) return hipSuccess;
+  int split = compress_split_k(n);
+  float* ypart = reinterpret_cast<float*>(ws);
+  dim3 grid(D / CG_BN, (unsigned)((n + CG_BM - 1) / CG_BM), split);
+  hipLaunchKernelGGL(compress_gemm_kernel, grid, dim3(256), 0, st, x, n_seq, n_per_seq, x_seq_stride,
+                     w, ypart, (4 * D) / split);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int64_t blocks = (n * 16 + 255) / 256;
+  hipLaunchKernelGGL(compress_epilogue_kernel, dim3((unsigned)blocks), dim3(256), 0, st, ypart, split,
+                     n_seq, n_per_seq, rope_cs, rope_dim, eps, codes, scales, out_seq_stride, e_out);
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,129 @@
+"""One CSA2 layer-group step driven through the C ABI.
+
+A step, in order (P3 §02 layer modes; P3 §03 window / MXFP4 store):
+  1. append the step's tokens to the FP8 window ring (a9);
+  2. compress + RoPE + MXFP4-store the entries the step's tokens complete (a1, a2);
+  3. run the layer group: Full (score, Top-K, optional pool), then Reuse and
+     Reindex layers in their static order (a3..a8).
+``setup()`` fills the state that exists before the step (prior entries when
+they are built from token latents, and the 127 window tokens before the
+step's first token); it is not part of the timed work.
+"""
+
+import math
+
+import torch
+
+from . import ops
+from .ops import D, HEADS, LayerCall, MODE_FULL, MODE_REINDEX, MODE_REUSE
+
+M = 4
+N_WIN = 128
+
+
+class LayerStep:
+    """State and prepared calls of one step.
+
+    kind: "decode" (one query per sequence at position q_pos, the last token)
+    or "prefill" (q_per_seq queries at consecutive positions).
+    x_tail: float32 [S, 127 + n_step, 512] -- the 127 tokens before the step
+    and the step's n_step tokens.  The last 4 * new_entries rows of x_tail are
+    compressed into entries prior_entries .. prior_entries + new_entries - 1.
+    """
+
+    def __init__(self, *, kind, layers, build_pool, x_tail, w, rope_cs, codes, scales, k_fp8, q_pos,
+                 q_attn, q_fp8, w_idx, prior_entries, new_entries, first_pos, x_prior=None,
+                 rope_prior=None, top_k=ops.TOP_K, n_pool_blocks=ops.POOL_BLOCKS, rope_dim=64,
+                 eps=1e-6):
+        dev = codes.device
+        S, cap = codes.shape[0], codes.shape[1]
+        self.kind, self.layers = kind, list(layers)
+        self.S, self.cap = S, cap
+        self.n_step = x_tail.shape[1] - (N_WIN - 1)
+        self.q_per_seq = 1 if kind == "decode" else self.n_step
+        self.Q = S * self.q_per_seq
+        self.prior, self.new = prior_entries, new_entries
+        self.x_tail, self.w, self.rope_cs = x_tail, w, rope_cs
+        self.x_prior, self.rope_prior = x_prior, rope_prior
+        self.codes, self.scales, self.k_fp8 = codes, scales, k_fp8
+        self.rope_dim, self.eps = rope_dim, eps
+        self.win_cap = N_WIN if kind == "decode" else self.n_step + N_WIN
+        self.win = torch.zeros((S, self.win_cap, D), dtype=torch.uint8, device=dev)
+        # position of x_tail row 0 of every sequence
+        self.pos_tail = first_pos.to(torch.int32).contiguous()
+        self.pos_step = (first_pos + (N_WIN - 1)).to(torch.int32).contiguous()
+        self.n_entries = prior_entries + new_entries
+        self.outs, self.idxs, self.calls = [], [], []
+        self.pool = None
+        if build_pool:
+            self.pool = torch.empty((self.Q, n_pool_blocks), dtype=torch.int32, device=dev)
+        idx_latest = None
+        for li, mode in enumerate(self.layers):
+            out = torch.empty((self.Q, HEADS, D), dtype=torch.float32, device=dev)
+            common = dict(codes=codes, scales=scales, k_fp8=k_fp8, win=self.win, q_pos=q_pos,
+                          q_attn=q_attn[li], out=out, n_seq=S, q_per_seq=self.q_per_seq,
+                          n_entries=self.n_entries, top_k=top_k, n_pool_blocks=n_pool_blocks,
+                          alloc_ws=False)
+            if mode == "F":
+                idx = torch.empty((self.Q, top_k), dtype=torch.int32, device=dev)
+                call = LayerCall(MODE_FULL, idx=idx, q_idx=q_fp8[li], w_idx=w_idx[li],
+                                 pool_blocks=self.pool, build_pool=build_pool, **common)
+                idx_latest = idx
+            elif mode == "I":
+                idx = torch.empty((self.Q, top_k), dtype=torch.int32, device=dev)
+                call = LayerCall(MODE_REINDEX, idx=idx, q_idx=q_fp8[li], w_idx=w_idx[li],
+                                 pool_blocks=self.pool, **common)
+                idx_latest = idx
+            elif mode == "U":
+                if idx_latest is None:
+                    raise ValueError("a Reuse layer needs an earlier Full or Reindex layer")
+                idx = idx_latest
+                call = LayerCall(MODE_REUSE, idx=idx, **common)
+            else:
+                raise ValueError(f"unknown layer mode {mode!r}")
+            self.outs.append(out)
+            self.idxs.append(idx)
+            self.calls.append(call)
+        # every call runs on the same stream in order, so one workspace serves all
+        big = max((c.ws_need for c in self.calls), default=0)
+        self.ws = torch.empty(big, dtype=torch.uint8, device=dev) if big else None
+        for c in self.calls:
+            c.set_workspace(self.ws)
+
+    def setup(self):
+        """Untimed: prior entries (from token latents) and the first 127 window tokens."""
+        if self.x_prior is not None and self.prior > 0:
+            ops.csa_compress_quant(self.x_prior, self.w, self.rope_prior, self.codes, self.scales,
+                                   n_seq=self.S, n_per_seq=self.prior,
+                                   x_seq_stride=self.x_prior.shape[1] * D, out_seq_stride=self.cap,
+                                   rope_dim=self.rope_dim, eps=self.eps)
+        tail = self.x_tail.shape[1]
+        ops.csa_window_append(self.x_tail, self.pos_tail, self.win, self.S, N_WIN - 1,
+                              x_seq_stride=tail * D)
+
+    def step(self):
+        tail = self.x_tail.shape[1]
+        ops.csa_window_append(self.x_tail, self.pos_step, self.win, self.S, self.n_step,
+                              x_seq_stride=tail * D, x_offset=(N_WIN - 1) * D)
+        ops.csa_compress_quant(self.x_tail, self.w, self.rope_cs, self.codes, self.scales,
+                               n_seq=self.S, n_per_seq=self.new, x_seq_stride=tail * D,
+                               x_offset=(tail - M * self.new) * D, out_seq_stride=self.cap,
+                               out_offset=self.prior, rope_dim=self.rope_dim, eps=self.eps)
+        for call in self.calls:
+            call()
+
+
+def from_workload(wl, device=None):
+    """LayerStep for a workload object with ``cfg`` and ``tensors`` (see workloads)."""
+    cfg, t = wl.cfg, wl.tensors
+    dev = device or t["codes"].device
+    S = cfg.n_seq
+    if cfg.kind == "decode":
+        first = torch.full((S,), cfg.ctx_tokens - N_WIN, dtype=torch.int32, device=dev)
+    else:
+        first = torch.full((S,), cfg.ctx_tokens - (N_WIN - 1), dtype=torch.int32, device=dev)
+    return LayerStep(kind=cfg.kind, layers=cfg.layers, build_pool=cfg.build_pool, x_tail=t["x_tail"],
+                     w=t["w"], rope_cs=t["rope_cs"], codes=t["codes"], scales=t["scales"],
+                     k_fp8=t["k_fp8"], q_pos=t["q_pos"], q_attn=t["q_attn"], q_fp8=t["q_fp8"],
+                     w_idx=t["w_idx"], prior_entries=cfg.prior_entries, new_entries=cfg.new_entries,
+                     first_pos=first, x_prior=t.get("x_prior"), rope_prior=t.get("rope_prior"))

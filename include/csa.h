@@ -1,0 +1,266 @@
+/*
+ * csa.h -- C ABI of libcsa: one CSA2 compressed-sparse-attention layer step on
+ * an AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the method ("the pages"):
+ *   P3  "DeepSeek-V4.1 架构解析：把长上下文的成本瓶颈从算力挪到存储"
+ *       (blog.yuzhonghai.cloud/deepseek-v41-arch), §02 CSA2 (layer modes
+ *       Full / Reindex / Reuse, Top-512, the hierarchical pool of 2,048 blocks
+ *       x 8 positions) and §03 精度与状态重建 (MXFP4 = E2M1 values with one E4M3
+ *       scale per 16 channels, quantize after RoPE, FP4 for storage only, SWA
+ *       KV in FP8, n_win = 128).
+ *   P2  DeepSeek V4 overview (wmrh.cn/news/159405) §2.1 (4:1 compression).
+ * The pages give no compressor or indexer formula and no dimensions; this
+ * library implements the readings stated at each entry point.
+ *
+ * Conventions (every entry point):
+ *   - Returns csa_status.  Arguments are validated on the host before any
+ *     launch; on error nothing is enqueued and csa_last_error() (thread-local)
+ *     describes the problem.
+ *   - All data pointers are DEVICE pointers owned by the caller; the library
+ *     keeps none of them after returning and never allocates or frees device
+ *     memory.  Scratch memory is a caller-provided workspace whose size the
+ *     matching *_workspace_size function returns.
+ *   - Work is enqueued asynchronously on the caller's stream; the library never
+ *     synchronizes the device or the stream.
+ *   - Rows of codes (256 B), scales (32 B), indexer keys (128 B) and window
+ *     tokens (512 B) and every base pointer must be 16-byte aligned; float and
+ *     int32 arrays must be 4-byte aligned (CSA_ERR_ALIGNMENT otherwise).
+ *   - Every output element an entry point documents is written (including -1
+ *     and -inf padding).
+ *
+ * Fixed dimensions (CSA_ERR_UNSUPPORTED for anything else):
+ *   latent D = 512 (key = value), attention heads 16, indexer heads 8 x 128,
+ *   tokens per entry 4, scale group 16, block 8, window 128 tokens.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_D 512
+#define CSA_HEADS 16
+#define CSA_IDX_HEADS 8
+#define CSA_IDX_DIM 128
+#define CSA_M 4
+#define CSA_GROUP 16
+#define CSA_CODE_BYTES 256   /* D / 2 */
+#define CSA_SCALE_BYTES 32   /* D / 16 */
+#define CSA_BLOCK 8
+#define CSA_TOP_K 512
+#define CSA_POOL_BLOCKS 2048
+#define CSA_N_WIN 128
+
+typedef int32_t csa_status;
+enum {
+  CSA_OK = 0,
+  CSA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad enum value */
+  CSA_ERR_UNSUPPORTED = 2, /* size outside what the kernels are built for */
+  CSA_ERR_ALIGNMENT = 3,   /* pointer or row not aligned as required */
+  CSA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+  CSA_ERR_HIP = 5          /* a HIP launch failed; csa_last_error has the text */
+};
+
+/* Static text of a status code. */
+const char* csa_status_string(csa_status s);
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* csa_last_error(void);
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t csa_version(void);
+
+/* ---------------------------------------------------------------- a2 ----
+ * csa_quantize: MXFP4-quantize n post-RoPE entries (P3 §03).
+ *   e      [n, 512] float32, the quantizer input
+ *   codes  [n, 256] uint8 out: channel 2k in the low nibble of byte k; each
+ *          nibble = signbit(x) << 3 | RNE_E2M1(|x| / s) (saturating at 6,
+ *          ties to the even code; magnitude 0 when s = 0)
+ *   scales [n, 32] uint8 out: per 16-channel group s = RNE_E4M3FN(amax / 6),
+ *          saturating at 448 (no global scale)
+ * Decisions are exact: the result equals rounding the exact real quotients.
+ * n = 0 is a no-op.
+ */
+csa_status csa_quantize(const float* e, int64_t n, uint8_t* codes, uint8_t* scales,
+                        hipStream_t stream);
+
+/* csa_dequantize: codes/scales of n entries -> float32 [n, 512] (s * E2M1(c)).
+ * P3 §03: the FP4 cache is dequantized before attention. */
+csa_status csa_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t n,
+                          float* out, hipStream_t stream);
+
+/* ----------------------------------------------------------- a1 + a2 ----
+ * csa_compress_quant: compress every 4 token latents into one entry, RMSNorm,
+ * RoPE, MXFP4-quantize and store (P3 §02 sequence compression; P2 §2.1 4:1;
+ * P3 §03 RMSNorm magnitude ~1, quantize after RoPE).
+ *   Entries are (sequence s < n_seq, r < n_per_seq).  Entry (s, r) reads the 4
+ *   tokens x + s * x_seq_stride + r * 4 * 512 (float32 [4, 512]) and writes
+ *   row s * out_seq_stride + r of codes [.., 256] / scales [.., 32].
+ *   y = sum_i W_i x_i with w float32 [4, 512 (out), 512 (in)];
+ *   e = y / sqrt(mean(y^2) + eps) (unit gain);
+ *   RoPE on the last rope_dim channels (0 or an even number <= 512, multiple
+ *   of 32 so that pairs never straddle a scale group boundary... any even value
+ *   up to 512 is accepted), pairs (c, c+1) rotated by rope_cs
+ *   float32 [n_seq, n_per_seq, rope_dim / 2, 2] = (cos, sin); rope_cs may be
+ *   NULL only when rope_dim = 0.
+ *   e_out (optional, may be NULL): float32 [n_seq * n_per_seq, 512], the
+ *   quantizer input (post-RoPE, float32), for inspection.
+ *   Workspace: csa_compress_quant_workspace_size(n_seq * n_per_seq) bytes.
+ */
+size_t csa_compress_quant_workspace_size(int64_t n_entries);
+csa_status csa_compress_quant(const float* x, int64_t n_seq, int64_t n_per_seq,
+                              int64_t x_seq_stride, const float* w, const float* rope_cs,
+                              int32_t rope_dim, float eps, uint8_t* codes, uint8_t* scales,
+                              int64_t out_seq_stride, float* e_out, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* ---------------------------------------------------------------- a9 ----
+ * csa_window_append: write n_tok token latents of each of n_seq sequences into
+ * the FP8 sliding-window ring (P3 §03: SWA KV kept in FP8; n_win = 128).
+ *   x       float32, token t of sequence s at x + s * x_seq_stride + t * 512
+ *   pos0    int32 [n_seq]: position of token 0 of each sequence
+ *   win     uint8 [n_seq, win_cap, 512]: token at position p goes to row
+ *           p % win_cap; value = RNE_E4M3FN(x), saturating at +-448, sign kept
+ *   win_cap >= 128 rows.
+ */
+csa_status csa_window_append(const float* x, int64_t n_seq, int64_t n_tok, int64_t x_seq_stride,
+                             const int32_t* pos0, uint8_t* win, int64_t win_cap,
+                             hipStream_t stream);
+
+/* ---------------------------------------------------------------- a3 ----
+ * csa_index_score: indexer scores of Q = n_seq * q_per_seq queries (P3 §02:
+ * Full layers score every causally visible position; Reindex layers rescore
+ * with their own query, inside the hierarchical pool when one exists).
+ *   Query q belongs to sequence q / q_per_seq and sits at token position
+ *   q_pos[q] >= 0; entry j is visible iff 4j + 3 <= q_pos[q].
+ *   score = sum_h w[q, h] * ReLU(q_fp8[q, h, :] . k_fp8[j, :]) (8 heads x 128,
+ *   E4M3 operands, float32 accumulation on the FP8 matrix cores).
+ *   q_fp8 uint8 [Q, 8, 128]; w float32 [Q, 8] (must be >= 0);
+ *   k_fp8 uint8 [n_seq, k_seq_stride, 128].
+ *   Dense mode (pool_blocks == NULL): ncols = n_entries columns; column j is
+ *   entry j (j < n_entries <= k_seq_stride).
+ *   Pooled mode: pool_blocks int32 [Q, n_pool_blocks] (ascending block ids,
+ *   -1 padded); ncols = 8 * n_pool_blocks; column c is entry
+ *   8 * pool[c / 8] + c % 8.
+ *   scores (may be NULL) float32 [Q, ncols] out; invisible columns, entries
+ *   >= n_entries and -1 pool slots are written as -inf.
+ *   block_max (may be NULL; dense mode only) float32 [Q, ceil(ncols / 8)] out:
+ *   max score of each aligned 8-entry block over its visible entries (-inf if
+ *   none).  At least one of scores / block_max must be given.
+ */
+csa_status csa_index_score(const uint8_t* q_fp8, const float* w, const int32_t* q_pos,
+                           int64_t n_seq, int64_t q_per_seq, const uint8_t* k_fp8,
+                           int64_t k_seq_stride, int64_t n_entries, const int32_t* pool_blocks,
+                           int32_t n_pool_blocks, float* scores, float* block_max,
+                           hipStream_t stream);
+
+/* ---------------------------------------------------------------- a4 ----
+ * csa_topk: for each of Q rows of scores float32 [Q, ncols], select the k
+ * columns with the largest scores (P3 §02 Top-512); equal scores go to the
+ * lower column; -inf columns are never selected.  Outputs the selected ids in
+ * ascending order, -1 padded, into idx int32 [Q, k].
+ *   col_blocks (may be NULL) int32 [Q, ncols / 8]: when given, column c maps
+ *   to id 8 * col_blocks[q, c / 8] + c % 8 (pooled scores; the block ids must
+ *   be ascending so that id order equals column order).
+ *   1 <= k <= 4096; ncols >= 1.
+ *   Workspace: csa_topk_workspace_size(Q, ncols, k).
+ */
+size_t csa_topk_workspace_size(int64_t Q, int64_t ncols, int32_t k);
+csa_status csa_topk(const float* scores, int64_t Q, int64_t ncols, const int32_t* col_blocks,
+                    int32_t k, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- a5 ----
+ * csa_block_pool: the hierarchical pool (P3 §02: rank 8-position blocks by
+ * their largest index score, keep 2,048 blocks = 16,384 candidates).
+ *   is_block_max = 1: values float32 [Q, ncols] are block maxima (one column
+ *   per block); 0: values are per-entry scores and the block maxima over
+ *   aligned 8-column blocks are formed first (-inf entries ignored).
+ *   Selects n_pool_blocks blocks per row by (block max desc, block id asc),
+ *   -inf blocks never; writes ascending block ids, -1 padded, to
+ *   pool_blocks int32 [Q, n_pool_blocks].  1 <= n_pool_blocks <= 4096.
+ *   Workspace: csa_block_pool_workspace_size(Q, ncols, is_block_max, n_pool_blocks).
+ */
+size_t csa_block_pool_workspace_size(int64_t Q, int64_t ncols, int32_t is_block_max,
+                                     int32_t n_pool_blocks);
+csa_status csa_block_pool(const float* values, int32_t is_block_max, int64_t Q, int64_t ncols,
+                          int32_t n_pool_blocks, int32_t* pool_blocks, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* ---------------------------------------------------------------- a7 ----
+ * csa_sparse_attn: sparse multi-query attention (P3 §02 the selected entries
+ * are used for attention; P3 §03 the FP4 cache is dequantized before
+ * attention and the SWA window stays FP8, n_win = 128).
+ *   Query q (sequence q / q_per_seq, position q_pos[q]) attends with 16 heads
+ *   q float32 [Q, 16, 512] over the union of
+ *     - the entries idx int32 [Q, k] (ids < 0 or >= kv_rows are skipped),
+ *       dequantized from codes [n_seq, kv_rows, 256] / scales [n_seq, kv_rows, 32]
+ *       (one shared latent is both key and value), and
+ *     - the window tokens max(0, p - 127) .. p, read from
+ *       win uint8 [n_seq, win_cap, 512] row p % win_cap (E4M3, no scale),
+ *   with one softmax of logits sm_scale * q . key.  out float32 [Q, 16, 512].
+ *   Arithmetic: keys and values are exact in fp16; q is rounded to fp16;
+ *   fp16 matrix cores with float32 accumulation; float32 softmax.
+ *   1 <= k <= 4096.  Workspace: csa_sparse_attn_workspace_size(Q, k).
+ */
+size_t csa_sparse_attn_workspace_size(int64_t Q, int32_t k);
+csa_status csa_sparse_attn(const float* q, const int32_t* q_pos, int64_t n_seq, int64_t q_per_seq,
+                           const uint8_t* codes, const uint8_t* scales, int64_t kv_rows,
+                           const int32_t* idx, int32_t k, const uint8_t* win, int64_t win_cap,
+                           float sm_scale, float* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------ a6 + a8 ----
+ * Layer entry points (P3 §02 layer modes).
+ *   Full:    score every visible entry with (q_idx, w_idx) -> Top-k idx;
+ *            when build_pool != 0 also the hierarchical pool -> pool_blocks.
+ *   Reindex: reuse the Full layer's cache, indexer keys and pool; rescore
+ *            inside the pool (or every visible entry if pool_blocks is NULL)
+ *            with this layer's (q_idx, w_idx) -> Top-k idx.
+ *   Reuse:   attention with the idx given (the most recent Full/Reindex).
+ *   All three then run csa_sparse_attn with q_attn -> out.
+ * Field meanings follow the entry points above.  Workspace:
+ *   csa_layer_workspace_size(mode, args) with mode CSA_MODE_*.
+ */
+enum { CSA_MODE_FULL = 0, CSA_MODE_REINDEX = 1, CSA_MODE_REUSE = 2 };
+
+typedef struct csa_layer_args {
+  /* cache view (per sequence: kv_rows rows) */
+  const uint8_t* codes;    /* [n_seq, kv_rows, 256] */
+  const uint8_t* scales;   /* [n_seq, kv_rows, 32] */
+  int64_t kv_rows;
+  const uint8_t* k_fp8;    /* [n_seq, k_rows, 128] */
+  int64_t k_rows;
+  int64_t n_entries;       /* entries in use per sequence (<= kv_rows, k_rows) */
+  const uint8_t* win;      /* [n_seq, win_cap, 512] */
+  int64_t win_cap;
+  /* queries */
+  int64_t n_seq;
+  int64_t q_per_seq;
+  const int32_t* q_pos;    /* [Q] */
+  const float* q_attn;     /* [Q, 16, 512] */
+  const uint8_t* q_idx;    /* [Q, 8, 128] (Full, Reindex) */
+  const float* w_idx;      /* [Q, 8] (Full, Reindex) */
+  float sm_scale;
+  int32_t top_k;           /* k (512 for the method) */
+  int32_t build_pool;      /* Full: also build the pool */
+  int32_t n_pool_blocks;   /* 2048 for the method */
+  int32_t* pool_blocks;    /* [Q, n_pool_blocks]: out (Full + build_pool), in (Reindex) */
+  int32_t* idx;            /* [Q, top_k]: out (Full, Reindex), in (Reuse) */
+  float* out;              /* [Q, 16, 512] */
+  void* ws;
+  size_t ws_bytes;
+} csa_layer_args;
+
+size_t csa_layer_workspace_size(int32_t mode, const csa_layer_args* a);
+csa_status csa_layer_full(const csa_layer_args* a, hipStream_t stream);
+csa_status csa_layer_reindex(const csa_layer_args* a, hipStream_t stream);
+csa_status csa_layer_reuse(const csa_layer_args* a, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H */

@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads, exports every function declared in include/csa.h, and
+rejects invalid arguments with the documented status before any launch (no
+device is touched: these calls fail validation first).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from compressed_sparse_attention_04_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE = 0, 1, 2, 3, 4
+P = ctypes.c_void_p(4096)            # a fake, aligned, never-dereferenced address
+P_ODD = ctypes.c_void_p(4097)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 19
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
+
+
+def test_status_strings_and_version(lib):
+    assert lib.csa_status_string(0) == b"ok"
+    assert lib.csa_status_string(4) == b"workspace too small"
+    assert lib.csa_version() >= 100
+
+
+def test_layer_struct_matches_header():
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct csa_layer_args"):text.index("} csa_layer_args;")]
+    fields = re.findall(r"\b([a-z_0-9]+);", body)
+    assert fields == [f for f, _ in _lib.CsaLayerArgs._fields_]
+
+
+def test_quantize_validation(lib):
+    assert lib.csa_quantize(None, 0, None, None, None) == OK              # n = 0: no-op
+    assert lib.csa_quantize(None, 4, P, P, None) == INVALID
+    assert b"NULL" in lib.csa_last_error()
+    assert lib.csa_quantize(P, -1, P, P, None) == INVALID
+    assert lib.csa_quantize(P_ODD, 4, P, P, None) == ALIGN
+
+
+def test_compress_validation(lib):
+    f = lib.csa_compress_quant
+    need = lib.csa_compress_quant_workspace_size(10)
+    assert need > 0
+    args = [P, 1, 10, 10 * 2048, P, P, 64, ctypes.c_float(1e-6), P, P, 10, None, P, need, None]
+    a = list(args); a[6] = 63
+    assert f(*a) == UNSUPPORTED                                           # odd rope_dim
+    a = list(args); a[5] = None
+    assert f(*a) == INVALID                                               # rope table missing
+    a = list(args); a[13] = need - 1
+    assert f(*a) == WORKSPACE
+    a = list(args); a[8] = P_ODD
+    assert f(*a) == ALIGN
+    a = list(args); a[1] = 2; a[3] = 100
+    assert f(*a) == INVALID                                               # overlapping sequences
+
+
+def test_topk_and_pool_validation(lib):
+    assert lib.csa_topk(P, 2, 100, None, 0, P, None, 0, None) == UNSUPPORTED
+    assert lib.csa_topk(P, 2, 100, None, 4097, P, None, 0, None) == UNSUPPORTED
+    assert lib.csa_topk(P, 2, 100, P, 10, P, None, 0, None) == INVALID     # pooled, 100 % 8 != 0
+    need = lib.csa_topk_workspace_size(2, 100000, 512)
+    assert need > 0
+    assert lib.csa_topk(P, 2, 100000, None, 512, P, P, need - 8, None) == WORKSPACE
+    assert lib.csa_block_pool(P, 2, 1, 10, 8, P, None, 0, None) == INVALID
+    assert lib.csa_block_pool(P, 1, 1, 10, 0, P, None, 0, None) == UNSUPPORTED
+
+
+def test_score_and_attn_validation(lib):
+    f = lib.csa_index_score
+    assert f(P, P, P, 1, 1, P, 100, 101, None, 0, P, None, None) == INVALID   # n_entries > k_rows
+    assert f(P, P, P, 1, 1, P, 100, 50, None, 0, None, None, None) == INVALID  # no output
+    assert f(P_ODD, P, P, 1, 1, P, 100, 50, None, 0, P, None, None) == ALIGN
+    g = lib.csa_sparse_attn
+    base = [P, P, 1, 1, P, P, 100, P, 512, P, 128, ctypes.c_float(0.04), P, P, 1 << 30, None]
+    a = list(base); a[10] = 64
+    assert g(*a) == UNSUPPORTED                                           # window ring too small
+    a = list(base); a[8] = 0
+    assert g(*a) == UNSUPPORTED
+    a = list(base); a[11] = ctypes.c_float(float("nan"))
+    assert g(*a) == INVALID
+
+
+def test_layer_validation(lib):
+    a = _lib.CsaLayerArgs()
+    a.n_seq, a.q_per_seq, a.top_k = 1, 1, 512
+    a.kv_rows, a.k_rows, a.n_entries = 100, 100, 100
+    assert lib.csa_layer_full(ctypes.byref(a), None) == INVALID           # null pointers
+    assert lib.csa_layer_full(None, None) == INVALID
+    a.top_k = 0
+    assert lib.csa_layer_reuse(ctypes.byref(a), None) == UNSUPPORTED
+    assert lib.csa_layer_workspace_size(7, ctypes.byref(a)) == 0

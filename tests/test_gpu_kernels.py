@@ -1,0 +1,275 @@
+"""GPU parity of each C-ABI entry point against the oracle, on seeded inputs.
+
+Every test calls the HIP library through its C ABI (ctypes binding) and
+compares with the float64 oracle under the method's rules (see helpers.py).
+Sizes span several tiles / chunks and end in ragged tails.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import formats, mxfp4
+from compressed_sparse_attention_04_amd import ops
+from helpers import check_attn, check_topk_set, np_, SM
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def t_(a, dtype=None):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV) if dtype is None else \
+        torch.from_numpy(np.ascontiguousarray(a)).to(DEV, dtype)
+
+
+def quant_inputs(rng, n):
+    """Entries with varied group magnitudes, zero groups, exact midpoints and saturation."""
+    x = rng.standard_normal((n, 512)) * rng.choice([1e-4, 0.01, 1.0, 30.0, 5000.0], (n, 32, 1)).repeat(16, -1).reshape(n, 512)
+    x = x.astype(np.float32)
+    if n >= 4:
+        x[0, :16] = 0.0
+        x[1, :16] = -0.0
+        # a group of exact E2M1 midpoints times an exact scale
+        s = np.float32(0.3125)
+        x[2, :16] = s * np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, -0.25, -0.75,
+                                  -1.25, -1.75, -2.5, -3.5, -5.0, -6.0], np.float32)
+        x[3, :16] = 2688.0 * np.sign(rng.standard_normal(16)).astype(np.float32)
+        x[3, 16:32] = 1e30
+    return x
+
+
+@pytest.mark.parametrize("n", [0, 1, 5, 17, 1000])
+def test_quantize_bit_exact(n):
+    rng = np.random.default_rng(n)
+    x = quant_inputs(rng, n)
+    codes, scales = ops.csa_quantize(t_(x))
+    torch.cuda.synchronize()
+    if n == 0:
+        return
+    rc, rs = mxfp4.quantize(x)
+    assert np.array_equal(np_(scales), rs)
+    assert np.array_equal(np_(codes), rc)
+
+
+def test_dequantize_exact():
+    rng = np.random.default_rng(1)
+    n = 300
+    codes = rng.integers(0, 256, (n, 256)).astype(np.uint8)
+    scales = rng.integers(0, 0x7F, (n, 32)).astype(np.uint8)        # every finite positive scale
+    out = ops.csa_dequantize(t_(codes), t_(scales))
+    torch.cuda.synchronize()
+    ref = mxfp4.dequantize(codes, scales)
+    assert np.array_equal(np_(out).astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("n_seq,n_tok,cap,p0", [(1, 1, 128, 0), (3, 200, 256, 50), (2, 130, 130, 1000)])
+def test_window_append_bit_exact(n_seq, n_tok, cap, p0):
+    rng = np.random.default_rng(n_tok)
+    x = (rng.standard_normal((n_seq, n_tok, 512)) * rng.choice([1e-3, 1, 300], (n_seq, n_tok, 1))).astype(np.float32)
+    x[0, 0, :4] = [500.0, -1e6, -0.0, 2.0 ** -10]
+    pos0 = np.array([p0 + 7 * s for s in range(n_seq)], np.int32)
+    win = torch.full((n_seq, cap, 512), 0xAB, dtype=torch.uint8, device=DEV)
+    ops.csa_window_append(t_(x), t_(pos0), win, n_seq, n_tok)
+    torch.cuda.synchronize()
+    got = np_(win)
+    for s in range(n_seq):
+        # later tokens overwrite earlier ones that share a ring row
+        expect = np.full((cap, 512), 0xAB, np.uint8)
+        for t in range(n_tok):
+            expect[(pos0[s] + t) % cap] = formats.e4m3_encode(x[s, t])
+        assert np.array_equal(got[s], expect)
+
+
+def test_compress_quant_chain():
+    """fp32 GPU chain vs the fp64 oracle: the quantizer input agrees to fp32
+    accuracy, its bytes equal the oracle's quantization of the GPU's own fp32
+    input, and any code that differs from the fp64 chain's sits at a rounding
+    boundary."""
+    rng = np.random.default_rng(2)
+    n_seq, n_per, rows = 3, 37, 50
+    x = rng.standard_normal((n_seq, 4 * n_per, 512)).astype(np.float32)
+    w = (rng.standard_normal((4, 512, 512)) / np.sqrt(2048)).astype(np.float32)
+    ang = rng.uniform(0, 100, (n_seq, n_per, 32))
+    cs = np.stack([np.cos(ang), np.sin(ang)], -1).astype(np.float32)
+    codes = torch.zeros((n_seq, rows, 256), dtype=torch.uint8, device=DEV)
+    scales = torch.zeros((n_seq, rows, 32), dtype=torch.uint8, device=DEV)
+    e_out = torch.empty((n_seq * n_per, 512), dtype=torch.float32, device=DEV)
+    ops.csa_compress_quant(t_(x), t_(w), t_(cs), codes, scales, n_seq, n_per,
+                           x_seq_stride=4 * n_per * 512, out_seq_stride=rows, out_offset=5, e_out=e_out)
+    torch.cuda.synchronize()
+    e_gpu = np_(e_out).reshape(n_seq, n_per, 512)
+    gc, gs = np_(codes), np_(scales)
+    assert not gc[:, :5].any() and not gc[:, 5 + n_per:].any()
+    flips = 0
+    for s in range(n_seq):
+        e_ref64 = oracle.rope_rotate(oracle.compress(x[s], w, 1e-6), cs[s], 64)
+        np.testing.assert_allclose(e_gpu[s], e_ref64, rtol=0, atol=2e-5)
+        c2, s2 = mxfp4.quantize(e_gpu[s])                 # strict: same fp32 input -> same bytes
+        assert np.array_equal(gc[s, 5:5 + n_per], c2)
+        assert np.array_equal(gs[s, 5:5 + n_per], s2)
+        rc, rsc = mxfp4.quantize(e_ref64.astype(np.float32))
+        flips += int((rc != c2).sum() + (rsc != s2).sum())
+    assert flips <= 3, flips
+
+
+def _scores_case(rng, n_seq, q_per_seq, n_entries, k_rows, pos_base):
+    Q = n_seq * q_per_seq
+    q8 = formats.e4m3_encode(rng.standard_normal((Q, 8, 128)))
+    k8 = formats.e4m3_encode(rng.standard_normal((n_seq, k_rows, 128)))
+    w = rng.random((Q, 8)).astype(np.float32)
+    pos = np.array([pos_base + (i % q_per_seq) for i in range(Q)], np.int32)
+    return q8, k8, w, pos
+
+
+@pytest.mark.parametrize("n_seq,q_per_seq,n_entries,pos_base",
+                         [(3, 1, 3000, 4 * 2990 + 1), (1, 96, 1500, 4 * 1480), (2, 40, 333, 4 * 300)])
+def test_index_score_dense(n_seq, q_per_seq, n_entries, pos_base):
+    rng = np.random.default_rng(n_entries)
+    k_rows = n_entries + 5
+    q8, k8, w, pos = _scores_case(rng, n_seq, q_per_seq, n_entries, k_rows, pos_base)
+    scores, bm = ops.csa_index_score(t_(q8), t_(w), t_(pos), t_(k8), n_seq, q_per_seq, n_entries,
+                                     want_block_max=True)
+    torch.cuda.synchronize()
+    sc, bmg = np_(scores), np_(bm)
+    worst = 0.0
+    for qi in range(n_seq * q_per_seq):
+        s = qi // q_per_seq
+        nv = oracle.visible_entries(pos[qi], n_entries)
+        ref = oracle.index_scores(q8[qi], w[qi], k8[s, :nv])
+        err = np.abs(sc[qi, :nv] - ref) / np.maximum(1.0, np.abs(ref))
+        worst = max(worst, float(err.max()) if nv else 0.0)
+        assert np.all(np.isneginf(sc[qi, nv:]))
+        # block max = max of this call's own scores, bit for bit
+        for b in range(bmg.shape[1]):
+            seg = sc[qi, 8 * b: 8 * b + 8]
+            assert bmg[qi, b] == seg.max() or (np.isneginf(bmg[qi, b]) and np.all(np.isneginf(seg)))
+    assert worst <= 2e-6, worst
+
+
+def test_index_score_pooled_matches_dense_bitwise():
+    rng = np.random.default_rng(5)
+    n_seq, n_entries = 2, 2000
+    q8, k8, w, pos = _scores_case(rng, n_seq, 1, n_entries, n_entries, 4 * 1995 + 2)
+    nb = 40
+    pool = np.full((n_seq, nb), -1, np.int32)
+    for s in range(n_seq):
+        blocks = np.sort(rng.choice(250, nb - 3, replace=False))
+        blocks[-1] = 249                                    # partially visible last block
+        pool[s, :nb - 3] = blocks
+    dense, _ = ops.csa_index_score(t_(q8), t_(w), t_(pos), t_(k8), n_seq, 1, n_entries)
+    pooled, _ = ops.csa_index_score(t_(q8), t_(w), t_(pos), t_(k8), n_seq, 1, n_entries,
+                                    pool_blocks=t_(pool))
+    torch.cuda.synchronize()
+    d, p = np_(dense), np_(pooled)
+    for s in range(n_seq):
+        nv = oracle.visible_entries(pos[s], n_entries)
+        for c in range(8 * nb):
+            b = pool[s, c // 8]
+            e = 8 * b + c % 8
+            if b < 0 or e >= nv:
+                assert np.isneginf(p[s, c])
+            else:
+                assert p[s, c] == d[s, e]
+
+
+def _oracle_topk_fp32(row, k, ids=None):
+    valid = ~np.isneginf(row)
+    ids = np.arange(len(row)) if ids is None else np.asarray(ids)
+    return oracle.topk(row[valid].astype(np.float64), k, ids=ids[valid])
+
+
+@pytest.mark.parametrize("Q,ncols,k", [(3, 100, 512), (2, 5000, 512), (2, 20000, 512),
+                                       (2, 300000, 512), (2, 40000, 2048), (1, 16384, 4096)])
+def test_topk_exact(Q, ncols, k):
+    rng = np.random.default_rng(ncols + k)
+    sc = rng.integers(0, 200, (Q, ncols)).astype(np.float32) * np.float32(0.25)   # heavy ties
+    sc[:, ::7] = -np.inf
+    sc[0, :ncols // 3] = -np.inf
+    if ncols > 10:
+        sc[-1, 3] = -0.0
+        sc[-1, 4] = 0.0
+    idx = ops.csa_topk(t_(sc), k=k)
+    torch.cuda.synchronize()
+    got = np_(idx)
+    for q in range(Q):
+        assert np.array_equal(got[q], _oracle_topk_fp32(sc[q], k)), q
+
+
+def test_topk_pooled_mapping():
+    rng = np.random.default_rng(9)
+    Q, nb, k = 2, 300, 100
+    blocks = np.stack([np.sort(rng.choice(5000, nb, replace=False)) for _ in range(Q)]).astype(np.int32)
+    sc = rng.integers(0, 30, (Q, 8 * nb)).astype(np.float32)
+    idx = ops.csa_topk(t_(sc), k=k, col_blocks=t_(blocks))
+    torch.cuda.synchronize()
+    got = np_(idx)
+    for q in range(Q):
+        ids = (8 * blocks[q][:, None] + np.arange(8)[None]).reshape(-1)
+        assert np.array_equal(got[q], _oracle_topk_fp32(sc[q], k, ids=ids))
+
+
+@pytest.mark.parametrize("is_bm,Q,ncols,nb", [(True, 2, 33000, 2048), (True, 3, 1000, 2048),
+                                              (False, 2, 70001, 2048), (False, 1, 4000, 100)])
+def test_block_pool_exact(is_bm, Q, ncols, nb):
+    rng = np.random.default_rng(ncols)
+    v = rng.integers(0, 500, (Q, ncols)).astype(np.float32)
+    v[:, ::5] = -np.inf
+    pool = ops.csa_block_pool(t_(v), is_block_max=is_bm, n_pool_blocks=nb)
+    torch.cuda.synchronize()
+    got = np_(pool)
+    for q in range(Q):
+        if is_bm:
+            ref = _oracle_topk_fp32(v[q], nb)
+        else:
+            row = v[q].astype(np.float64)
+            nblk = (ncols + 7) // 8
+            bm = np.array([row[8 * b: 8 * b + 8].max() for b in range(nblk)])
+            ref = _oracle_topk_fp32(bm, nb)
+        assert np.array_equal(got[q], ref)
+
+
+def _attn_case(rng, n_seq, q_per_seq, rows, k, win_cap, p_base, invalid_frac=0.05):
+    Q = n_seq * q_per_seq
+    codes = rng.integers(0, 256, (n_seq, rows, 256)).astype(np.uint8)
+    scales = rng.integers(0x28, 0x31, (n_seq, rows, 32)).astype(np.uint8)
+    win = formats.e4m3_encode(rng.standard_normal((n_seq, win_cap, 512)))
+    q = rng.standard_normal((Q, 16, 512)).astype(np.float32)
+    idx = np.stack([np.sort(rng.choice(rows, k, replace=False)) for _ in range(Q)]).astype(np.int32)
+    idx[rng.random(idx.shape) < invalid_frac] = -1
+    pos = np.array([p_base + (i % q_per_seq) for i in range(Q)], np.int32)
+    return codes, scales, win, q, idx, pos
+
+
+def _attn_ref(codes, scales, win, q, idx, pos, q_per_seq, win_cap):
+    outs = []
+    for qi in range(len(q)):
+        s = qi // q_per_seq
+        wp = oracle.window_positions(pos[qi])
+        outs.append(oracle.sparse_attention(q[qi], codes[s], scales[s], idx[qi], win[s, wp % win_cap], SM))
+    return np.stack(outs)
+
+
+@pytest.mark.parametrize("n_seq,q_per_seq,k,p_base", [(4, 1, 512, 5000), (1, 300, 512, 2000),
+                                                      (2, 1, 77, 60), (1, 1, 512, 0)])
+def test_sparse_attn(n_seq, q_per_seq, k, p_base):
+    rng = np.random.default_rng(k + p_base)
+    rows, win_cap = 1200, 128 + (q_per_seq if q_per_seq > 1 else 0)
+    codes, scales, win, q, idx, pos = _attn_case(rng, n_seq, q_per_seq, rows, k, win_cap, p_base)
+    out = ops.csa_sparse_attn(t_(q), t_(pos), t_(codes), t_(scales), t_(idx), t_(win), n_seq, q_per_seq)
+    torch.cuda.synchronize()
+    check_attn(np_(out), _attn_ref(codes, scales, win, q, idx, pos, q_per_seq, win_cap))
+
+
+def test_sparse_attn_dense_case_and_empty_selection():
+    """K >= visible: attention over every entry + window; and no entry selected."""
+    rng = np.random.default_rng(11)
+    rows = 900
+    codes, scales, win, q, _, pos = _attn_case(rng, 1, 1, rows, 10, 128, 7000)
+    idx = np.arange(rows, dtype=np.int32)[None]
+    out = ops.csa_sparse_attn(t_(q), t_(pos), t_(codes), t_(scales), t_(idx), t_(win), 1, 1)
+    none = np.full((1, 512), -1, np.int32)
+    out2 = ops.csa_sparse_attn(t_(q), t_(pos), t_(codes), t_(scales), t_(none), t_(win), 1, 1)
+    torch.cuda.synchronize()
+    check_attn(np_(out), _attn_ref(codes, scales, win, q, idx, pos, 1, 128))
+    check_attn(np_(out2), _attn_ref(codes, scales, win, q, none, pos, 1, 128))
