@@ -327,7 +327,7 @@ static csa_status check_layer(const char* fn, int32_t mode, const csa_layer_args
   if (plan->total) CHECK_ALIGN(a->ws, 256);
   if (mode != CSA_MODE_REUSE && plan->Q > 0) {
     ScoreArgs s{a->q_idx, a->w_idx, a->q_pos, a->n_seq, a->q_per_seq, a->k_fp8, a->k_rows, a->n_entries,
-                plan->pooled ? a->pool_blocks : nullptr, a->n_pool_blocks, reinterpret_cast<float*>(1),
+                plan->pooled ? a->pool_blocks : nullptr, a->n_pool_blocks, reinterpret_cast<float*>(256),
                 nullptr};
     csa_status st = check_score(fn, s);
     if (st != CSA_OK) return st;

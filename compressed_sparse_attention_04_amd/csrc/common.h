@@ -21,6 +21,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -136,6 +137,11 @@ __device__ __forceinline__ f32x4 mfma_f16_16x16x16(f16x4 a, f16x4 b, f32x4 c) {
 }
 __device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// fp64 16x16x4: A lane l = row l%16, k l/16 (same as fp32), but the result
+// lane l, register r holds row l/16 + 4r, column l%16 (verified on gfx950).
+__device__ __forceinline__ f64x4 mfma_f64_16x16x4(double a, double b, f64x4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ int visible_count(int32_t pos) { return pos < 0 ? 0 : (pos + 1) >> 2; }

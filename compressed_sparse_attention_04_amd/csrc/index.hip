@@ -1,15 +1,22 @@
-// Indexer scoring on the FP8 matrix cores.
+// Indexer scoring on the matrix cores.
 //
 // P3 §02: Full layers score every causally visible position; Reindex layers
 // rescore with their own indexer query, inside the hierarchical pool.
 // score_j = sum_h w_h * ReLU(q_h . k_j), 8 heads x 128 dims, E4M3 operands.
 //
-// One v_mfma 16x16x128 (fp8) contracts a 16-row A fragment (8 heads of one
-// query, or 8 heads each of two queries) against 16 indexer keys: the whole
-// 128-wide head dimension is a single instruction.  The epilogue applies
-// ReLU and the head weights on the accumulator (lane l holds rows
-// 4*(l/16)+r, column l%16), folds the two 16-lane halves that hold the 8
-// heads of a query, and optionally reduces 8 adjacent columns to a block max.
+// The E4M3 operands are converted in registers to fp16 (exact: 4 significant
+// bits, exponents 2^-9 .. 2^8) and contracted on the fp16 matrix cores with
+// float32 accumulation, four v_mfma 16x16x32 per 16-row x 16-key fragment.
+// Every product is exact and the sum is a float32 sum.  (The gfx950 fp8
+// v_mfma 16x16x128 accumulates 128 products with about 2^-15 relative
+// precision, too coarse for a Top-K that must agree with the exact scores up
+// to 1e-5 near the threshold.)
+//
+// A fragment holds 8 heads of one query (rows 8-15 zero) or 8 heads each of
+// two queries.  The epilogue applies ReLU and the head weights on the
+// accumulator (lane l holds rows 4*(l/16)+r, column l%16), folds the two
+// 16-lane halves that hold the 8 heads of a query, and optionally reduces 8
+// adjacent columns to a block max.
 #include "common.h"
 #include "kernels.h"
 
@@ -17,30 +24,49 @@ namespace csa {
 
 namespace {
 
-// A-fragment register block of one lane: 32 fp8 bytes of one (query, head)
-// row: bytes 32 * (lane / 16) .. +32.  Rows whose query is absent are zero.
-__device__ __forceinline__ i32x8 load_qfrag(const uint8_t* q_fp8, int64_t q, int head, bool live,
-                                            int lane) {
-  i32x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+// One lane's share of a 16 x 128 operand fragment: 32 E4M3 bytes of one row,
+// bytes 32 * (lane / 16) .. +32.  A and B use the same byte -> k mapping
+// (k-step s takes bytes 8 s .. 8 s + 7 of the lane's 32), so the four
+// 16x16x32 products contract exactly the 128 channels.
+struct Raw32 { uint4 u0, u1; };
+struct Frag16 { f16x8 s[4]; };
+
+__device__ __forceinline__ Raw32 load_raw32(const uint8_t* row, bool live, int lane) {
+  Raw32 r = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
   if (live) {
-    const uint4* p = reinterpret_cast<const uint4*>(q_fp8 + (q * IH + head) * ID + 32 * (lane >> 4));
-    uint4 u0 = p[0], u1 = p[1];
-    a[0] = u0.x; a[1] = u0.y; a[2] = u0.z; a[3] = u0.w;
-    a[4] = u1.x; a[5] = u1.y; a[6] = u1.z; a[7] = u1.w;
+    const uint4* p = reinterpret_cast<const uint4*>(row + 32 * (lane >> 4));
+    r.u0 = p[0];
+    r.u1 = p[1];
   }
-  return a;
+  return r;
 }
 
-// B fragment: lane l loads bytes 32 * (l / 16) .. +32 of key row `e`.
-__device__ __forceinline__ i32x8 load_kfrag(const uint8_t* krow_base, int64_t e, bool live, int lane) {
-  i32x8 b = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (live) {
-    const uint4* p = reinterpret_cast<const uint4*>(krow_base + e * ID + 32 * (lane >> 4));
-    uint4 u0 = p[0], u1 = p[1];
-    b[0] = u0.x; b[1] = u0.y; b[2] = u0.z; b[3] = u0.w;
-    b[4] = u1.x; b[5] = u1.y; b[6] = u1.z; b[7] = u1.w;
-  }
-  return b;
+__device__ __forceinline__ f16x8 fp8x8_to_f16(uint32_t w0, uint32_t w1) {
+  f16x2 a = fp8x2_to_f16<0>(w0), b = fp8x2_to_f16<1>(w0);
+  f16x2 c = fp8x2_to_f16<0>(w1), d = fp8x2_to_f16<1>(w1);
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ Frag16 to_frag(const Raw32& r) {
+  Frag16 f;
+  f.s[0] = fp8x8_to_f16(r.u0.x, r.u0.y);
+  f.s[1] = fp8x8_to_f16(r.u0.z, r.u0.w);
+  f.s[2] = fp8x8_to_f16(r.u1.x, r.u1.y);
+  f.s[3] = fp8x8_to_f16(r.u1.z, r.u1.w);
+  return f;
+}
+
+__device__ __forceinline__ f32x4 frag_mma(const Frag16& a, const Frag16& b) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = mfma_f16_16x16x32(a.s[s], b.s[s], acc);
+  return acc;
+}
+
+// A fragment of (query q, head) for this lane; zero when the row is absent.
+__device__ __forceinline__ Frag16 load_qfrag(const uint8_t* q_fp8, int64_t q, int head, bool live,
+                                             int lane) {
+  return to_frag(load_raw32(q_fp8 + (q * IH + head) * ID, live, lane));
 }
 
 // Weighted ReLU head sum of one accumulator fragment; lanes 0-15 end with the
@@ -84,7 +110,7 @@ __global__ __launch_bounds__(256) void score_query_kernel(ScoreArgs a, int64_t n
   const int nv_pos = visible_count(a.q_pos[q]);
   const int64_t nv = nv_pos < a.n_entries ? nv_pos : a.n_entries;
   const int row = lane & 15;
-  const i32x8 afrag = load_qfrag(a.q_fp8, q, row, row < IH, lane);
+  const Frag16 afrag = load_qfrag(a.q_fp8, q, row, row < IH, lane);
   float w4[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -95,7 +121,7 @@ __global__ __launch_bounds__(256) void score_query_kernel(ScoreArgs a, int64_t n
   const int64_t nblk = (ncols + 7) >> 3;
   const int64_t c_wave = (int64_t)blockIdx.x * SQ_COLS + wave * (SQ_COLS / 4);
   for (int f0 = 0; f0 < SQ_COLS / 4 / 16; f0 += SQ_UNROLL) {
-    i32x8 b[SQ_UNROLL];
+    Raw32 b[SQ_UNROLL];
     bool valid[SQ_UNROLL];
 #pragma unroll
     for (int u = 0; u < SQ_UNROLL; ++u) {
@@ -109,12 +135,11 @@ __global__ __launch_bounds__(256) void score_query_kernel(ScoreArgs a, int64_t n
       }
       ok = ok && e < nv;
       valid[u] = ok;
-      b[u] = load_kfrag(kbase, e, ok, lane);
+      b[u] = load_raw32(kbase + e * ID, ok, lane);
     }
 #pragma unroll
     for (int u = 0; u < SQ_UNROLL; ++u) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma_f8_16x16x128(afrag, b[u], acc);
+      f32x4 acc = frag_mma(afrag, to_frag(b[u]));
       float s = head_sum(acc, w4);
       int64_t col = c_wave + 16 * (f0 + u) + (lane & 15);
       float v = valid[u] ? s : -__builtin_huge_valf();
@@ -139,7 +164,7 @@ __global__ __launch_bounds__(256) void score_tile_kernel(ScoreArgs a, int64_t nc
   const int64_t qend = (seq + 1) * a.q_per_seq;
   const int64_t qbase = seq * a.q_per_seq + qs0;
   const int row = lane & 15;
-  i32x8 afrag[8];
+  Frag16 afrag[8];
   float w4[8][4];
   int64_t nvq[8];
   int64_t my_q[8];
@@ -183,11 +208,10 @@ __global__ __launch_bounds__(256) void score_tile_kernel(ScoreArgs a, int64_t nc
                      owner);
       continue;
     }
-    i32x8 b = load_kfrag(kbase, col, col < ncols && col < nv_max, lane);
+    const Frag16 b = to_frag(load_raw32(kbase + col * ID, col < ncols && col < nv_max, lane));
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma_f8_16x16x128(afrag[f], b, acc);
+      f32x4 acc = frag_mma(afrag[f], b);
       float s = head_sum(acc, w4[f]);
       float v = (col < nvq[f]) ? s : -__builtin_huge_valf();
       if (my_q[f] < qend)

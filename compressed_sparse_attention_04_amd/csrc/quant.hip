@@ -95,17 +95,22 @@ __global__ __launch_bounds__(256) void window_append_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Compression GEMM on the fp32 matrix cores: Y[i, o] = sum_k Xc[i, k] Wc[o, k]
+// Compression GEMM on the fp64 matrix cores: Y[i, o] = sum_k Xc[i, k] Wc[o, k]
 // with Xc[i] = the 4 token rows of entry i (2048 contiguous floats) and
-// Wc[o, i*512 + c] = W_i[o, c].  Tile 32 entries x 64 outputs, k-chunks of 32;
-// optional split-K over blockIdx.z writes partial sums to ypart[z].
+// Wc[o, i*512 + c] = W_i[o, c].  Every fp32 x fp32 product is exact in fp64,
+// and the chain (GEMM, RMSNorm, RoPE) stays in fp64 until the quantizer input
+// is rounded to fp32 once; so that input is the correctly rounded value of the
+// exact result except within ~1e-13 (relative) of an fp32 rounding boundary,
+// and the stored bytes do not depend on the summation order.
+// Tile 32 entries x 64 outputs, k-chunks of 32; optional split-K over
+// blockIdx.z writes partial sums to ypart[z].
 constexpr int CG_BM = 32, CG_BN = 64, CG_BK = 32, CG_PITCH = CG_BK + 1;
 
 __global__ __launch_bounds__(256) void compress_gemm_kernel(const float* __restrict__ x,
                                                             int64_t n_seq, int64_t n_per_seq,
                                                             int64_t x_seq_stride,
                                                             const float* __restrict__ w,
-                                                            float* __restrict__ ypart,
+                                                            double* __restrict__ ypart,
                                                             int k_per_split) {
   __shared__ float As[CG_BM][CG_PITCH];
   __shared__ float Bs[CG_BN][CG_PITCH];
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(256) void compress_gemm_kernel(const float* __restr
   }
   const int wr = (wave >> 1) * 16;          // wave's row offset in the tile
   const int wc = (wave & 1) * 32;           // wave's column offset
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
   for (int k0 = kbeg; k0 < kend; k0 += CG_BK) {
     float4 av = a_src ? *reinterpret_cast<const float4*>(a_src + k0 + a_k4)
                       : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -151,17 +156,17 @@ __global__ __launch_bounds__(256) void compress_gemm_kernel(const float* __restr
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < CG_BK; kk += 4) {
-      float a = As[wr + (lane & 15)][kk + (lane >> 4)];
-      float b0 = Bs[wc + (lane & 15)][kk + (lane >> 4)];
-      float b1 = Bs[wc + 16 + (lane & 15)][kk + (lane >> 4)];
-      acc0 = mfma_f32_16x16x4(a, b0, acc0);
-      acc1 = mfma_f32_16x16x4(a, b1, acc1);
+      double a = As[wr + (lane & 15)][kk + (lane >> 4)];
+      double b0 = Bs[wc + (lane & 15)][kk + (lane >> 4)];
+      double b1 = Bs[wc + 16 + (lane & 15)][kk + (lane >> 4)];
+      acc0 = mfma_f64_16x16x4(a, b0, acc0);
+      acc1 = mfma_f64_16x16x4(a, b1, acc1);
     }
   }
-  float* yp = ypart + (int64_t)blockIdx.z * n * D;
+  double* yp = ypart + (int64_t)blockIdx.z * n * D;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    int64_t row = r0 + wr + 4 * (lane >> 4) + r;
+    int64_t row = r0 + wr + (lane >> 4) + 4 * r;      // fp64 16x16x4 result layout
     if (row < n) {
       yp[row * D + o0 + wc + (lane & 15)] = acc0[r];
       yp[row * D + o0 + wc + 16 + (lane & 15)] = acc1[r];
@@ -169,11 +174,11 @@ __global__ __launch_bounds__(256) void compress_gemm_kernel(const float* __restr
   }
 }
 
-// RMSNorm + RoPE + quantize + packed store.  16 lanes per entry (32 channels
-// per lane), 16 entries per 256-thread block.  Sums the split-K partials in a
-// fixed order.
+// RMSNorm + RoPE (fp64) + quantize + packed store.  16 lanes per entry (32
+// channels per lane), 16 entries per 256-thread block.  Sums the split-K
+// partials in a fixed order.
 __global__ __launch_bounds__(256) void compress_epilogue_kernel(
-    const float* __restrict__ ypart, int n_split, int64_t n_seq, int64_t n_per_seq,
+    const double* __restrict__ ypart, int n_split, int64_t n_seq, int64_t n_per_seq,
     const float* __restrict__ rope_cs, int rope_dim, float eps, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, int64_t out_seq_stride, float* __restrict__ e_out) {
   const int64_t n = n_seq * n_per_seq;
@@ -182,26 +187,26 @@ __global__ __launch_bounds__(256) void compress_epilogue_kernel(
   int lane16 = (int)(t & 15);
   bool live = entry < n;
   int64_t ent = live ? entry : 0;
-  float v[32];
+  double y[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = 0.f;
+  for (int i = 0; i < 32; ++i) y[i] = 0.0;
   for (int z = 0; z < n_split; ++z) {
-    const float4* src = reinterpret_cast<const float4*>(ypart + ((int64_t)z * n + ent) * D + 32 * lane16);
+    const double2* src = reinterpret_cast<const double2*>(ypart + ((int64_t)z * n + ent) * D + 32 * lane16);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float4 f = src[i];
-      v[4 * i] += f.x; v[4 * i + 1] += f.y; v[4 * i + 2] += f.z; v[4 * i + 3] += f.w;
+    for (int i = 0; i < 16; ++i) {
+      double2 f = src[i];
+      y[2 * i] += f.x;
+      y[2 * i + 1] += f.y;
     }
   }
-  float ss = 0.f;
+  double ss = 0.0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) ss = fmaf(v[i], v[i], ss);
-  // reduce over the 16 lanes of this entry
+  for (int i = 0; i < 32; ++i) ss = fma(y[i], y[i], ss);
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 16);
-  float inv = 1.0f / sqrtf(ss * (1.0f / (float)D) + eps);
+  const double inv = 1.0 / sqrt(ss * (1.0 / (double)D) + (double)eps);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] *= inv;
+  for (int i = 0; i < 32; ++i) y[i] *= inv;
   const int c_lane = 32 * lane16;
   const int c0 = D - rope_dim;
   if (rope_dim > 0 && c_lane + 32 > c0) {
@@ -211,14 +216,17 @@ __global__ __launch_bounds__(256) void compress_epilogue_kernel(
       int c = c_lane + i;
       if (c >= c0) {
         int pi = (c - c0) >> 1;
-        float cs_c = cs[2 * pi], cs_s = cs[2 * pi + 1];
-        float x0 = v[i], x1 = v[i + 1];
-        v[i] = x0 * cs_c - x1 * cs_s;
-        v[i + 1] = x0 * cs_s + x1 * cs_c;
+        double cs_c = cs[2 * pi], cs_s = cs[2 * pi + 1];
+        double x0 = y[i], x1 = y[i + 1];
+        y[i] = x0 * cs_c - x1 * cs_s;
+        y[i + 1] = x0 * cs_s + x1 * cs_c;
       }
     }
   }
   if (!live) return;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = (float)y[i];
   if (e_out) {
     float4* dst = reinterpret_cast<float4*>(e_out + entry * D + c_lane);
 #pragma unroll
@@ -265,7 +273,7 @@ int compress_split_k(int64_t n) {
 }
 
 size_t compress_workspace_bytes(int64_t n) {
-  return (size_t)compress_split_k(n) * (size_t)n * D * sizeof(float);
+  return (size_t)compress_split_k(n) * (size_t)n * D * sizeof(double);
 }
 
 hipError_t launch_compress_quant(const float* x, int64_t n_seq, int64_t n_per_seq,
@@ -275,7 +283,7 @@ hipError_t launch_compress_quant(const float* x, int64_t n_seq, int64_t n_per_se
   int64_t n = n_seq * n_per_seq;
   if (n == 0) return hipSuccess;
   int split = compress_split_k(n);
-  float* ypart = reinterpret_cast<float*>(ws);
+  double* ypart = reinterpret_cast<double*>(ws);
   dim3 grid(D / CG_BN, (unsigned)((n + CG_BM - 1) / CG_BM), split);
   hipLaunchKernelGGL(compress_gemm_kernel, grid, dim3(256), 0, st, x, n_seq, n_per_seq, x_seq_stride,
                      w, ypart, (4 * D) / split);

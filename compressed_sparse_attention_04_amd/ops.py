@@ -308,7 +308,8 @@ class LayerCall:
         self.ws = None
         if ws is None and alloc_ws:
             ws = _workspace(self.ws_need, dev)
-        self.set_workspace(ws)
+        if ws is not None or alloc_ws:
+            self.set_workspace(ws)
 
     def set_workspace(self, ws):
         """Use ``ws`` (uint8 tensor of at least ``ws_need`` bytes, or None when none is needed)."""

@@ -113,3 +113,23 @@ def test_layer_validation(lib):
     a.top_k = 0
     assert lib.csa_layer_reuse(ctypes.byref(a), None) == UNSUPPORTED
     assert lib.csa_layer_workspace_size(7, ctypes.byref(a)) == 0
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(),
+                    reason="would launch on fake pointers; host-only check")
+def test_valid_layer_args_pass_validation(lib):
+    """With valid arguments validation succeeds and the launch is attempted;
+    without a GPU that launch reports CSA_ERR_HIP (status 5)."""
+    a = _lib.CsaLayerArgs()
+    for f in ["codes", "scales", "k_fp8", "win", "q_pos", "q_attn", "q_idx", "w_idx", "pool_blocks",
+              "idx", "out"]:
+        setattr(a, f, 1 << 20)
+    a.kv_rows = a.k_rows = a.n_entries = 1000
+    a.win_cap, a.n_seq, a.q_per_seq = 128, 2, 1
+    a.sm_scale, a.top_k, a.build_pool, a.n_pool_blocks = 0.044, 512, 1, 2048
+    need = [lib.csa_layer_workspace_size(m, ctypes.byref(a)) for m in (0, 1, 2)]
+    a.ws, a.ws_bytes = 1 << 20, max(need)
+    for fn in (lib.csa_layer_full, lib.csa_layer_reindex, lib.csa_layer_reuse):
+        assert fn(ctypes.byref(a), None) == 5, lib.csa_last_error()
+    a.ws_bytes = need[0] - 1
+    assert lib.csa_layer_full(ctypes.byref(a), None) == WORKSPACE

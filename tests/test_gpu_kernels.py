@@ -82,10 +82,10 @@ def test_window_append_bit_exact(n_seq, n_tok, cap, p0):
 
 
 def test_compress_quant_chain():
-    """fp32 GPU chain vs the fp64 oracle: the quantizer input agrees to fp32
-    accuracy, its bytes equal the oracle's quantization of the GPU's own fp32
-    input, and any code that differs from the fp64 chain's sits at a rounding
-    boundary."""
+    """The GPU chain (fp64 GEMM, RMSNorm, RoPE; one rounding to fp32) gives the
+    fp32 rounding of the oracle's fp64 result, up to one fp32 ulp where the
+    exact value sits on an fp32 rounding boundary; its bytes equal the oracle's
+    quantization of the GPU's own fp32 input (strict), and of the oracle chain."""
     rng = np.random.default_rng(2)
     n_seq, n_per, rows = 3, 37, 50
     x = rng.standard_normal((n_seq, 4 * n_per, 512)).astype(np.float32)
@@ -101,16 +101,14 @@ def test_compress_quant_chain():
     e_gpu = np_(e_out).reshape(n_seq, n_per, 512)
     gc, gs = np_(codes), np_(scales)
     assert not gc[:, :5].any() and not gc[:, 5 + n_per:].any()
-    flips = 0
     for s in range(n_seq):
-        e_ref64 = oracle.rope_rotate(oracle.compress(x[s], w, 1e-6), cs[s], 64)
-        np.testing.assert_allclose(e_gpu[s], e_ref64, rtol=0, atol=2e-5)
+        e_ref32 = oracle.compress_rope_fp32(x[s], w, cs[s], 64, 1e-6)
+        ulps = np.abs(e_gpu[s].view(np.int32).astype(np.int64) - e_ref32.view(np.int32).astype(np.int64))
+        assert ulps.max() <= 1 and (ulps > 0).mean() < 1e-3, (ulps.max(), (ulps > 0).mean())
         c2, s2 = mxfp4.quantize(e_gpu[s])                 # strict: same fp32 input -> same bytes
-        assert np.array_equal(gc[s, 5:5 + n_per], c2)
-        assert np.array_equal(gs[s, 5:5 + n_per], s2)
-        rc, rsc = mxfp4.quantize(e_ref64.astype(np.float32))
-        flips += int((rc != c2).sum() + (rsc != s2).sum())
-    assert flips <= 3, flips
+        assert np.array_equal(gc[s, 5:5 + n_per], c2) and np.array_equal(gs[s, 5:5 + n_per], s2)
+        rc, rsc = mxfp4.quantize(e_ref32)                 # chain level
+        assert np.array_equal(rc, c2) and np.array_equal(rsc, s2)
 
 
 def _scores_case(rng, n_seq, q_per_seq, n_entries, k_rows, pos_base):
