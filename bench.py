@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Benchmark of one CSA2 layer-group step on one MI355X.
+
+Default workload (the headline): decode, batch 32 x 1,048,576-token context
+(262,144 MXFP4 entries per sequence), Full layer + hierarchical pool + 3
+Reindex layers.  A step is the whole hot path on one batch: window append,
+compression + MXFP4 store of the entry the newest tokens complete, Full-layer
+scoring / Top-512 / pool, three Reindex rescorings / Top-512, four sparse
+attentions.  Secondary lines: the 128K decode (Full + 5 Reuse) and the 256K
+prefill (Full, Reuse, Reuse, Reindex, Reuse) with its indexer TFLOPS.
+
+Inputs are synthetic and seeded (workloads module) and already resident in
+HBM when timing starts.  Each step is replayed from a captured HIP graph of
+the library's launches.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+"""
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s + achieved HBM GB/s at 128K/1M ctx; prefill indexer TFLOPS"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16 matrix peak
+F8_PEAK_TFLOPS = 5000.0        # MI355X dense fp8 matrix peak (reference only)
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ sizes ----
+
+def visible_sum(cfg):
+    """sum over queries of the visible entries (decode: all; prefill: causal)."""
+    if cfg.kind == "decode":
+        return cfg.n_seq * cfg.entries_total
+    return cfg.n_seq * sum((cfg.ctx_tokens + i + 1) // 4 for i in range(cfg.chunk))
+
+
+def algorithmic_bytes(cfg):
+    """Minimum HBM bytes of one step (reads + writes the method needs)."""
+    Q = cfg.n_queries
+    b = 0
+    n_idx = sum(1 for m in cfg.layers if m in ("F", "I"))
+    for m in cfg.layers:
+        if m == "F":
+            b += visible_sum(cfg) * 128                    # indexer keys
+        elif m == "I":
+            b += Q * (16384 if cfg.build_pool else cfg.entries_total) * 128
+    b += Q * n_idx * (8 * 128 + 8 * 4)                      # indexer queries + weights
+    per_attn = 512 * 288 + 128 * 512 + 2 * 16 * 512 * 4     # entries, window, q, out
+    b += len(cfg.layers) * Q * per_attn
+    new_tok = 1 if cfg.kind == "decode" else cfg.chunk
+    b += cfg.n_seq * cfg.new_entries * (4 * 512 * 4 + 288) + 4 * 512 * 512 * 4   # compress
+    b += cfg.n_seq * new_tok * (512 * 4 + 512)                                  # window
+    return b
+
+
+def indexer_flops(cfg):
+    return 2 * 8 * 128 * visible_sum(cfg)
+
+
+# ------------------------------------------------------------- GPU timing ----
+
+def build_steps(cfg, n_inst):
+    import torch
+    import workloads as W
+    from compressed_sparse_attention_04_amd.step import from_workload
+    insts = []
+    for k in range(n_inst):
+        c = dataclasses.replace(cfg, cid=cfg.cid + 1000 * k) if k else cfg
+        wl = W.make_workload(c, device="cuda")
+        st = from_workload(wl)
+        st.setup()
+        insts.append((wl, st))
+    torch.cuda.synchronize()
+    return insts
+
+
+def capture(st, use_graph):
+    import torch
+    if not use_graph:
+        return st.step
+    st.step()                       # allocate per-call workspaces before capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.step()
+    torch.cuda.synchronize()
+    return g.replay
+
+
+def time_step(runs, steps, warmup):
+    import torch
+    n = len(runs)
+    for i in range(warmup):
+        runs[i % n]()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        runs[i % n]()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def time_kernel(fn, reps):
+    """Average duration of fn's launch(es) on the current stream, HIP events."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / reps
+
+
+def dense_score_call(wl, st, block_max):
+    """The Full layer's dense indexer launch, with the step's own inputs."""
+    import torch
+    from compressed_sparse_attention_04_amd import ops
+    cfg, t = wl.cfg, wl.tensors
+    li = cfg.layers.index("F")
+    Q, nc = cfg.n_queries, st.n_entries
+    scores = torch.empty((Q, nc), dtype=torch.float32, device="cuda")
+    bm = torch.empty((Q, (nc + 7) // 8), dtype=torch.float32, device="cuda") if block_max else None
+    lib = ops._lib.load()
+    args = (ops._p(t["q_fp8"][li]), ops._p(t["w_idx"][li]), ops._p(t["q_pos"]), cfg.n_seq, st.q_per_seq,
+            ops._p(t["k_fp8"]), t["k_fp8"].shape[1], nc, None, 0, ops._p(scores), ops._p(bm))
+
+    def fn():
+        rc = lib.csa_index_score(*args, ops._stream())
+        if rc:
+            raise RuntimeError(lib.csa_last_error().decode())
+    return fn, scores, bm
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "compressed_sparse_attention_04_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel_key, digest):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(PROFILE_DIR, "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        e = data["kernels"][kernel_key]
+        if e.get("source_digest") != digest:
+            return None
+        cal = data["copy_calibration"]
+        f = cal["bytes_read"] / (cal["fetch_kib"] * 1024.0)
+        w = cal["bytes_written"] / (cal["write_kib"] * 1024.0)
+        return e["fetch_kib"] * 1024.0 * f + e["write_kib"] * 1024.0 * w
+    except (KeyError, ValueError, ZeroDivisionError):
+        return None
+
+
+def measure_config(cid, steps, warmup, use_graph, kernel_reps):
+    import torch
+    import workloads as W
+    cfg = W.CONFIGS[cid]
+    n_inst = 2 if cid == 2 else 1            # 128K: alternate two caches so the MALL cannot hold K_I
+    log(f"[bench] config {cid} {cfg.name}: building {n_inst} instance(s)")
+    insts = build_steps(cfg, n_inst)
+    runs = [capture(st, use_graph) for _, st in insts]
+    ms = time_step(runs, steps, warmup)
+    log(f"[bench] config {cid}: {ms:.3f} ms/step")
+    wl, st = insts[0]
+    res = {"workload": cfg.name, "ms_per_step": ms, "algorithmic_bytes": algorithmic_bytes(cfg)}
+    res["hbm_gbps"] = res["algorithmic_bytes"] / (ms * 1e-3) / 1e9
+    if cfg.kind == "decode":
+        res["tokens_per_s"] = cfg.n_seq / (ms * 1e-3)
+    else:
+        res["tokens_per_s"] = cfg.n_queries / (ms * 1e-3)
+    # dominant kernel: the Full layer's dense indexer launch
+    fn, _, _ = dense_score_call(wl, st, block_max=cfg.build_pool and cfg.kind == "decode")
+    kms = time_kernel(fn, kernel_reps)
+    res["indexer_ms"] = kms
+    if cfg.kind == "decode":
+        nc = st.n_entries
+        per = visible_sum(cfg) * 128 + cfg.n_queries * nc * 4
+        if cfg.build_pool:
+            per += cfg.n_queries * ((nc + 7) // 8) * 4
+        res["indexer_bytes"] = per
+        res["indexer_gbps"] = per / (kms * 1e-3) / 1e9
+    else:
+        res["indexer_tflops"] = indexer_flops(cfg) / (kms * 1e-3) / 1e12
+    del insts, runs, wl, st
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------ CPU baseline ----
+
+def cpu_baseline(cid, n_sample):
+    """The oracle, as it stands, on a bounded sample of the workload."""
+    import torch
+    import workloads as W
+    from oracle.runner import OracleStep
+    cfg = W.CONFIGS[cid]
+    wl = W.make_workload(cfg, device="cuda")
+    sub_cfg = dataclasses.replace(cfg, n_seq=n_sample)
+    host = {}
+    for k, v in wl.tensors.items():
+        if isinstance(v, list):
+            host[k] = [None if x is None else x[:n_sample * cfg.chunk].cpu() for x in v]
+        elif k == "q_pos":
+            host[k] = v[:n_sample * cfg.chunk].cpu()
+        elif k == "w":
+            host[k] = v.cpu()
+        else:
+            host[k] = v[:n_sample].cpu()
+    del wl
+    torch.cuda.empty_cache()
+    sub = W.Workload(sub_cfg, host)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=None)
+    except Exception:
+        pass
+    ref = OracleStep(sub)
+    t0 = time.perf_counter()
+    for qi in range(sub_cfg.n_queries):
+        ref.query(qi)
+    dt = time.perf_counter() - t0
+    return {"value": sub_cfg.n_queries / dt, "unit": "tokens/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"{n_sample} of {cfg.n_seq} sequences of {cfg.name}, whole layer group "
+                      f"(numpy float64 on the host), {dt:.1f} s"}
+
+
+# --------------------------------------------------------------------- main ----
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=16)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB copy kernel (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(sequences shard with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import workloads as W
+    from compressed_sparse_attention_04_amd import ops
+    ops._lib.load()
+    main_res = measure_config(args.config, args.steps, args.warmup, not args.no_graph,
+                              kernel_reps=max(5, args.steps))
+    cfg = W.CONFIGS[args.config]
+    digest = source_digest(["index.hip", "common.h"])
+    if cfg.kind == "decode":
+        key = "score_query_dense_" + cfg.name
+        achieved = main_res["indexer_gbps"]
+        traffic = counter_traffic(key, digest)
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": None if traffic is None else int(traffic),
+                    "kernel": "score_query_kernel<false> (Full-layer dense indexer)",
+                    "algorithmic_bytes_per_launch": main_res["indexer_bytes"],
+                    "avg_launch_ms": round(main_res["indexer_ms"], 4)}
+        value, unit = main_res["tokens_per_s"], "tokens/s"
+    else:
+        key = "score_tile_" + cfg.name
+        achieved = main_res["indexer_tflops"]
+        traffic = counter_traffic(key, digest)
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": F16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / F16_PEAK_TFLOPS, 4),
+                    "traffic": None if traffic is None else int(traffic),
+                    "kernel": "score_tile_kernel (Full-layer dense indexer, fp16 MFMA)",
+                    "flops_per_launch": indexer_flops(cfg),
+                    "avg_launch_ms": round(main_res["indexer_ms"], 4)}
+        value, unit = main_res["tokens_per_s"], "tokens/s"
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(main_res["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.n_seq, "context_tokens": cfg.ctx_tokens,
+                   "entries_per_seq": cfg.entries_total, "layers": "".join(cfg.layers),
+                   "hierarchical_pool": cfg.build_pool},
+        "hbm_gbps": round(main_res["hbm_gbps"], 1),
+        "hbm_frac": round(main_res["hbm_gbps"] / HBM_PEAK_GBS, 4),
+        "roofline": roofline,
+    }
+    if not args.no_secondary:
+        sec = {}
+        for cid in (2, 4):
+            if cid == args.config:
+                continue
+            r = measure_config(cid, max(3, args.steps // 2), max(1, args.warmup // 2), not args.no_graph,
+                               kernel_reps=max(3, args.steps // 2))
+            e = {"ms_per_step": round(r["ms_per_step"], 4), "tokens_per_s": round(r["tokens_per_s"], 1),
+                 "hbm_gbps": round(r["hbm_gbps"], 1)}
+            if "indexer_tflops" in r:
+                e["indexer_tflops"] = round(r["indexer_tflops"], 1)
+                e["indexer_frac_f16_peak"] = round(r["indexer_tflops"] / F16_PEAK_TFLOPS, 4)
+                e["indexer_frac_f8_peak"] = round(r["indexer_tflops"] / F8_PEAK_TFLOPS, 4)
+            else:
+                e["indexer_gbps"] = round(r["indexer_gbps"], 1)
+            sec[r["workload"]] = e
+        out["secondary"] = sec
+    if args.calib_copy:
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = src.numel() * 4
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,92 @@
+"""The oracle's version of one layer-group step of a seeded workload.
+
+TEST INFRASTRUCTURE ONLY (see the package header).  It reads the workload's
+input tensors (copying one sequence at a time to the host) and runs the
+oracle functions of this package on them; nothing here touches the GPU path.
+"""
+
+import numpy as np
+
+from .attention import window_positions
+from .compressor import compress, rope_rotate
+from .layer import layer_full, layer_reindex, layer_reuse, window_encode
+from .mxfp4 import quantize
+
+SM = 512 ** -0.5
+
+
+def _np(t):
+    return t.detach().cpu().numpy() if hasattr(t, "detach") else np.asarray(t)
+
+
+class OracleStep:
+    """The oracle's version of one step of a workload, built lazily per sequence."""
+
+    def __init__(self, wl):
+        self.wl = wl
+        self.cfg = wl.cfg
+        t = wl.tensors
+        self.w = _np(t["w"]).astype(np.float64)
+        self._cache = {}
+
+    def cache(self, s):
+        """(codes, scales, k_fp8, x_tail) of sequence s after the step's compression."""
+        if s in self._cache:
+            return self._cache[s]
+        cfg, t = self.cfg, self.wl.tensors
+        prior, new = cfg.prior_entries, cfg.new_entries
+        codes = _np(t["codes"][s]).copy()
+        scales = _np(t["scales"][s]).copy()
+        e64 = np.full((cfg.entries_total, 512), np.nan)      # pre-quantization values (computed rows)
+        if not cfg.synthetic_cache and prior > 0:
+            e = rope_rotate(compress(_np(t["x_prior"][s]), self.w, 1e-6),
+                                   _np(t["rope_prior"][s]), 64)
+            e64[:prior] = e
+            codes[:prior], scales[:prior] = quantize(e.astype(np.float32))
+        x_tail = _np(t["x_tail"][s])
+        toks = x_tail[x_tail.shape[0] - 4 * new:]
+        e = rope_rotate(compress(toks, self.w, 1e-6), _np(t["rope_cs"][s]), 64)
+        e64[prior:prior + new] = e
+        codes[prior:prior + new], scales[prior:prior + new] = quantize(e.astype(np.float32))
+        k_fp8 = _np(t["k_fp8"][s])
+        self._cache[s] = (codes, scales, k_fp8, x_tail)
+        self._e64 = getattr(self, "_e64", {})
+        self._e64[s] = e64
+        return self._cache[s]
+
+    def e64(self, s):
+        self.cache(s)
+        return self._e64[s]
+
+    def window(self, s, p):
+        """E4M3 bytes of the window tokens of a query at position p."""
+        cfg = self.cfg
+        x_tail = self.cache(s)[3]
+        first = (cfg.ctx_tokens - 128) if cfg.kind == "decode" else (cfg.ctx_tokens - 127)
+        pos = window_positions(p)
+        return window_encode(x_tail[pos - first])
+
+    def query(self, qi):
+        """Per-layer oracle results for query qi: list of LayerState."""
+        cfg, t = self.cfg, self.wl.tensors
+        s = qi // cfg.chunk
+        p = int(t["q_pos"][qi])
+        codes, scales, k_fp8, _ = self.cache(s)
+        win = self.window(s, p)
+        n_entries = cfg.entries_total
+        res, idx, pool = [], None, None
+        for li, mode in enumerate(cfg.layers):
+            qa = _np(t["q_attn"][li][qi])
+            if mode == "F":
+                st = layer_full(codes, scales, k_fp8, _np(t["q_fp8"][li][qi]),
+                                       _np(t["w_idx"][li][qi]), qa, p, win, SM,
+                                       build_pool=cfg.build_pool, n_entries=n_entries)
+                pool = st.pool
+            elif mode == "I":
+                st = layer_reindex(codes, scales, k_fp8, pool, _np(t["q_fp8"][li][qi]),
+                                          _np(t["w_idx"][li][qi]), qa, p, win, SM, n_entries=n_entries)
+            else:
+                st = layer_reuse(codes, scales, idx, qa, win, SM)
+            idx = st.idx
+            res.append(st)
+        return res

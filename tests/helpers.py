@@ -101,74 +101,4 @@ def cache_flips(gpu_codes, gpu_scales, ref_codes, ref_scales, ref_e64, rows, tol
     return flipped
 
 
-class OracleStep:
-    """The oracle's version of one step of a workload, built lazily per sequence."""
-
-    def __init__(self, wl):
-        self.wl = wl
-        self.cfg = wl.cfg
-        t = wl.tensors
-        self.w = np_(t["w"]).astype(np.float64)
-        self._cache = {}
-
-    def cache(self, s):
-        """(codes, scales, k_fp8, x_tail) of sequence s after the step's compression."""
-        if s in self._cache:
-            return self._cache[s]
-        cfg, t = self.cfg, self.wl.tensors
-        prior, new = cfg.prior_entries, cfg.new_entries
-        codes = np_(t["codes"][s]).copy()
-        scales = np_(t["scales"][s]).copy()
-        e64 = np.full((cfg.entries_total, 512), np.nan)      # pre-quantization values (computed rows)
-        if not cfg.synthetic_cache and prior > 0:
-            e = oracle.rope_rotate(oracle.compress(np_(t["x_prior"][s]), self.w, 1e-6),
-                                   np_(t["rope_prior"][s]), 64)
-            e64[:prior] = e
-            codes[:prior], scales[:prior] = mxfp4.quantize(e.astype(np.float32))
-        x_tail = np_(t["x_tail"][s])
-        toks = x_tail[x_tail.shape[0] - 4 * new:]
-        e = oracle.rope_rotate(oracle.compress(toks, self.w, 1e-6), np_(t["rope_cs"][s]), 64)
-        e64[prior:prior + new] = e
-        codes[prior:prior + new], scales[prior:prior + new] = mxfp4.quantize(e.astype(np.float32))
-        k_fp8 = np_(t["k_fp8"][s])
-        self._cache[s] = (codes, scales, k_fp8, x_tail)
-        self._e64 = getattr(self, "_e64", {})
-        self._e64[s] = e64
-        return self._cache[s]
-
-    def e64(self, s):
-        self.cache(s)
-        return self._e64[s]
-
-    def window(self, s, p):
-        """E4M3 bytes of the window tokens of a query at position p."""
-        cfg = self.cfg
-        x_tail = self.cache(s)[3]
-        first = (cfg.ctx_tokens - 128) if cfg.kind == "decode" else (cfg.ctx_tokens - 127)
-        pos = oracle.window_positions(p)
-        return oracle.window_encode(x_tail[pos - first])
-
-    def query(self, qi):
-        """Per-layer oracle results for query qi: list of LayerState."""
-        cfg, t = self.cfg, self.wl.tensors
-        s = qi // cfg.chunk
-        p = int(t["q_pos"][qi])
-        codes, scales, k_fp8, _ = self.cache(s)
-        win = self.window(s, p)
-        n_entries = cfg.entries_total
-        res, idx, pool = [], None, None
-        for li, mode in enumerate(cfg.layers):
-            qa = np_(t["q_attn"][li][qi])
-            if mode == "F":
-                st = oracle.layer_full(codes, scales, k_fp8, np_(t["q_fp8"][li][qi]),
-                                       np_(t["w_idx"][li][qi]), qa, p, win, SM,
-                                       build_pool=cfg.build_pool, n_entries=n_entries)
-                pool = st.pool
-            elif mode == "I":
-                st = oracle.layer_reindex(codes, scales, k_fp8, pool, np_(t["q_fp8"][li][qi]),
-                                          np_(t["w_idx"][li][qi]), qa, p, win, SM, n_entries=n_entries)
-            else:
-                st = oracle.layer_reuse(codes, scales, idx, qa, win, SM)
-            idx = st.idx
-            res.append(st)
-        return res
+from oracle.runner import OracleStep  # noqa: E402,F401
