@@ -51,9 +51,14 @@ size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
   } while (0)
 
 // Workspace plan of a layer call: offsets of its scratch buffers.
+// Full layers select their Top-K among the entries of the best blocks: the
+// top-P blocks by (block max desc, block id asc) contain every Top-K entry
+// whenever P >= K (a block ranked above the block of a Top-K entry e has a
+// max >= s(e), equality only at a lower block id, whose entry then ties with
+// and precedes e).  P is the pool when one is built, else K blocks.
 struct LayerPlan {
   int64_t Q = 0, ncols = 0, nblk = 0;
-  size_t off_scores = 0, off_bm = 0, off_sel = 0, off_attn = 0, total = 0;
+  size_t off_scores = 0, off_bm = 0, off_blocks = 0, off_sel = 0, off_attn = 0, total = 0;
   bool pooled = false;
 };
 
@@ -66,13 +71,21 @@ LayerPlan plan_layer(int32_t mode, const csa_layer_args* a) {
     p.ncols = p.pooled ? (int64_t)CSA_BLOCK * a->n_pool_blocks : a->n_entries;
     p.off_scores = off;
     off += round_up((size_t)(p.Q * p.ncols) * sizeof(float));
-    size_t sel = topk_workspace_bytes(p.Q, p.ncols, a->top_k);
-    if (mode == CSA_MODE_FULL && a->build_pool) {
+    size_t sel = 0;
+    if (mode == CSA_MODE_FULL) {
       p.nblk = (p.ncols + 7) / 8;
       p.off_bm = off;
       off += round_up((size_t)(p.Q * p.nblk) * sizeof(float));
-      size_t pool_ws = block_pool_workspace_bytes(p.Q, p.nblk, 1, a->n_pool_blocks);
-      sel = sel > pool_ws ? sel : pool_ws;
+      const int32_t nb = a->build_pool ? a->n_pool_blocks : a->top_k;
+      if (!a->build_pool) {
+        p.off_blocks = off;
+        off += round_up((size_t)(p.Q * nb) * sizeof(int32_t));
+      }
+      size_t pool_ws = block_pool_workspace_bytes(p.Q, p.nblk, 1, nb);
+      size_t gat_ws = topk_gather_workspace_bytes(p.Q, nb, a->top_k);
+      sel = pool_ws > gat_ws ? pool_ws : gat_ws;
+    } else {
+      sel = topk_workspace_bytes(p.Q, p.ncols, a->top_k);
     }
     p.off_sel = off;
     off += round_up(sel);
@@ -321,6 +334,9 @@ static csa_status check_layer(const char* fn, int32_t mode, const csa_layer_args
           "%s: n_pool_blocks must be in [1, 4096]", fn);
     CHECK_ALIGN(a->pool_blocks, 4);
   }
+  if (mode == CSA_MODE_FULL && a->build_pool)
+    CHECK(a->n_pool_blocks >= a->top_k, CSA_ERR_UNSUPPORTED,
+          "%s: the pool must hold at least top_k blocks", fn);
   *plan = plan_layer(mode, a);
   CHECK(plan->total == 0 || (a->ws != nullptr && a->ws_bytes >= plan->total), CSA_ERR_WORKSPACE,
         "%s: workspace needs %zu bytes", fn, plan->total);
@@ -354,20 +370,22 @@ static csa_status run_index(const char* fn, int32_t mode, const csa_layer_args* 
                             hipStream_t st) {
   char* ws = reinterpret_cast<char*>(a->ws);
   float* scores = reinterpret_cast<float*>(ws + p.off_scores);
-  float* bm = (mode == CSA_MODE_FULL && a->build_pool) ? reinterpret_cast<float*>(ws + p.off_bm) : nullptr;
+  float* bm = (mode == CSA_MODE_FULL) ? reinterpret_cast<float*>(ws + p.off_bm) : nullptr;
   ScoreArgs s{a->q_idx, a->w_idx, a->q_pos, a->n_seq, a->q_per_seq, a->k_fp8, a->k_rows, a->n_entries,
               p.pooled ? a->pool_blocks : nullptr, a->n_pool_blocks, scores, bm};
   csa_status r = hip_status(launch_index_score(s, st), fn);
   if (r != CSA_OK) return r;
-  r = hip_status(launch_topk(scores, p.Q, p.ncols, p.pooled ? a->pool_blocks : nullptr, a->top_k, a->idx,
-                             ws + p.off_sel, st),
-                 fn);
+  if (mode != CSA_MODE_FULL)
+    return hip_status(launch_topk(scores, p.Q, p.ncols, p.pooled ? a->pool_blocks : nullptr, a->top_k,
+                                  a->idx, ws + p.off_sel, st),
+                      fn);
+  // Full: best blocks (the pool, or top_k blocks), then Top-K among their entries
+  int32_t* blocks = a->build_pool ? a->pool_blocks : reinterpret_cast<int32_t*>(ws + p.off_blocks);
+  const int32_t nb = a->build_pool ? a->n_pool_blocks : a->top_k;
+  r = hip_status(launch_block_pool(bm, 1, p.Q, p.nblk, nb, blocks, ws + p.off_sel, st), fn);
   if (r != CSA_OK) return r;
-  if (bm) {
-    r = hip_status(launch_block_pool(bm, 1, p.Q, p.nblk, a->n_pool_blocks, a->pool_blocks, ws + p.off_sel, st),
-                   fn);
-  }
-  return r;
+  return hip_status(launch_topk_gather(scores, p.Q, p.ncols, blocks, nb, a->top_k, a->idx, ws + p.off_sel, st),
+                    fn);
 }
 
 csa_status csa_layer_full(const csa_layer_args* a, hipStream_t stream) {

@@ -34,30 +34,47 @@ __device__ __forceinline__ float e4m3_code_value(uint32_t c) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
-// RNE_E4M3FN(a / f) for a >= 0 and f in {1, 6}, saturating at 448.
-// Exact: it counts the rounding midpoints mid_i (between codes i and i+1)
-// with f * mid_i < a; f * mid_i has at most 7 significant bits, so it and the
-// comparisons are exact in fp32.  A tie (a == f * mid_i) goes to the even code.
-__device__ __forceinline__ uint32_t e4m3_rne_div(float a, float f) {
-  uint32_t lo = 0;
-#pragma unroll
-  for (uint32_t step = 64; step >= 1; step >>= 1) {
-    uint32_t c = lo + step;              // test midpoint c-1 (between c-1 and c)
-    if (c <= 126u) {
-      float mid = 0.5f * (e4m3_code_value(c - 1) + e4m3_code_value(c));
-      if (f * mid < a) lo = c;
-    }
-  }
-  if (lo < 126u && (lo & 1u)) {
-    float mid = 0.5f * (e4m3_code_value(lo) + e4m3_code_value(lo + 1));
-    if (f * mid == a) lo += 1;
-  }
-  return lo;
+// Non-negative E4M3FN code of RNE(v), saturating at 448 (v >= 0; NaN -> 0).
+// Normal range: v = f * 2^E, f in [1, 2): mantissa = rint((f - 1) * 8), a
+// carry to 8 moves to the next exponent; below 2^-6 the code is rint(v * 2^9)
+// (8 there is the smallest normal, code 0x08).  rint rounds half to even, and
+// the even integer is the code whose last bit is 0.  All steps are exact.
+__device__ __forceinline__ uint32_t e4m3_rne_f64(double v) {
+  if (!(v > 0.0)) return 0u;
+  if (v >= 448.0) return 0x7Eu;
+  if (v < 0x1p-6) return (uint32_t)rint(v * 512.0);
+  int e;
+  double f = frexp(v, &e);                 // v = f * 2^e, f in [0.5, 1)
+  int E = e - 1;
+  uint32_t m = (uint32_t)rint((2.0 * f - 1.0) * 8.0);
+  if (m == 8u) { m = 0u; E += 1; }
+  uint32_t c = ((uint32_t)(E + 7) << 3) | m;
+  return c > 0x7Eu ? 0x7Eu : c;
+}
+__device__ __forceinline__ uint32_t e4m3_rne_f32(float v) {
+  if (!(v > 0.f)) return 0u;
+  if (v >= 448.f) return 0x7Eu;
+  if (v < 0x1p-6f) return (uint32_t)rintf(v * 512.f);
+  int e;
+  float f = frexpf(v, &e);
+  int E = e - 1;
+  uint32_t m = (uint32_t)rintf((2.f * f - 1.f) * 8.f);
+  if (m == 8u) { m = 0u; E += 1; }
+  uint32_t c = ((uint32_t)(E + 7) << 3) | m;
+  return c > 0x7Eu ? 0x7Eu : c;
+}
+
+// Scale code RNE_E4M3(amax / 6): the quotient is formed in fp64, which takes
+// the same rounding decision as exact division (amax has 24 significant bits,
+// 6 and every E4M3 midpoint at most 5, so a quotient that is not exactly a
+// midpoint is at least ~2^-24 relative away from one; fp64 errs by 2^-53).
+__device__ __forceinline__ uint32_t e4m3_scale_code(float amax) {
+  return e4m3_rne_f64((double)amax / 6.0);
 }
 
 // Signed E4M3FN encode of x (RNE, saturating, sign bit of x kept).
 __device__ __forceinline__ uint32_t e4m3_encode(float x) {
-  uint32_t mag = e4m3_rne_div(fabsf(x), 1.0f);
+  uint32_t mag = e4m3_rne_f32(fabsf(x));
   return mag | ((__float_as_uint(x) >> 24) & 0x80u);
 }
 
@@ -71,7 +88,7 @@ __device__ __forceinline__ uint32_t mxfp4_group(const float* v, uint32_t codes8[
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  uint32_t sc = e4m3_rne_div(amax, 6.0f);
+  uint32_t sc = e4m3_scale_code(amax);
   float s = e4m3_code_value(sc);
   float t0 = s * 0.25f, t1 = s * 0.75f, t2 = s * 1.25f, t3 = s * 1.75f;
   float t4 = s * 2.5f, t5 = s * 3.5f, t6 = s * 5.0f;
@@ -91,6 +108,17 @@ __device__ __forceinline__ uint32_t mxfp4_group(const float* v, uint32_t codes8[
   codes8[0] = w0;
   codes8[1] = w1;
   return sc;
+}
+
+// One element's 4-bit code under scale value s (scale code sc): sign bit of x,
+// magnitude RNE_E2M1(|x| / s) decided by comparing |x| with s * midpoints.
+__device__ __forceinline__ uint32_t e2m1_code(float x, float s, uint32_t sc) {
+  float r = fabsf(x);
+  uint32_t c = (uint32_t)(r > s * 0.25f) + (uint32_t)(r >= s * 0.75f) + (uint32_t)(r > s * 1.25f) +
+               (uint32_t)(r >= s * 1.75f) + (uint32_t)(r > s * 2.5f) + (uint32_t)(r >= s * 3.5f) +
+               (uint32_t)(r > s * 5.0f);
+  c = (sc == 0u) ? 0u : c;
+  return c | ((__float_as_uint(x) >> 28) & 0x8u);
 }
 
 // E2M1 magnitude of a 3-bit code (exact): 0, .5, 1, 1.5, 2, 3, 4, 6.

@@ -41,6 +41,19 @@ __device__ __forceinline__ Raw32 load_raw32(const uint8_t* row, bool live, int l
   return r;
 }
 
+// Streaming variant: each indexer key row is read once per query, so the
+// loads are marked non-temporal (they need not stay in the caches).
+__device__ __forceinline__ Raw32 load_raw32_stream(const uint8_t* row, bool live, int lane) {
+  Raw32 r = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+  if (live) {
+    const i32x4* p = reinterpret_cast<const i32x4*>(row + 32 * (lane >> 4));
+    const i32x4 v0 = __builtin_nontemporal_load(p), v1 = __builtin_nontemporal_load(p + 1);
+    r.u0 = make_uint4((uint32_t)v0[0], (uint32_t)v0[1], (uint32_t)v0[2], (uint32_t)v0[3]);
+    r.u1 = make_uint4((uint32_t)v1[0], (uint32_t)v1[1], (uint32_t)v1[2], (uint32_t)v1[3]);
+  }
+  return r;
+}
+
 __device__ __forceinline__ f16x8 fp8x8_to_f16(uint32_t w0, uint32_t w1) {
   f16x2 a = fp8x2_to_f16<0>(w0), b = fp8x2_to_f16<1>(w0);
   f16x2 c = fp8x2_to_f16<0>(w1), d = fp8x2_to_f16<1>(w1);
@@ -120,31 +133,44 @@ __global__ __launch_bounds__(256) void score_query_kernel(ScoreArgs a, int64_t n
   const uint8_t* kbase = a.k_fp8 + seq * a.k_rows * ID;
   const int64_t nblk = (ncols + 7) >> 3;
   const int64_t c_wave = (int64_t)blockIdx.x * SQ_COLS + wave * (SQ_COLS / 4);
-  for (int f0 = 0; f0 < SQ_COLS / 4 / 16; f0 += SQ_UNROLL) {
-    Raw32 b[SQ_UNROLL];
-    bool valid[SQ_UNROLL];
+  constexpr int NFRAG = SQ_COLS / 4 / 16;
+  // entry of this lane's column in every fragment of the wave (pool ids first)
+  int64_t ent[NFRAG];
+  bool valid[NFRAG];
 #pragma unroll
-    for (int u = 0; u < SQ_UNROLL; ++u) {
-      int64_t col = c_wave + 16 * (f0 + u) + (lane & 15);
-      int64_t e = col;
-      bool ok = col < ncols;
-      if (POOLED && ok) {
-        int32_t blk = a.pool[q * a.n_pool_blocks + (col >> 3)];
-        ok = blk >= 0;
-        e = 8 * (int64_t)blk + (col & 7);
-      }
-      ok = ok && e < nv;
-      valid[u] = ok;
-      b[u] = load_raw32(kbase + e * ID, ok, lane);
+  for (int f = 0; f < NFRAG; ++f) {
+    const int64_t col = c_wave + 16 * f + (lane & 15);
+    int64_t e = col;
+    bool ok = col < ncols;
+    if (POOLED && ok) {
+      const int32_t blk = a.pool[q * a.n_pool_blocks + (col >> 3)];
+      ok = blk >= 0;
+      e = 8 * (int64_t)blk + (col & 7);
+    }
+    valid[f] = ok && e < nv;
+    ent[f] = e;
+  }
+  // software pipeline: the next SQ_UNROLL fragments load while these compute
+  Raw32 cur[SQ_UNROLL], nxt[SQ_UNROLL];
+#pragma unroll
+  for (int u = 0; u < SQ_UNROLL; ++u) cur[u] = load_raw32_stream(kbase + ent[u] * ID, valid[u], lane);
+#pragma unroll
+  for (int f0 = 0; f0 < NFRAG; f0 += SQ_UNROLL) {
+    if (f0 + SQ_UNROLL < NFRAG) {
+#pragma unroll
+      for (int u = 0; u < SQ_UNROLL; ++u)
+        nxt[u] = load_raw32_stream(kbase + ent[f0 + SQ_UNROLL + u] * ID, valid[f0 + SQ_UNROLL + u], lane);
     }
 #pragma unroll
     for (int u = 0; u < SQ_UNROLL; ++u) {
-      f32x4 acc = frag_mma(afrag, to_frag(b[u]));
+      f32x4 acc = frag_mma(afrag, to_frag(cur[u]));
       float s = head_sum(acc, w4);
       int64_t col = c_wave + 16 * (f0 + u) + (lane & 15);
-      float v = valid[u] ? s : -__builtin_huge_valf();
+      float v = valid[f0 + u] ? s : -__builtin_huge_valf();
       store_frag(v, q, col, ncols, nblk, a.scores, POOLED ? nullptr : a.block_max, lane, lane < 16);
     }
+#pragma unroll
+    for (int u = 0; u < SQ_UNROLL; ++u) cur[u] = nxt[u];
   }
 }
 

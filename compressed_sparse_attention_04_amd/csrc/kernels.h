@@ -40,6 +40,9 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t st);
 size_t topk_workspace_bytes(int64_t Q, int64_t ncols, int32_t k);
 hipError_t launch_topk(const float* scores, int64_t Q, int64_t ncols, const int32_t* col_blocks,
                        int32_t k, int32_t* idx, void* ws, hipStream_t st);
+size_t topk_gather_workspace_bytes(int64_t Q, int64_t nmap, int32_t k);
+hipError_t launch_topk_gather(const float* scores, int64_t Q, int64_t ncols, const int32_t* blocks,
+                              int64_t nmap, int32_t k, int32_t* idx, void* ws, hipStream_t st);
 size_t block_pool_workspace_bytes(int64_t Q, int64_t ncols, int32_t is_block_max, int32_t nb);
 hipError_t launch_block_pool(const float* values, int32_t is_block_max, int64_t Q, int64_t ncols,
                              int32_t nb, int32_t* pool, void* ws, hipStream_t st);

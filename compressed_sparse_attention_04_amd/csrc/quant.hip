@@ -174,67 +174,67 @@ __global__ __launch_bounds__(256) void compress_gemm_kernel(const float* __restr
   }
 }
 
-// RMSNorm + RoPE (fp64) + quantize + packed store.  16 lanes per entry (32
-// channels per lane), 16 entries per 256-thread block.  Sums the split-K
-// partials in a fixed order.
+// RMSNorm + RoPE (fp64) + quantize + packed store.  One 256-thread block per
+// entry, channels 2t and 2t+1 per thread (one RoPE pair).  The split-K
+// partials are loaded together and summed in a fixed order; a 16-channel scale
+// group is 8 adjacent threads.  The packed row is assembled in LDS and stored
+// with 16-byte stores (codes: 16 lanes x 16 B, scales: 2 lanes x 16 B).
+constexpr int CE_MAX_SPLIT = 16;
+
 __global__ __launch_bounds__(256) void compress_epilogue_kernel(
     const double* __restrict__ ypart, int n_split, int64_t n_seq, int64_t n_per_seq,
     const float* __restrict__ rope_cs, int rope_dim, float eps, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, int64_t out_seq_stride, float* __restrict__ e_out) {
+  __shared__ double red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t row_codes[CODE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t row_scales[SCALE_BYTES];
   const int64_t n = n_seq * n_per_seq;
-  int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  int64_t entry = t >> 4;
-  int lane16 = (int)(t & 15);
-  bool live = entry < n;
-  int64_t ent = live ? entry : 0;
-  double y[32];
+  const int64_t entry = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  double2 part[CE_MAX_SPLIT];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) y[i] = 0.0;
-  for (int z = 0; z < n_split; ++z) {
-    const double2* src = reinterpret_cast<const double2*>(ypart + ((int64_t)z * n + ent) * D + 32 * lane16);
+  for (int z = 0; z < CE_MAX_SPLIT; ++z)
+    if (z < n_split) part[z] = reinterpret_cast<const double2*>(ypart + ((int64_t)z * n + entry) * D)[t];
+  double y0 = 0.0, y1 = 0.0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      double2 f = src[i];
-      y[2 * i] += f.x;
-      y[2 * i + 1] += f.y;
-    }
-  }
-  double ss = 0.0;
+  for (int z = 0; z < CE_MAX_SPLIT; ++z)
+    if (z < n_split) { y0 += part[z].x; y1 += part[z].y; }
+  double ss = fma(y0, y0, y1 * y1);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) ss = fma(y[i], y[i], ss);
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 16);
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  ss = (red[0] + red[1]) + (red[2] + red[3]);
   const double inv = 1.0 / sqrt(ss * (1.0 / (double)D) + (double)eps);
-#pragma unroll
-  for (int i = 0; i < 32; ++i) y[i] *= inv;
-  const int c_lane = 32 * lane16;
-  const int c0 = D - rope_dim;
-  if (rope_dim > 0 && c_lane + 32 > c0) {
-    const float* cs = rope_cs + ent * (int64_t)rope_dim;   // [rope_dim/2][2]
-#pragma unroll
-    for (int i = 0; i < 32; i += 2) {
-      int c = c_lane + i;
-      if (c >= c0) {
-        int pi = (c - c0) >> 1;
-        double cs_c = cs[2 * pi], cs_s = cs[2 * pi + 1];
-        double x0 = y[i], x1 = y[i + 1];
-        y[i] = x0 * cs_c - x1 * cs_s;
-        y[i + 1] = x0 * cs_s + x1 * cs_c;
-      }
-    }
+  y0 *= inv;
+  y1 *= inv;
+  const int c = 2 * t;
+  if (rope_dim > 0 && c >= D - rope_dim) {
+    const float* cs = rope_cs + entry * (int64_t)rope_dim + 2 * ((c - (D - rope_dim)) >> 1);
+    const double cc = cs[0], sn = cs[1];
+    const double x0 = y0, x1 = y1;
+    y0 = x0 * cc - x1 * sn;
+    y1 = x0 * sn + x1 * cc;
   }
-  if (!live) return;
-  float v[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = (float)y[i];
-  if (e_out) {
-    float4* dst = reinterpret_cast<float4*>(e_out + entry * D + c_lane);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-  }
-  int64_t s = entry / n_per_seq, r = entry % n_per_seq;
-  int64_t row = s * out_seq_stride + r;
-  quantize32_store(v, codes + row * CODE_BYTES, scales + row * SCALE_BYTES, lane16);
+  const float v0 = (float)y0, v1 = (float)y1;
+  if (e_out) reinterpret_cast<float2*>(e_out + entry * D)[t] = make_float2(v0, v1);
+  // scale of the 16-channel group held by threads 8k .. 8k+7
+  float amax = fmaxf(fabsf(v0), fabsf(v1));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  const uint32_t sc = e4m3_scale_code(amax);
+  const float sv = e4m3_code_value(sc);
+  row_codes[t] = (uint8_t)(e2m1_code(v0, sv, sc) | (e2m1_code(v1, sv, sc) << 4));
+  if ((t & 7) == 0) row_scales[t >> 3] = (uint8_t)sc;
+  __syncthreads();
+  const int64_t s = entry / n_per_seq, r = entry % n_per_seq;
+  const int64_t row = s * out_seq_stride + r;
+  if (t < 16)
+    reinterpret_cast<uint4*>(codes + row * CODE_BYTES)[t] = reinterpret_cast<const uint4*>(row_codes)[t];
+  else if (t < 18)
+    reinterpret_cast<uint4*>(scales + row * SCALE_BYTES)[t - 16] =
+        reinterpret_cast<const uint4*>(row_scales)[t - 16];
 }
 
 // ------------------------------------------------------------- launchers --
@@ -289,8 +289,7 @@ hipError_t launch_compress_quant(const float* x, int64_t n_seq, int64_t n_per_se
                      w, ypart, (4 * D) / split);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int64_t blocks = (n * 16 + 255) / 256;
-  hipLaunchKernelGGL(compress_epilogue_kernel, dim3((unsigned)blocks), dim3(256), 0, st, ypart, split,
+  hipLaunchKernelGGL(compress_epilogue_kernel, dim3((unsigned)n), dim3(256), 0, st, ypart, split,
                      n_seq, n_per_seq, rope_cs, rope_dim, eps, codes, scales, out_seq_stride, e_out);
   return hipGetLastError();
 }

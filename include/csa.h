@@ -102,9 +102,8 @@ csa_status csa_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t n
  *   row s * out_seq_stride + r of codes [.., 256] / scales [.., 32].
  *   y = sum_i W_i x_i with w float32 [4, 512 (out), 512 (in)];
  *   e = y / sqrt(mean(y^2) + eps) (unit gain);
- *   RoPE on the last rope_dim channels (0 or an even number <= 512, multiple
- *   of 32 so that pairs never straddle a scale group boundary... any even value
- *   up to 512 is accepted), pairs (c, c+1) rotated by rope_cs
+ *   RoPE on the last rope_dim channels (rope_dim even, 0 <= rope_dim <= 512,
+ *   else CSA_ERR_UNSUPPORTED), pairs (c, c+1) rotated by rope_cs
  *   float32 [n_seq, n_per_seq, rope_dim / 2, 2] = (cos, sin); rope_cs may be
  *   NULL only when rope_dim = 0.
  *   e_out (optional, may be NULL): float32 [n_seq * n_per_seq, 512], the
@@ -138,7 +137,8 @@ csa_status csa_window_append(const float* x, int64_t n_seq, int64_t n_tok, int64
  *   Query q belongs to sequence q / q_per_seq and sits at token position
  *   q_pos[q] >= 0; entry j is visible iff 4j + 3 <= q_pos[q].
  *   score = sum_h w[q, h] * ReLU(q_fp8[q, h, :] . k_fp8[j, :]) (8 heads x 128,
- *   E4M3 operands, float32 accumulation on the FP8 matrix cores).
+ *   E4M3 operands; every dot product is exact before its one float32
+ *   rounding, as the operands are widened to fp16 for the matrix cores).
  *   q_fp8 uint8 [Q, 8, 128]; w float32 [Q, 8] (must be >= 0);
  *   k_fp8 uint8 [n_seq, k_seq_stride, 128].
  *   Dense mode (pool_blocks == NULL): ncols = n_entries columns; column j is
@@ -161,7 +161,8 @@ csa_status csa_index_score(const uint8_t* q_fp8, const float* w, const int32_t* 
 /* ---------------------------------------------------------------- a4 ----
  * csa_topk: for each of Q rows of scores float32 [Q, ncols], select the k
  * columns with the largest scores (P3 §02 Top-512); equal scores go to the
- * lower column; -inf columns are never selected.  Outputs the selected ids in
+ * lower column (-0 equals +0); -inf and NaN columns are never selected.
+ * Outputs the selected ids in
  * ascending order, -1 padded, into idx int32 [Q, k].
  *   col_blocks (may be NULL) int32 [Q, ncols / 8]: when given, column c maps
  *   to id 8 * col_blocks[q, c / 8] + c % 8 (pooled scores; the block ids must

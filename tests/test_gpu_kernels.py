@@ -172,21 +172,44 @@ def test_index_score_pooled_matches_dense_bitwise():
 
 
 def _oracle_topk_fp32(row, k, ids=None):
-    valid = ~np.isneginf(row)
+    valid = ~(np.isneginf(row) | np.isnan(row))
     ids = np.arange(len(row)) if ids is None else np.asarray(ids)
     return oracle.topk(row[valid].astype(np.float64), k, ids=ids[valid])
 
 
-@pytest.mark.parametrize("Q,ncols,k", [(3, 100, 512), (2, 5000, 512), (2, 20000, 512),
-                                       (2, 300000, 512), (2, 40000, 2048), (1, 16384, 4096)])
-def test_topk_exact(Q, ncols, k):
+def _score_rows(rng, dist, Q, ncols):
+    """Score rows of several value distributions (ties, few levels, wide range)."""
+    if dist == "ties":
+        return rng.integers(0, 200, (Q, ncols)).astype(np.float32) * np.float32(0.25)
+    if dist == "few":          # a handful of levels: the threshold bin is large
+        return rng.integers(0, 4, (Q, ncols)).astype(np.float32)
+    if dist == "const":
+        return np.full((Q, ncols), 1.5, np.float32)
+    if dist == "normal":
+        return rng.standard_normal((Q, ncols)).astype(np.float32)
+    # wide: magnitudes over 60 decades, both signs, plus the largest finite values
+    v = (10.0 ** rng.uniform(-30, 30, (Q, ncols))) * rng.choice([-1.0, 1.0], (Q, ncols))
+    v = v.astype(np.float32)
+    v[:, 1::97] = np.float32(3.4e38)
+    v[:, 2::89] = np.float32(-3.4e38)
+    return v
+
+
+@pytest.mark.parametrize("Q,ncols,k,dist", [(3, 100, 512, "ties"), (2, 5000, 512, "ties"),
+                                            (2, 20000, 512, "ties"), (2, 300000, 512, "ties"),
+                                            (2, 40000, 2048, "ties"), (1, 16384, 4096, "ties"),
+                                            (2, 16384, 512, "few"), (2, 40000, 512, "few"),
+                                            (2, 16384, 512, "const"), (2, 50000, 512, "normal"),
+                                            (2, 16384, 512, "wide"), (2, 70000, 1000, "wide")])
+def test_topk_exact(Q, ncols, k, dist):
     rng = np.random.default_rng(ncols + k)
-    sc = rng.integers(0, 200, (Q, ncols)).astype(np.float32) * np.float32(0.25)   # heavy ties
+    sc = _score_rows(rng, dist, Q, ncols)
     sc[:, ::7] = -np.inf
     sc[0, :ncols // 3] = -np.inf
     if ncols > 10:
         sc[-1, 3] = -0.0
         sc[-1, 4] = 0.0
+        sc[-1, 5] = np.nan
     idx = ops.csa_topk(t_(sc), k=k)
     torch.cuda.synchronize()
     got = np_(idx)
