@@ -81,9 +81,7 @@ LayerPlan plan_layer(int32_t mode, const csa_layer_args* a) {
         p.off_blocks = off;
         off += round_up((size_t)(p.Q * nb) * sizeof(int32_t));
       }
-      size_t pool_ws = block_pool_workspace_bytes(p.Q, p.nblk, 1, nb);
-      size_t gat_ws = topk_gather_workspace_bytes(p.Q, nb, a->top_k);
-      sel = pool_ws > gat_ws ? pool_ws : gat_ws;
+      sel = pool_topk_workspace_bytes(p.Q, p.nblk, nb, a->top_k);
     } else {
       sel = topk_workspace_bytes(p.Q, p.ncols, a->top_k);
     }
@@ -382,9 +380,8 @@ static csa_status run_index(const char* fn, int32_t mode, const csa_layer_args* 
   // Full: best blocks (the pool, or top_k blocks), then Top-K among their entries
   int32_t* blocks = a->build_pool ? a->pool_blocks : reinterpret_cast<int32_t*>(ws + p.off_blocks);
   const int32_t nb = a->build_pool ? a->n_pool_blocks : a->top_k;
-  r = hip_status(launch_block_pool(bm, 1, p.Q, p.nblk, nb, blocks, ws + p.off_sel, st), fn);
-  if (r != CSA_OK) return r;
-  return hip_status(launch_topk_gather(scores, p.Q, p.ncols, blocks, nb, a->top_k, a->idx, ws + p.off_sel, st),
+  return hip_status(launch_pool_topk(bm, p.nblk, scores, p.ncols, p.Q, nb, blocks, a->top_k, a->idx,
+                                    ws + p.off_sel, st),
                     fn);
 }
 

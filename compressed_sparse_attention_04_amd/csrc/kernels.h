@@ -46,6 +46,12 @@ hipError_t launch_topk_gather(const float* scores, int64_t Q, int64_t ncols, con
 size_t block_pool_workspace_bytes(int64_t Q, int64_t ncols, int32_t is_block_max, int32_t nb);
 hipError_t launch_block_pool(const float* values, int32_t is_block_max, int64_t Q, int64_t ncols,
                              int32_t nb, int32_t* pool, void* ws, hipStream_t st);
+// Full layer: the nb best blocks by block max -> pool [Q, nb], then the k best
+// entries of those blocks -> idx [Q, k].  One kernel when a row fits one block.
+size_t pool_topk_workspace_bytes(int64_t Q, int64_t nblk, int32_t nb, int32_t k);
+hipError_t launch_pool_topk(const float* block_max, int64_t nblk, const float* scores, int64_t ncols,
+                            int64_t Q, int32_t nb, int32_t* pool, int32_t k, int32_t* idx, void* ws,
+                            hipStream_t st);
 
 // attn.hip
 size_t attn_workspace_bytes(int64_t Q, int32_t k);

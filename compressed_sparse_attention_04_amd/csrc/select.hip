@@ -3,42 +3,47 @@
 // P3 §02: the first Full layer picks the Top-512 over every visible position,
 // then ranks 8-position blocks by their largest score and keeps 2,048 of them
 // (16,384 candidates) for the Reindex layers.  Equal scores go to the lower
-// column (and so the lower entry id); -inf columns are never selected.
+// column (and so the lower entry id); -inf and NaN columns are never selected.
 //
-// One 1024-thread block selects the K best of up to SEL_CHUNK keys, 16 per
-// thread in registers (lane l of wave v holds positions 1024 v + 64 u + l,
-// u < 16, so that every load is one contiguous 256-byte run):
+// One block of NT threads selects the K best of up to NT * PER keys held in
+// registers, PER per thread (lane l of wave v holds positions
+// 64 PER v + 64 u + l, u < PER, so that every load is one contiguous run):
 //   1. block-reduce the largest and smallest valid value and the valid count;
 //   2. histogram the values into SEL_BINS bins linear in value between the two
 //      (a monotone map, so every key of a lower bin beats every key of a
 //      higher one) and scan it to find the bin holding the K-th largest key;
-//   3. find that key T exactly among the bin's keys only (pairwise ranking
-//      when the bin is small, else a three-digit radix select over it), and
-//      how many keys equal to T are still needed;
+//   3. find that key T exactly among the bin's keys only: pairwise ranking
+//      when the bin is small, else a three-digit radix select over the keys
+//      of the bin; also how many keys equal to T are still needed;
 //   4. compact in position order (a block scan of per-wave counts, then wave
 //      ballots), which keeps the output ascending and gives ties to the lower
 //      positions.
-// Rows longer than SEL_CHUNK are cut into chunks; every chunk's K best are
-// kept as candidates (the global K best are among them) and selected again.
+// Rows of 8K+ keys first narrow the keys to a sampled lower bound of the K-th
+// largest (block_select), so that steps 1-4 run over about 1.5 K candidates.
+// Longer rows are cut into chunks whose K best are kept as candidates (the
+// global K best are among them) and selected again.  A Full layer runs the
+// block pool and the Top-K among the pooled blocks' entries in one kernel.
 #include "common.h"
 #include "kernels.h"
 
 namespace csa {
 
-constexpr int SEL_CHUNK = 16384;
-constexpr int SEL_THREADS = 1024;
-constexpr int SEL_WAVES = SEL_THREADS / 64;
-constexpr int SEL_PER = SEL_CHUNK / SEL_THREADS;      // keys per thread
 constexpr int SEL_BINS = 2048;
-constexpr int SEL_RANK_MAX = 256;                     // pairwise ranking up to this many keys
+constexpr int SEL_RANK_MAX = 256;                      // pairwise ranking up to this many keys
+constexpr int SEL_MAX_WAVES = 16;
+constexpr int64_t SEL_CHUNK_MAX = 32768;               // keys of one block
+constexpr int SEL_POOL_MAX = 4096;                     // pool size of the fused kernel
+constexpr int SEL_CAND_MAX = 4096;                     // candidates of the sampled path
 
 namespace {
 
 struct SelShared {
   uint32_t hist[SEL_BINS];
-  uint32_t cand[SEL_CHUNK];       // keys of the threshold bin
-  uint32_t wred[3][SEL_WAVES];    // per-wave partials
-  uint32_t n_cand, bstar, rem, T, take_eq;
+  uint32_t cand[SEL_RANK_MAX];
+  uint32_t ckey[SEL_CAND_MAX];    // sampled path: candidates in position order
+  uint16_t cpos[SEL_CAND_MAX];
+  uint32_t wred[3][SEL_MAX_WAVES];
+  uint32_t bstar, rem, n_cand, T, take_eq, tlo;
 };
 
 // Value of a valid (non-zero) key: the inverse of select_key.
@@ -47,8 +52,8 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 }
 
 // Cross-lane steps on the DPP network (gfx9 controls: quad_perm, row_shr,
-// row_mirror, row_half_mirror, row_bcast15, row_bcast31).  A lane whose source
-// is outside the row mask keeps `old`.
+// row_mirror, row_half_mirror, row_bcast15, row_bcast31).  A lane whose row is
+// outside the row mask, or whose source lane is outside its row, keeps `old`.
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
@@ -68,11 +73,11 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
-// Wave-wide max / min / sum, returned uniformly (the full result lands in lane 63).
-template <int OP>   // 0 max, 1 min, 2 sum
+// Wave-wide max / min, returned uniformly (the full result lands in lane 63).
+template <int OP>   // 0 max, 1 min
 __device__ __forceinline__ uint32_t wave_reduce(uint32_t v) {
-  auto f = [](uint32_t a, uint32_t b) { return OP == 0 ? (a > b ? a : b) : OP == 1 ? (a < b ? a : b) : a + b; };
-  const uint32_t id = OP == 0 ? 0u : OP == 1 ? 0xFFFFFFFFu : 0u;
+  auto f = [](uint32_t a, uint32_t b) { return OP == 0 ? (a > b ? a : b) : (a < b ? a : b); };
+  const uint32_t id = OP == 1 ? 0xFFFFFFFFu : 0u;
   v = f(v, dpp<DPP_XOR1>(id, v));
   v = f(v, dpp<DPP_XOR2>(id, v));
   v = f(v, dpp<DPP_ROW_HALF_MIRROR>(id, v));
@@ -82,15 +87,21 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 // Exclusive block scan of v; *total = the block sum.  Two barriers.
+template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(SelShared& s, uint32_t v, uint32_t* total) {
+  constexpr int W = NT / 64;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) s.wred[0][wv] = incl;
   __syncthreads();
   uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < SEL_WAVES; ++w) {
+  for (int w = 0; w < W; ++w) {
     const uint32_t x = s.wred[0][w];
     before += w < wv ? x : 0u;
     all += x;
@@ -101,46 +112,317 @@ __device__ __forceinline__ uint32_t block_excl_scan(SelShared& s, uint32_t v, ui
 }
 
 // Bin of a valid value: 0 holds the largest values.
-__device__ __forceinline__ int value_bin(float v, float vmax, float inv) {
+__device__ __forceinline__ int value_bin(uint32_t key, float vmax, float inv) {
   if (inv == 0.0f) return 0;
-  const float x = (vmax - v) * inv;
+  const float x = (vmax - key_value(key)) * inv;
   return (int)fminf(x, (float)(SEL_BINS - 1));
 }
 
-// The rem-th largest of the n keys in s.cand (1 <= rem <= n) and how many
-// keys equal to it are taken: exact three-digit radix select (11, 11, 10 bits).
-__device__ void radix_select_cand(SelShared& s, int n, uint32_t rem) {
-  const int tid = threadIdx.x;
+// Thread t owns bins BPT t .. BPT t + BPT - 1 of h (already loaded): the bin
+// where the running count from bin 0 reaches `need`, and how many of that
+// bin's keys are needed.  Exactly one thread returns true.
+template <int NT, int BPT>
+__device__ __forceinline__ bool find_bin(SelShared& s, const uint32_t (&h)[BPT], uint32_t need, int* bin,
+                                         uint32_t* left) {
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) sum += h[j];
+  uint32_t tot;
+  const uint32_t excl = block_excl_scan<NT>(s, sum, &tot);
+  if (!(excl < need && need <= excl + sum)) return false;
+  uint32_t run = excl;
+  bool found = false;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    if (!found && run + h[j] >= need) {
+      *bin = BPT * (int)threadIdx.x + j;
+      *left = need - run;
+      found = true;
+    }
+    run += h[j];
+  }
+  return true;
+}
+
+// Steps 1-3: the K-th largest key *T of the block's keys and how many keys
+// equal to it are taken (*take_eq); T = 0 when at most K keys are valid (every
+// valid key is taken).  Every thread of the block calls it.
+template <int NT, int PER>
+__device__ __forceinline__ void block_threshold(SelShared& s, const uint32_t (&key)[PER], uint32_t K,
+                                                uint32_t* T_out, uint32_t* take_out) {
+  constexpr int W = NT / 64, BPT = SEL_BINS / NT;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t kmax = 0, kmin = 0xFFFFFFFFu, nv_w = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    kmax = key[u] > kmax ? key[u] : kmax;
+    kmin = (key[u] != 0 && key[u] < kmin) ? key[u] : kmin;
+    nv_w += (uint32_t)__popcll(__ballot(key[u] != 0));
+  }
+  kmax = wave_reduce<0>(kmax);
+  kmin = wave_reduce<1>(kmin);
+  __syncthreads();   // earlier readers of the shared state are done
+  for (int b = tid; b < SEL_BINS; b += NT) s.hist[b] = 0;
+  if (lane == 0) {
+    s.wred[0][wv] = kmax;
+    s.wred[1][wv] = kmin;
+    s.wred[2][wv] = nv_w;
+  }
+  if (tid == 0) s.n_cand = 0;
+  __syncthreads();
+  uint32_t nval = 0;
+  kmax = 0; kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    kmax = s.wred[0][w] > kmax ? s.wred[0][w] : kmax;
+    kmin = s.wred[1][w] < kmin ? s.wred[1][w] : kmin;
+    nval += s.wred[2][w];
+  }
+  if (nval <= K) {
+    *T_out = 0;
+    *take_out = 0;
+    return;
+  }
+
+  // 2. value-linear histogram and the bin of the K-th largest key
+  const float vmax = key_value(kmax), vmin = key_value(kmin);
+  const float range = vmax - vmin;
+  const float inv = (range > 0.0f && range < __builtin_huge_valf()) ? (float)SEL_BINS / range : 0.0f;
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (key[u] != 0) atomicAdd(&s.hist[value_bin(key[u], vmax, inv)], 1u);
+  __syncthreads();
+  {
+    uint32_t h[BPT];
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) h[j] = s.hist[BPT * tid + j];
+    int bin;
+    uint32_t left;
+    if (find_bin<NT, BPT>(s, h, K, &bin, &left)) {
+      s.bstar = (uint32_t)bin;
+      s.rem = left;
+    }
+  }
+  __syncthreads();
+  const int bstar = (int)s.bstar;
+  uint32_t rem = s.rem;
+  const uint32_t nc = s.hist[bstar];
+  uint64_t inbin = 0;   // bit u: key[u] lies in the threshold bin
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (key[u] != 0 && value_bin(key[u], vmax, inv) == bstar) inbin |= 1ull << u;
+
+  // 3. the exact rem-th largest key of the threshold bin
+  if (nc <= SEL_RANK_MAX) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if ((inbin >> u) & 1u) s.cand[atomicAdd(&s.n_cand, 1u)] = key[u];
+    __syncthreads();
+    for (int i = tid; i < (int)nc; i += NT) {
+      const uint32_t ki = s.cand[i];
+      uint32_t g = 0, e = 0;
+      for (int j = 0; j < (int)nc; ++j) {
+        const uint32_t kj = s.cand[j];
+        g += kj > ki;
+        e += kj == ki;
+      }
+      if (g < rem && rem <= g + e) {   // keys equal to ki write equal values
+        s.T = ki;
+        s.take_eq = rem - g;
+      }
+    }
+    __syncthreads();
+    *T_out = s.T;
+    *take_out = s.take_eq;
+    return;
+  }
   uint32_t prefix = 0;
   const int shifts[3] = {21, 10, 0};
   const uint32_t masks[3] = {0u, 0xFFE00000u, 0xFFFFFC00u};
   for (int pass = 0; pass < 3; ++pass) {
-    for (int b = tid; b < SEL_BINS; b += SEL_THREADS) s.hist[b] = 0;
+    __syncthreads();   // earlier readers of hist / T / rem are done
+    for (int b = tid; b < SEL_BINS; b += NT) s.hist[b] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += SEL_THREADS) {
-      const uint32_t k = s.cand[i];
-      if ((k & masks[pass]) == prefix) atomicAdd(&s.hist[(k >> shifts[pass]) & (SEL_BINS - 1)], 1u);
-    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (((inbin >> u) & 1u) && (key[u] & masks[pass]) == prefix)
+        atomicAdd(&s.hist[(key[u] >> shifts[pass]) & (SEL_BINS - 1)], 1u);
     __syncthreads();
-    // thread t owns digits 2047 - 2t and 2046 - 2t (largest digits first)
-    const uint32_t h0 = s.hist[SEL_BINS - 1 - 2 * tid], h1 = s.hist[SEL_BINS - 2 - 2 * tid];
-    uint32_t total;
-    const uint32_t excl = block_excl_scan(s, h0 + h1, &total);
-    if (excl < rem && rem <= excl + h0 + h1) {
-      const bool first = rem <= excl + h0;
-      const uint32_t digit = first ? SEL_BINS - 1 - 2 * tid : SEL_BINS - 2 - 2 * tid;
-      s.T = digit;
-      s.rem = first ? rem - excl : rem - excl - h0;
+    // thread t owns digits 2047 - BPT t - j (largest digits first)
+    uint32_t h[BPT];
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) h[j] = s.hist[SEL_BINS - 1 - (BPT * tid + j)];
+    int bin;
+    uint32_t left;
+    if (find_bin<NT, BPT>(s, h, rem, &bin, &left)) {
+      s.T = (uint32_t)(SEL_BINS - 1 - bin);
+      s.rem = left;
     }
     __syncthreads();
     prefix |= s.T << shifts[pass];
     rem = s.rem;
+  }
+  *T_out = prefix;
+  *take_out = rem;
+}
+
+// Step 4: the selected keys (key > T, or key == T among the first take_eq in
+// position order) get consecutive slots in position order; emit(u, slot) is
+// called for every selected key with slot < K.  Returns the number selected.
+template <int NT, int PER, class Emit>
+__device__ __forceinline__ uint32_t block_compact(SelShared& s, const uint32_t (&key)[PER], uint32_t T,
+                                                  uint32_t take_eq, uint32_t K, Emit emit) {
+  constexpr int W = NT / 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint32_t gt_w = 0, eq_w = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    gt_w += (uint32_t)__popcll(__ballot(key[u] > T));
+    eq_w += (uint32_t)__popcll(__ballot(T != 0 && key[u] == T));
+  }
+  __syncthreads();   // earlier readers of wred are done
+  if (lane == 0) {
+    s.wred[0][wv] = gt_w;
+    s.wred[1][wv] = eq_w;
+  }
+  __syncthreads();
+  uint32_t gt_before = 0, eq_before = 0, gt_tot = 0, eq_tot = 0;
+#pragma unroll
+  for (int v = 0; v < W; ++v) {
+    const uint32_t g = s.wred[0][v], e = s.wred[1][v];
+    gt_before += v < wv ? g : 0u;
+    eq_before += v < wv ? e : 0u;
+    gt_tot += g;
+    eq_tot += e;
+  }
+  uint32_t slot_base = gt_before + (eq_before < take_eq ? eq_before : take_eq);
+  uint32_t eq_seen = eq_before;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const bool is_gt = key[u] > T, is_eq = T != 0 && key[u] == T;
+    const uint64_t eq_b = __ballot(is_eq);
+    const bool take = is_gt || (is_eq && eq_seen + lanes_below(eq_b) < take_eq);
+    const uint64_t tk_b = __ballot(take);
+    const uint32_t slot = slot_base + lanes_below(tk_b);
+    if (take && slot < K) emit(u, slot);
+    slot_base += (uint32_t)__popcll(tk_b);
+    eq_seen += (uint32_t)__popcll(eq_b);
+  }
+  return gt_tot + (eq_tot < take_eq ? eq_tot : take_eq);
+}
+
+// Steps 1-4 over a candidate list of n keys in LDS (position order), CP per
+// thread; emit(p, key, slot) with p from cpos.
+template <int NT, int CP, class Emit>
+__device__ __forceinline__ uint32_t select_candidates(SelShared& s, uint32_t n, uint32_t K, Emit emit) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint32_t ck[CP];
+#pragma unroll
+  for (int i = 0; i < CP; ++i) {
+    const uint32_t c = 64 * CP * wv + 64 * i + lane;
+    ck[i] = c < n ? s.ckey[c] : 0u;
+  }
+  uint32_t T, take_eq;
+  block_threshold<NT, CP>(s, ck, K, &T, &take_eq);
+  return block_compact<NT, CP>(s, ck, T, take_eq, K, [&](int i, uint32_t slot) {
+    const uint32_t c = 64 * CP * wv + 64 * i + lane;
+    emit((int)s.cpos[c], ck[i], slot);
+  });
+}
+
+// The K best keys of the block (thread layout as above; p = 64 PER v + 64 u + l
+// is the position of key[u]): emit(p, key, slot) for each, slots ascending
+// with p.  Returns the number selected (min(K, valid keys)).
+//
+// With 8+ keys per thread the K-th largest key is first bounded from below
+// with a sample (one key per thread, spread over each wave's run): T_lo = the
+// smallest sample key of the sample bin where the sample count reaches m,
+// about 1.5 K n_sample / n (+8).  If the keys >= T_lo number between K and
+// SEL_CAND_MAX, they hold the K best (every other key is smaller), so they
+// are gathered in position order and selected exactly; otherwise the exact
+// selection runs over all keys.
+template <int NT, int PER, class Emit>
+__device__ __forceinline__ uint32_t block_select(SelShared& s, const uint32_t (&key)[PER], uint32_t K, Emit emit) {
+  constexpr int W = NT / 64, BPT = SEL_BINS / NT;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int pw = 64 * PER * wv + lane;
+  if constexpr (PER >= 8) {
+    uint32_t nv_w = 0, smp = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      nv_w += (uint32_t)__popcll(__ballot(key[u] != 0));
+      smp = (u == (lane & (PER - 1))) ? key[u] : smp;
+    }
+    const uint32_t smax = wave_reduce<0>(smp), smin = wave_reduce<1>(smp != 0 ? smp : 0xFFFFFFFFu);
+    const uint32_t sv_w = (uint32_t)__popcll(__ballot(smp != 0));
+    __syncthreads();   // earlier readers of the shared state are done
+    for (int b = tid; b < SEL_BINS; b += NT) s.hist[b] = 0;
+    if (lane == 0) {
+      s.wred[0][wv] = smax;
+      s.wred[1][wv] = smin;
+      s.wred[2][wv] = nv_w | (sv_w << 16);   // <= 32768 keys, <= 1024 samples
+    }
+    if (tid == 0) s.tlo = 0xFFFFFFFFu;
     __syncthreads();
+    uint32_t kmax = 0, kmin = 0xFFFFFFFFu, nval = 0, sval = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      kmax = s.wred[0][w] > kmax ? s.wred[0][w] : kmax;
+      kmin = s.wred[1][w] < kmin ? s.wred[1][w] : kmin;
+      nval += s.wred[2][w] & 0xFFFFu;
+      sval += s.wred[2][w] >> 16;
+    }
+    const uint32_t m = (uint32_t)(1.5f * (float)K * (float)sval / (float)(nval > 0 ? nval : 1)) + 8u;
+    if (nval > K && m < sval) {
+      const float vmax = key_value(kmax), vmin = key_value(kmin);
+      const float range = vmax - vmin;
+      const float inv = (range > 0.0f && range < __builtin_huge_valf()) ? (float)SEL_BINS / range : 0.0f;
+      if (smp != 0) atomicAdd(&s.hist[value_bin(smp, vmax, inv)], 1u);
+      __syncthreads();
+      {
+        uint32_t h[BPT];
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) h[j] = s.hist[BPT * tid + j];
+        int bin;
+        uint32_t left;
+        if (find_bin<NT, BPT>(s, h, m, &bin, &left)) s.bstar = (uint32_t)bin;
+      }
+      __syncthreads();
+      if (smp != 0 && value_bin(smp, vmax, inv) == (int)s.bstar) atomicMin(&s.tlo, smp);
+      __syncthreads();
+      const uint32_t tlo = s.tlo;
+      uint32_t c_w = 0;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) c_w += (uint32_t)__popcll(__ballot(key[u] >= tlo));
+      if (lane == 0) s.wred[0][wv] = c_w;
+      __syncthreads();
+      uint32_t C = 0, off = 0;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        C += s.wred[0][w];
+        off += w < wv ? s.wred[0][w] : 0u;
+      }
+      if (C >= K && C <= SEL_CAND_MAX) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+          const bool in = key[u] >= tlo;
+          const uint64_t mk = __ballot(in);
+          if (in) {
+            const uint32_t c = off + lanes_below(mk);
+            s.ckey[c] = key[u];
+            s.cpos[c] = (uint16_t)(pw + 64 * u);
+          }
+          off += (uint32_t)__popcll(mk);
+        }
+        __syncthreads();
+        if (C <= 4 * NT) return select_candidates<NT, 4>(s, C, K, emit);
+        return select_candidates<NT, SEL_CAND_MAX / NT>(s, C, K, emit);
+      }
+    }
   }
-  if (tid == 0) {
-    s.T = prefix;
-    s.take_eq = rem;
-  }
+  uint32_t T, take_eq;
+  block_threshold<NT, PER>(s, key, K, &T, &take_eq);
+  return block_compact<NT, PER>(s, key, T, take_eq, K, [&](int u, uint32_t slot) { emit(pw + 64 * u, key[u], slot); });
 }
 
 }  // namespace
@@ -150,11 +432,12 @@ __device__ void radix_select_cand(SelShared& s, int n, uint32_t rem) {
 // MODE 2: positions are the entries of the blocks listed in
 //   col_blocks [Q, nblk_map] (ascending, -1 padded): position i is entry
 //   8 * col_blocks[q, i / 8] + i % 8 of scores [Q, ncols]; n_in = 8 * nblk_map.
-// FINAL: write ids ascending to idx [Q, K]; otherwise write the chunk's K
-// best (key, column) pairs ascending to cand_out [Q, gridDim.x * K] (MODE 2
-// writes entry ids as the columns).  One block per (chunk, row).
-template <int MODE, bool FINAL>
-__global__ __launch_bounds__(SEL_THREADS) void select_kernel(
+// FINAL: write ids ascending to idx [Q, K] (with col_blocks, MODE 0 / 1 map
+// the column through the blocks); otherwise write the chunk's K best (key,
+// column) pairs ascending to out_keys / out_cols [Q, gridDim.x * K] (MODE 2
+// writes entry ids as the columns).  One block per (chunk of NT PER keys, row).
+template <int MODE, bool FINAL, int NT, int PER>
+__global__ __launch_bounds__(NT) void select_kernel(
     const float* __restrict__ scores, int64_t ncols, const uint32_t* __restrict__ cand_keys,
     const int32_t* __restrict__ cand_cols, int64_t n_in, const int32_t* __restrict__ col_blocks,
     int64_t nblk_map, int32_t K, int32_t* __restrict__ idx, uint32_t* __restrict__ out_keys,
@@ -163,21 +446,20 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t q = blockIdx.y;
   const int64_t total = MODE == 0 ? ncols : n_in;
-  const int64_t start = (int64_t)blockIdx.x * SEL_CHUNK;
-  const int n = (int)((total - start) < SEL_CHUNK ? (total - start) : SEL_CHUNK);
-  const int pw = 1024 * wv + lane;       // position of key[u] is pw + 64 u
+  const int64_t start = (int64_t)blockIdx.x * (NT * PER);
+  const int n = (int)((total - start) < NT * PER ? (total - start) : NT * PER);
+  const int pw = 64 * PER * wv + lane;       // position of key[u] is pw + 64 u
 
-  // keys (0 = not selectable)
-  uint32_t key[SEL_PER];
+  uint32_t key[PER];   // 0 = not selectable
   if (MODE == 0) {
     const float* row = scores + q * ncols + start;
 #pragma unroll
-    for (int u = 0; u < SEL_PER; ++u) key[u] = pw + 64 * u < n ? select_key(row[pw + 64 * u]) : 0u;
+    for (int u = 0; u < PER; ++u) key[u] = pw + 64 * u < n ? select_key(row[pw + 64 * u]) : 0u;
   } else if (MODE == 2) {
     const float* row = scores + q * ncols;
     const int32_t* map = col_blocks + q * nblk_map;
 #pragma unroll
-    for (int u = 0; u < SEL_PER; ++u) {
+    for (int u = 0; u < PER; ++u) {
       const int pp = pw + 64 * u;
       key[u] = 0u;
       if (pp < n) {
@@ -190,140 +472,26 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   } else {
     const uint32_t* row = cand_keys + q * n_in + start;
 #pragma unroll
-    for (int u = 0; u < SEL_PER; ++u) key[u] = pw + 64 * u < n ? row[pw + 64 * u] : 0u;
+    for (int u = 0; u < PER; ++u) key[u] = pw + 64 * u < n ? row[pw + 64 * u] : 0u;
   }
 
-  // 1. largest / smallest valid key and the valid count
-  uint32_t kmax = 0, kmin = 0xFFFFFFFFu, nval = 0;
-#pragma unroll
-  for (int u = 0; u < SEL_PER; ++u) {
-    kmax = key[u] > kmax ? key[u] : kmax;
-    kmin = (key[u] != 0 && key[u] < kmin) ? key[u] : kmin;
-    nval += key[u] != 0;
-  }
-  kmax = wave_reduce<0>(kmax);
-  kmin = wave_reduce<1>(kmin);
-  nval = wave_reduce<2>(nval);
-  for (int b = tid; b < SEL_BINS; b += SEL_THREADS) s.hist[b] = 0;
-  if (lane == 0) {
-    s.wred[0][wv] = kmax;
-    s.wred[1][wv] = kmin;
-    s.wred[2][wv] = nval;
-  }
-  if (tid == 0) s.n_cand = 0;
-  __syncthreads();
-  kmax = 0; kmin = 0xFFFFFFFFu; nval = 0;
-#pragma unroll
-  for (int w = 0; w < SEL_WAVES; ++w) {
-    kmax = s.wred[0][w] > kmax ? s.wred[0][w] : kmax;
-    kmin = s.wred[1][w] < kmin ? s.wred[1][w] : kmin;
-    nval += s.wred[2][w];
-  }
-
-  uint32_t T = 0, take_eq = 0;     // T = 0: every valid key is taken
-  if (nval > (uint32_t)K) {
-    // 2. value-linear histogram and the bin of the K-th largest key
-    const float vmax = key_value(kmax), vmin = key_value(kmin);
-    const float range = vmax - vmin;
-    const float inv = (range > 0.0f && range < __builtin_huge_valf()) ? (float)SEL_BINS / range : 0.0f;
-#pragma unroll
-    for (int u = 0; u < SEL_PER; ++u)
-      if (key[u] != 0) atomicAdd(&s.hist[value_bin(key_value(key[u]), vmax, inv)], 1u);
-    __syncthreads();
-    const uint32_t h0 = s.hist[2 * tid], h1 = s.hist[2 * tid + 1];
-    uint32_t tot;
-    const uint32_t excl = block_excl_scan(s, h0 + h1, &tot);
-    if (excl < (uint32_t)K && (uint32_t)K <= excl + h0 + h1) {
-      const bool first = (uint32_t)K <= excl + h0;
-      s.bstar = first ? 2 * tid : 2 * tid + 1;
-      s.rem = first ? K - excl : K - excl - h0;
-    }
-    __syncthreads();
-    const int bstar = (int)s.bstar;
-    const uint32_t rem = s.rem;
-    // 3. the exact K-th largest among the threshold bin's keys
-#pragma unroll
-    for (int u = 0; u < SEL_PER; ++u) {
-      if (key[u] != 0 && value_bin(key_value(key[u]), vmax, inv) == bstar) {
-        const uint32_t slot = atomicAdd(&s.n_cand, 1u);
-        s.cand[slot] = key[u];
-      }
-    }
-    __syncthreads();
-    const int nc = (int)s.n_cand;
-    if (nc <= SEL_RANK_MAX) {
-      if (tid < nc) {
-        const uint32_t ki = s.cand[tid];
-        uint32_t g = 0, e = 0;
-        for (int j = 0; j < nc; ++j) {
-          const uint32_t kj = s.cand[j];
-          g += kj > ki;
-          e += kj == ki;
-        }
-        if (g < rem && rem <= g + e) {   // equal keys write equal values
-          s.T = ki;
-          s.take_eq = rem - g;
-        }
-      }
+  const uint32_t n_sel = block_select<NT, PER>(s, key, (uint32_t)K, [&](int p, uint32_t k, uint32_t slot) {
+    const int64_t pos = start + p;
+    int64_t col;
+    if (MODE == 0) col = pos;
+    else if (MODE == 1) col = cand_cols[q * n_in + pos];
+    else col = 8 * (int64_t)col_blocks[q * nblk_map + (pos >> 3)] + (pos & 7);
+    if (FINAL) {
+      int64_t id = col;
+      if (MODE != 2 && col_blocks) id = 8 * (int64_t)col_blocks[q * nblk_map + (col >> 3)] + (col & 7);
+      idx[q * K + slot] = (int32_t)id;
     } else {
-      radix_select_cand(s, nc, rem);
+      const int64_t o = (q * gridDim.x + blockIdx.x) * (int64_t)K + slot;
+      out_keys[o] = k;
+      out_cols[o] = (int32_t)col;
     }
-    __syncthreads();
-    T = s.T;
-    take_eq = s.take_eq;
-  }
-
-  // 4. position-ordered compaction: per-wave counts of keys > T and == T
-  //    (packed), a block scan over the waves, then ballots within the wave
-  uint32_t gt_w = 0, eq_w = 0;
-#pragma unroll
-  for (int u = 0; u < SEL_PER; ++u) {
-    gt_w += __popcll(__ballot(key[u] > T));
-    eq_w += __popcll(__ballot(T != 0 && key[u] == T));
-  }
-  if (lane == 0) s.wred[0][wv] = gt_w | (eq_w << 16);
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int v = 0; v < SEL_WAVES; ++v) {
-    const uint32_t x = s.wred[0][v];
-    before += v < wv ? x : 0u;
-    tot += x;
-  }
-  const uint32_t gt_before = before & 0xFFFFu, eq_before = before >> 16;
-  const uint32_t n_sel = (tot & 0xFFFFu) + ((tot >> 16) < take_eq ? (tot >> 16) : take_eq);
-  uint32_t slot_base = gt_before + (eq_before < take_eq ? eq_before : take_eq);
-  uint32_t eq_seen = eq_before;
-#pragma unroll
-  for (int u = 0; u < SEL_PER; ++u) {
-    const bool is_gt = key[u] > T, is_eq = T != 0 && key[u] == T;
-    const uint64_t eq_b = __ballot(is_eq);
-    const uint32_t eq_rank = eq_seen + __builtin_amdgcn_mbcnt_hi((uint32_t)(eq_b >> 32),
-                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)eq_b, 0u));
-    const bool take = is_gt || (is_eq && eq_rank < take_eq);
-    const uint64_t tk_b = __ballot(take);
-    const uint32_t slot = slot_base + __builtin_amdgcn_mbcnt_hi((uint32_t)(tk_b >> 32),
-                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)tk_b, 0u));
-    if (take && slot < (uint32_t)K) {
-      const int pp = pw + 64 * u;
-      int64_t col;
-      if (MODE == 0) col = start + pp;
-      else if (MODE == 1) col = cand_cols[q * n_in + start + pp];
-      else col = 8 * (int64_t)col_blocks[q * nblk_map + ((start + pp) >> 3)] + ((start + pp) & 7);
-      if (FINAL) {
-        int64_t id = col;
-        if (MODE == 0 && col_blocks) id = 8 * (int64_t)col_blocks[q * nblk_map + (col >> 3)] + (col & 7);
-        idx[q * K + slot] = (int32_t)id;
-      } else {
-        const int64_t o = (q * gridDim.x + blockIdx.x) * (int64_t)K + slot;
-        out_keys[o] = key[u];
-        out_cols[o] = (int32_t)col;
-      }
-    }
-    slot_base += (uint32_t)__popcll(tk_b);
-    eq_seen += (uint32_t)__popcll(eq_b);
-  }
-  for (int j = (int)n_sel + tid; j < K; j += SEL_THREADS) {
+  });
+  for (int j = (int)n_sel + tid; j < K; j += NT) {
     if (FINAL) {
       idx[q * K + j] = -1;
     } else {
@@ -332,6 +500,54 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
       out_cols[o] = -1;
     }
   }
+}
+
+// Full layer, one block per row: the NB blocks with the largest block max
+// (block_max [Q, nblk], nblk <= NT PER) -> pool [Q, NB] (ascending, -1
+// padded; may be null), then the K best of the pooled blocks' entries
+// (scores [Q, ncols]; 8 NB <= NT PER2) -> idx [Q, K] ascending, -1 padded.
+template <int NT, int PER, int PER2>
+__global__ __launch_bounds__(NT) void pool_topk_kernel(
+    const float* __restrict__ block_max, int64_t nblk, const float* __restrict__ scores, int64_t ncols,
+    int32_t NB, int32_t* __restrict__ pool_out, int32_t K, int32_t* __restrict__ idx) {
+  __shared__ SelShared s;
+  __shared__ int32_t pool[SEL_POOL_MAX];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t q = blockIdx.y;
+  {
+    const int pw = 64 * PER * wv + lane;
+    const float* row = block_max + q * nblk;
+    uint32_t key[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) key[u] = pw + 64 * u < nblk ? select_key(row[pw + 64 * u]) : 0u;
+    const uint32_t n_sel = block_select<NT, PER>(s, key, (uint32_t)NB, [&](int p, uint32_t, uint32_t slot) {
+      pool[slot] = p;
+      if (pool_out) pool_out[q * NB + slot] = p;
+    });
+    for (int j = (int)n_sel + tid; j < NB; j += NT) {
+      pool[j] = -1;
+      if (pool_out) pool_out[q * NB + j] = -1;
+    }
+  }
+  __syncthreads();
+  const int pw = 64 * PER2 * wv + lane;
+  const int n = 8 * NB;
+  const float* row = scores + q * ncols;
+  uint32_t key[PER2];
+#pragma unroll
+  for (int u = 0; u < PER2; ++u) {
+    const int pp = pw + 64 * u;
+    key[u] = 0u;
+    if (pp < n) {
+      const int32_t blk = pool[pp >> 3];
+      const int64_t e = 8 * (int64_t)blk + (pp & 7);
+      if (blk >= 0 && e < ncols) key[u] = select_key(row[e]);
+    }
+  }
+  const uint32_t n_sel = block_select<NT, PER2>(s, key, (uint32_t)K, [&](int p, uint32_t, uint32_t slot) {
+    idx[q * K + slot] = 8 * pool[p >> 3] + (p & 7);
+  });
+  for (int j = (int)n_sel + tid; j < K; j += NT) idx[q * K + j] = -1;
 }
 
 // Block maxima over aligned 8-column blocks (-inf entries ignored).
@@ -350,7 +566,12 @@ __global__ __launch_bounds__(256) void block_max_kernel(const float* __restrict_
 }
 
 namespace {
-int64_t chunks_of(int64_t n) { return (n + SEL_CHUNK - 1) / SEL_CHUNK; }
+// Block shapes: 1024 threads (four waves per SIMD hide the latency of each
+// step) with 16 keys each for rows up to 16K keys, 32 up to 32K.
+constexpr int SEL_NT = 1024, SEL_PER_S = 16, SEL_PER_L = 32;
+static_assert(SEL_NT * SEL_PER_L == SEL_CHUNK_MAX, "block shape");
+
+int64_t chunks_of(int64_t n) { return (n + SEL_CHUNK_MAX - 1) / SEL_CHUNK_MAX; }
 
 // Candidate-buffer length per row needed by the multi-stage selection.
 int64_t cand_len(int64_t ncols, int32_t k) {
@@ -358,10 +579,42 @@ int64_t cand_len(int64_t ncols, int32_t k) {
   if (c <= 1) return 0;
   return c * (int64_t)k;
 }
+
+// One block per row over n <= SEL_CHUNK_MAX keys.
+template <int MODE>
+void launch_single(int64_t n, int64_t Q, const float* scores, int64_t ncols, const uint32_t* ck,
+                   const int32_t* cc, int64_t n_in, const int32_t* col_blocks, int64_t nblk_map, int32_t k,
+                   int32_t* idx, hipStream_t st) {
+  if (n <= SEL_NT * SEL_PER_S)
+    hipLaunchKernelGGL((select_kernel<MODE, true, SEL_NT, SEL_PER_S>), dim3(1, (unsigned)Q), dim3(SEL_NT), 0,
+                       st, scores, ncols, ck, cc, n_in, col_blocks, nblk_map, k, idx, nullptr, nullptr);
+  else
+    hipLaunchKernelGGL((select_kernel<MODE, true, SEL_NT, SEL_PER_L>), dim3(1, (unsigned)Q), dim3(SEL_NT), 0,
+                       st, scores, ncols, ck, cc, n_in, col_blocks, nblk_map, k, idx, nullptr, nullptr);
+}
+
+// Chunk candidates (keys0 / cols0, n_in per row) -> final ids.
+hipError_t merge_candidates(int64_t Q, int64_t n_in, int32_t k, uint32_t* keys0, int32_t* cols0,
+                            uint32_t* keys1, int32_t* cols1, const int32_t* col_blocks, int64_t nblk_map,
+                            int32_t* idx, hipStream_t st) {
+  hipError_t e;
+  while (chunks_of(n_in) > 1) {
+    const int64_t c2 = chunks_of(n_in);
+    hipLaunchKernelGGL((select_kernel<1, false, SEL_NT, SEL_PER_L>), dim3((unsigned)c2, (unsigned)Q),
+                       dim3(SEL_NT), 0, st, nullptr, 0, keys0, cols0, n_in, nullptr, 0, k, nullptr, keys1,
+                       cols1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    uint32_t* tk = keys0; keys0 = keys1; keys1 = tk;
+    int32_t* tc = cols0; cols0 = cols1; cols1 = tc;
+    n_in = c2 * k;
+  }
+  launch_single<1>(n_in, Q, nullptr, 0, keys0, cols0, n_in, col_blocks, nblk_map, k, idx, st);
+  return hipGetLastError();
+}
 }  // namespace
 
 size_t topk_workspace_bytes(int64_t Q, int64_t ncols, int32_t k) {
-  int64_t len = cand_len(ncols, k);
+  const int64_t len = cand_len(ncols, k);
   // two ping-pong candidate buffers of (key, column) pairs
   return (size_t)(2 * Q * len) * (sizeof(uint32_t) + sizeof(int32_t));
 }
@@ -369,35 +622,23 @@ size_t topk_workspace_bytes(int64_t Q, int64_t ncols, int32_t k) {
 hipError_t launch_topk(const float* scores, int64_t Q, int64_t ncols, const int32_t* col_blocks,
                        int32_t k, int32_t* idx, void* ws, hipStream_t st) {
   if (Q == 0) return hipSuccess;
-  int64_t nblk_map = (ncols + 7) >> 3;
-  int64_t c = chunks_of(ncols);
+  const int64_t nblk_map = (ncols + 7) >> 3;
+  const int64_t c = chunks_of(ncols);
   if (c <= 1) {
-    hipLaunchKernelGGL((select_kernel<0, true>), dim3(1, (unsigned)Q), dim3(SEL_THREADS), 0, st, scores,
-                       ncols, nullptr, nullptr, 0, col_blocks, nblk_map, k, idx, nullptr, nullptr);
+    launch_single<0>(ncols, Q, scores, ncols, nullptr, nullptr, 0, col_blocks, nblk_map, k, idx, st);
     return hipGetLastError();
   }
-  int64_t len = cand_len(ncols, k);
+  const int64_t len = cand_len(ncols, k);
   uint32_t* keys0 = reinterpret_cast<uint32_t*>(ws);
   int32_t* cols0 = reinterpret_cast<int32_t*>(keys0 + Q * len);
   uint32_t* keys1 = reinterpret_cast<uint32_t*>(cols0 + Q * len);
   int32_t* cols1 = reinterpret_cast<int32_t*>(keys1 + Q * len);
-  hipLaunchKernelGGL((select_kernel<0, false>), dim3((unsigned)c, (unsigned)Q), dim3(SEL_THREADS), 0, st,
-                     scores, ncols, nullptr, nullptr, 0, nullptr, 0, k, nullptr, keys0, cols0);
+  hipLaunchKernelGGL((select_kernel<0, false, SEL_NT, SEL_PER_L>), dim3((unsigned)c, (unsigned)Q),
+                     dim3(SEL_NT), 0, st, scores, ncols, nullptr, nullptr, 0, nullptr, 0, k, nullptr, keys0,
+                     cols0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int64_t n_in = c * k;
-  while (chunks_of(n_in) > 1) {
-    int64_t c2 = chunks_of(n_in);
-    hipLaunchKernelGGL((select_kernel<1, false>), dim3((unsigned)c2, (unsigned)Q), dim3(SEL_THREADS), 0,
-                       st, nullptr, 0, keys0, cols0, n_in, nullptr, 0, k, nullptr, keys1, cols1);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    uint32_t* tk = keys0; keys0 = keys1; keys1 = tk;
-    int32_t* tc = cols0; cols0 = cols1; cols1 = tc;
-    n_in = c2 * k;
-  }
-  hipLaunchKernelGGL((select_kernel<1, true>), dim3(1, (unsigned)Q), dim3(SEL_THREADS), 0, st, nullptr, 0,
-                     keys0, cols0, n_in, col_blocks, nblk_map, k, idx, nullptr, nullptr);
-  return hipGetLastError();
+  return merge_candidates(Q, c * k, k, keys0, cols0, keys1, cols1, col_blocks, nblk_map, idx, st);
 }
 
 size_t topk_gather_workspace_bytes(int64_t Q, int64_t nmap, int32_t k) {
@@ -409,38 +650,26 @@ hipError_t launch_topk_gather(const float* scores, int64_t Q, int64_t ncols, con
                               int64_t nmap, int32_t k, int32_t* idx, void* ws, hipStream_t st) {
   if (Q == 0) return hipSuccess;
   const int64_t n = 8 * nmap;
-  int64_t c = chunks_of(n);
+  const int64_t c = chunks_of(n);
   if (c <= 1) {
-    hipLaunchKernelGGL((select_kernel<2, true>), dim3(1, (unsigned)Q), dim3(SEL_THREADS), 0, st, scores,
-                       ncols, nullptr, nullptr, n, blocks, nmap, k, idx, nullptr, nullptr);
+    launch_single<2>(n, Q, scores, ncols, nullptr, nullptr, n, blocks, nmap, k, idx, st);
     return hipGetLastError();
   }
-  int64_t len = cand_len(n, k);
+  const int64_t len = cand_len(n, k);
   uint32_t* keys0 = reinterpret_cast<uint32_t*>(ws);
   int32_t* cols0 = reinterpret_cast<int32_t*>(keys0 + Q * len);
   uint32_t* keys1 = reinterpret_cast<uint32_t*>(cols0 + Q * len);
   int32_t* cols1 = reinterpret_cast<int32_t*>(keys1 + Q * len);
-  hipLaunchKernelGGL((select_kernel<2, false>), dim3((unsigned)c, (unsigned)Q), dim3(SEL_THREADS), 0, st,
-                     scores, ncols, nullptr, nullptr, n, blocks, nmap, k, nullptr, keys0, cols0);
+  hipLaunchKernelGGL((select_kernel<2, false, SEL_NT, SEL_PER_L>), dim3((unsigned)c, (unsigned)Q),
+                     dim3(SEL_NT), 0, st, scores, ncols, nullptr, nullptr, n, blocks, nmap, k, nullptr, keys0,
+                     cols0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int64_t n_in = c * k;
-  while (chunks_of(n_in) > 1) {
-    int64_t c2 = chunks_of(n_in);
-    hipLaunchKernelGGL((select_kernel<1, false>), dim3((unsigned)c2, (unsigned)Q), dim3(SEL_THREADS), 0,
-                       st, nullptr, 0, keys0, cols0, n_in, nullptr, 0, k, nullptr, keys1, cols1);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    uint32_t* tk = keys0; keys0 = keys1; keys1 = tk;
-    int32_t* tc = cols0; cols0 = cols1; cols1 = tc;
-    n_in = c2 * k;
-  }
-  hipLaunchKernelGGL((select_kernel<1, true>), dim3(1, (unsigned)Q), dim3(SEL_THREADS), 0, st, nullptr, 0,
-                     keys0, cols0, n_in, nullptr, 0, k, idx, nullptr, nullptr);
-  return hipGetLastError();
+  return merge_candidates(Q, c * k, k, keys0, cols0, keys1, cols1, nullptr, 0, idx, st);
 }
 
 size_t block_pool_workspace_bytes(int64_t Q, int64_t ncols, int32_t is_block_max, int32_t nb) {
-  int64_t nblk = is_block_max ? ncols : (ncols + 7) / 8;
+  const int64_t nblk = is_block_max ? ncols : (ncols + 7) / 8;
   size_t bm = is_block_max ? 0 : (size_t)(Q * nblk) * sizeof(float);
   bm = (bm + 255) & ~(size_t)255;
   return bm + topk_workspace_bytes(Q, nblk, nb);
@@ -455,16 +684,50 @@ hipError_t launch_block_pool(const float* values, int32_t is_block_max, int64_t 
   if (!is_block_max) {
     nblk = (ncols + 7) / 8;
     float* tmp = reinterpret_cast<float*>(ws);
-    int64_t tot = Q * nblk;
+    const int64_t tot = Q * nblk;
     hipLaunchKernelGGL(block_max_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, values, Q,
                        ncols, tmp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     bm = tmp;
-    size_t used = ((size_t)tot * sizeof(float) + 255) & ~(size_t)255;
+    const size_t used = ((size_t)tot * sizeof(float) + 255) & ~(size_t)255;
     rest += used;
   }
   return launch_topk(bm, Q, nblk, nullptr, nb, pool, rest, st);
+}
+
+size_t pool_topk_workspace_bytes(int64_t Q, int64_t nblk, int32_t nb, int32_t k) {
+  if (nblk <= SEL_CHUNK_MAX && nb <= SEL_POOL_MAX) return 0;
+  const size_t a = block_pool_workspace_bytes(Q, nblk, 1, nb);
+  const size_t b = topk_gather_workspace_bytes(Q, nb, k);
+  return a > b ? a : b;
+}
+
+hipError_t launch_pool_topk(const float* block_max, int64_t nblk, const float* scores, int64_t ncols,
+                            int64_t Q, int32_t nb, int32_t* pool, int32_t k, int32_t* idx, void* ws,
+                            hipStream_t st) {
+  if (Q == 0) return hipSuccess;
+  if (nblk <= SEL_CHUNK_MAX && nb <= SEL_POOL_MAX) {
+    const dim3 grid(1, (unsigned)Q), blk(SEL_NT);
+    const bool big1 = nblk > SEL_NT * SEL_PER_S, big2 = 8 * (int64_t)nb > SEL_NT * SEL_PER_S;
+    if (!big1 && !big2)
+      hipLaunchKernelGGL((pool_topk_kernel<SEL_NT, SEL_PER_S, SEL_PER_S>), grid, blk, 0, st, block_max, nblk,
+                         scores, ncols, nb, pool, k, idx);
+    else if (!big1)
+      hipLaunchKernelGGL((pool_topk_kernel<SEL_NT, SEL_PER_S, SEL_PER_L>), grid, blk, 0, st, block_max, nblk,
+                         scores, ncols, nb, pool, k, idx);
+    else if (!big2)
+      hipLaunchKernelGGL((pool_topk_kernel<SEL_NT, SEL_PER_L, SEL_PER_S>), grid, blk, 0, st, block_max, nblk,
+                         scores, ncols, nb, pool, k, idx);
+    else
+      hipLaunchKernelGGL((pool_topk_kernel<SEL_NT, SEL_PER_L, SEL_PER_L>), grid, blk, 0, st, block_max, nblk,
+                         scores, ncols, nb, pool, k, idx);
+    return hipGetLastError();
+  }
+  // rows longer than one block: chunked block pool, then the gathered selection
+  hipError_t e = launch_block_pool(block_max, 1, Q, nblk, nb, pool, ws, st);
+  if (e != hipSuccess) return e;
+  return launch_topk_gather(scores, Q, ncols, pool, nb, k, idx, ws, st);
 }
 
 }  // namespace csa

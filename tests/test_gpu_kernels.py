@@ -217,11 +217,14 @@ def test_topk_exact(Q, ncols, k, dist):
         assert np.array_equal(got[q], _oracle_topk_fp32(sc[q], k)), q
 
 
-def test_topk_pooled_mapping():
-    rng = np.random.default_rng(9)
-    Q, nb, k = 2, 300, 100
-    blocks = np.stack([np.sort(rng.choice(5000, nb, replace=False)) for _ in range(Q)]).astype(np.int32)
+@pytest.mark.parametrize("nb,k", [(300, 100), (5000, 512)])     # 5000 blocks: several chunks
+def test_topk_pooled_mapping(nb, k):
+    rng = np.random.default_rng(9 + nb)
+    Q = 2
+    blocks = np.stack([np.sort(rng.choice(3 * nb, nb, replace=False)) for _ in range(Q)]).astype(np.int32)
+    blocks[1, -7:] = -1
     sc = rng.integers(0, 30, (Q, 8 * nb)).astype(np.float32)
+    sc[1, -56:] = -np.inf
     idx = ops.csa_topk(t_(sc), k=k, col_blocks=t_(blocks))
     torch.cuda.synchronize()
     got = np_(idx)
