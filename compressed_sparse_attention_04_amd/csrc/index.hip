@@ -25,32 +25,44 @@ namespace csa {
 namespace {
 
 // One lane's share of a 16 x 128 operand fragment: 32 E4M3 bytes of one row,
-// bytes 32 * (lane / 16) .. +32.  A and B use the same byte -> k mapping
-// (k-step s takes bytes 8 s .. 8 s + 7 of the lane's 32), so the four
-// 16x16x32 products contract exactly the 128 channels.
+// bytes 16 g .. 16 g + 15 (u0) and 64 + 16 g .. 64 + 16 g + 15 (u1) with
+// g = lane / 16.  A and B use the same byte -> k mapping (k-steps 0, 1 take
+// u0, k-steps 2, 3 take u1), so the four 16x16x32 products contract exactly
+// the 128 channels.
 struct Raw32 { uint4 u0, u1; };
 struct Frag16 { f16x8 s[4]; };
 
 __device__ __forceinline__ Raw32 load_raw32(const uint8_t* row, bool live, int lane) {
   Raw32 r = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
   if (live) {
-    const uint4* p = reinterpret_cast<const uint4*>(row + 32 * (lane >> 4));
+    const uint4* p = reinterpret_cast<const uint4*>(row + 16 * (lane >> 4));
     r.u0 = p[0];
-    r.u1 = p[1];
+    r.u1 = p[4];
   }
   return r;
 }
 
-// Streaming variant: each indexer key row is read once per query, so the
-// loads are marked non-temporal (they need not stay in the caches).
-__device__ __forceinline__ Raw32 load_raw32_stream(const uint8_t* row, bool live, int lane) {
-  Raw32 r = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
-  if (live) {
-    const i32x4* p = reinterpret_cast<const i32x4*>(row + 32 * (lane >> 4));
-    const i32x4 v0 = __builtin_nontemporal_load(p), v1 = __builtin_nontemporal_load(p + 1);
-    r.u0 = make_uint4((uint32_t)v0[0], (uint32_t)v0[1], (uint32_t)v0[2], (uint32_t)v0[3]);
-    r.u1 = make_uint4((uint32_t)v1[0], (uint32_t)v1[1], (uint32_t)v1[2], (uint32_t)v1[3]);
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const uint8_t* p) {
+  if (NT) {
+    const i32x4 v = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
+    return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
   }
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// Key fragments are loaded whole-line and transposed through LDS: half h of a
+// 16-row fragment (rows 8h .. 8h+7, 1 KB) is one load instruction in which
+// lane i reads 16-byte chunk (i % 8) ^ (n / 2) of row n = 8h + i / 8 and
+// stores it to staging slot 64h + i.  Row n's chunk c therefore sits in slot
+// 8n + (c ^ (n / 2)): the stores are contiguous and the 16 rows a read
+// instruction touches fall in 16 distinct bank groups.
+__device__ __forceinline__ int stage_chunk(int lane, int h) { return (lane & 7) ^ ((8 * h + (lane >> 3)) >> 1); }
+__device__ __forceinline__ Raw32 read_staged(const uint4* stage, int lane) {
+  const int n = lane & 15, g = lane >> 4, sw = n >> 1;
+  Raw32 r;
+  r.u0 = stage[8 * n + (g ^ sw)];
+  r.u1 = stage[8 * n + ((4 + g) ^ sw)];
   return r;
 }
 
@@ -112,12 +124,16 @@ __device__ __forceinline__ void store_frag(float v, int64_t q, int64_t col, int6
 // ---------------------------------------------------------------------------
 // One query per block (decode, and every pooled call): the block covers
 // SQ_COLS columns, each of its 4 waves SQ_COLS / 4 of them, 16 per MFMA.
+// Key rows stream through whole-line loads (non-temporal for the dense scan,
+// whose rows are read once) and a per-wave LDS staging slot.
 constexpr int SQ_COLS = 1024;
 constexpr int SQ_UNROLL = 4;
 
 template <bool POOLED>
 __global__ __launch_bounds__(256) void score_query_kernel(ScoreArgs a, int64_t ncols) {
+  __shared__ uint4 stage_all[4][128];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint4* stage = stage_all[wave];
   const int64_t q = blockIdx.y;
   const int64_t seq = q / a.q_per_seq;
   const int nv_pos = visible_count(a.q_pos[q]);
@@ -134,43 +150,68 @@ __global__ __launch_bounds__(256) void score_query_kernel(ScoreArgs a, int64_t n
   const int64_t nblk = (ncols + 7) >> 3;
   const int64_t c_wave = (int64_t)blockIdx.x * SQ_COLS + wave * (SQ_COLS / 4);
   constexpr int NFRAG = SQ_COLS / 4 / 16;
-  // entry of this lane's column in every fragment of the wave (pool ids first)
-  int64_t ent[NFRAG];
-  bool valid[NFRAG];
-#pragma unroll
-  for (int f = 0; f < NFRAG; ++f) {
-    const int64_t col = c_wave + 16 * f + (lane & 15);
+  // pooled: lane i < 2 NFRAG holds the pool block of half i (8 columns from
+  // c_wave + 8 i); every half reads it back as a wave-uniform value
+  int32_t my_blk = -1;
+  if (POOLED && lane < 2 * NFRAG && c_wave + 8 * lane < ncols)
+    my_blk = a.pool[q * a.n_pool_blocks + ((c_wave + 8 * lane) >> 3)];
+  auto half_blk = [&](int i) { return __builtin_amdgcn_readlane(my_blk, i); };
+  // half h of fragment f: one whole-line load of 8 rows (lane / 8 picks the row)
+  auto load_half = [&](int f, int h) {
+    const int64_t col = c_wave + 16 * f + 8 * h + (lane >> 3);
     int64_t e = col;
     bool ok = col < ncols;
-    if (POOLED && ok) {
-      const int32_t blk = a.pool[q * a.n_pool_blocks + (col >> 3)];
-      ok = blk >= 0;
+    if (POOLED) {
+      const int32_t blk = half_blk(2 * f + h);
+      ok = ok && blk >= 0;
       e = 8 * (int64_t)blk + (col & 7);
     }
-    valid[f] = ok && e < nv;
-    ent[f] = e;
-  }
+    return (ok && e < nv) ? load16<!POOLED>(kbase + e * ID + 16 * stage_chunk(lane, h)) : make_uint4(0u, 0u, 0u, 0u);
+  };
+  auto load_frag = [&](int f, uint4& v0, uint4& v1) {
+    v0 = load_half(f, 0);
+    v1 = load_half(f, 1);
+  };
+  // validity of the lane's output column c_wave + 16 f + lane % 16
+  auto col_valid = [&](int f) {
+    const int64_t col = c_wave + 16 * f + (lane & 15);
+    bool ok = col < ncols;
+    int64_t e = col;
+    if (POOLED) {
+      const int32_t b0 = half_blk(2 * f), b1 = half_blk(2 * f + 1);
+      const int32_t blk = (lane & 8) ? b1 : b0;
+      ok = ok && blk >= 0;
+      e = 8 * (int64_t)blk + (col & 7);
+    }
+    return ok && e < nv;
+  };
   // software pipeline: the next SQ_UNROLL fragments load while these compute
-  Raw32 cur[SQ_UNROLL], nxt[SQ_UNROLL];
+  uint4 cur[SQ_UNROLL][2], nxt[SQ_UNROLL][2];
 #pragma unroll
-  for (int u = 0; u < SQ_UNROLL; ++u) cur[u] = load_raw32_stream(kbase + ent[u] * ID, valid[u], lane);
+  for (int u = 0; u < SQ_UNROLL; ++u) load_frag(u, cur[u][0], cur[u][1]);
 #pragma unroll
   for (int f0 = 0; f0 < NFRAG; f0 += SQ_UNROLL) {
     if (f0 + SQ_UNROLL < NFRAG) {
 #pragma unroll
-      for (int u = 0; u < SQ_UNROLL; ++u)
-        nxt[u] = load_raw32_stream(kbase + ent[f0 + SQ_UNROLL + u] * ID, valid[f0 + SQ_UNROLL + u], lane);
+      for (int u = 0; u < SQ_UNROLL; ++u) load_frag(f0 + SQ_UNROLL + u, nxt[u][0], nxt[u][1]);
     }
 #pragma unroll
     for (int u = 0; u < SQ_UNROLL; ++u) {
-      f32x4 acc = frag_mma(afrag, to_frag(cur[u]));
+      __builtin_amdgcn_wave_barrier();   // the previous fragment's staged reads come first
+      stage[lane] = cur[u][0];
+      stage[64 + lane] = cur[u][1];
+      __builtin_amdgcn_wave_barrier();   // stores before the transposed reads (LDS keeps wave order)
+      f32x4 acc = frag_mma(afrag, to_frag(read_staged(stage, lane)));
       float s = head_sum(acc, w4);
       int64_t col = c_wave + 16 * (f0 + u) + (lane & 15);
-      float v = valid[f0 + u] ? s : -__builtin_huge_valf();
+      float v = col_valid(f0 + u) ? s : -__builtin_huge_valf();
       store_frag(v, q, col, ncols, nblk, a.scores, POOLED ? nullptr : a.block_max, lane, lane < 16);
     }
 #pragma unroll
-    for (int u = 0; u < SQ_UNROLL; ++u) cur[u] = nxt[u];
+    for (int u = 0; u < SQ_UNROLL; ++u) {
+      cur[u][0] = nxt[u][0];
+      cur[u][1] = nxt[u][1];
+    }
   }
 }
 
