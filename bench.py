@@ -48,21 +48,28 @@ def visible_sum(cfg):
 
 
 def algorithmic_bytes(cfg):
-    """Minimum HBM bytes of one step (reads + writes the method needs)."""
-    Q = cfg.n_queries
+    """Minimum HBM bytes of one step (reads + writes the method needs).
+
+    Data that several queries of one sequence share (prefill chunks) is
+    counted once per sequence: indexer keys of the visible prefix, the union
+    of the entries the queries select (at most every entry), the window."""
+    Q, S = cfg.n_queries, cfg.n_seq
+    qps = Q // S
+    n_ent = cfg.entries_total                                   # entries visible to the last query
     b = 0
     n_idx = sum(1 for m in cfg.layers if m in ("F", "I"))
     for m in cfg.layers:
         if m == "F":
-            b += visible_sum(cfg) * 128                    # indexer keys
+            b += S * n_ent * 128                                # indexer keys, once per sequence
         elif m == "I":
-            b += Q * (16384 if cfg.build_pool else cfg.entries_total) * 128
-    b += Q * n_idx * (8 * 128 + 8 * 4)                      # indexer queries + weights
-    per_attn = 512 * 288 + 128 * 512 + 2 * 16 * 512 * 4     # entries, window, q, out
-    b += len(cfg.layers) * Q * per_attn
+            b += S * min(qps * (16384 if cfg.build_pool else n_ent), n_ent) * 128
+    b += Q * n_idx * (8 * 128 + 8 * 4)                          # indexer queries + weights
+    win_rows = 127 + (1 if cfg.kind == "decode" else cfg.chunk)
+    per_seq_attn = min(qps * 512, n_ent) * 288 + win_rows * 512  # selected entries (union), window
+    b += len(cfg.layers) * (S * per_seq_attn + Q * 2 * 16 * 512 * 4)   # + queries and outputs
     new_tok = 1 if cfg.kind == "decode" else cfg.chunk
-    b += cfg.n_seq * cfg.new_entries * (4 * 512 * 4 + 288) + 4 * 512 * 512 * 4   # compress
-    b += cfg.n_seq * new_tok * (512 * 4 + 512)                                  # window
+    b += S * cfg.new_entries * (4 * 512 * 4 + 288) + 4 * 512 * 512 * 4   # compress
+    b += S * new_tok * (512 * 4 + 512)                                  # window
     return b
 
 
