@@ -76,6 +76,12 @@ SMALL = [
                    build_pool=True, cid=103),
     W.small_config("prefill", n_seq=1, ctx_tokens=4 * 300, chunk=100, layers=("F", "U"), cid=104),
     W.small_config("decode", n_seq=2, ctx_tokens=4 * 100, layers=("F", "U"), cid=105),   # < K entries
+    # 33,000 blocks per row: more than one selection block holds, so the pool
+    # and the Top-K take the chunked path
+    W.small_config("decode", n_seq=1, ctx_tokens=4 * 8 * 33000, layers=("F", "I"), build_pool=True,
+                   synthetic_cache=True, cid=106),
+    W.small_config("decode", n_seq=1, ctx_tokens=4 * 8 * 33000, layers=("F", "U"), synthetic_cache=True,
+                   cid=107),
 ]
 
 
