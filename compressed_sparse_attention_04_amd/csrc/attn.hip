@@ -219,8 +219,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(AttnArgs a) {
       x[r] = ok ? S[r] * a.c_log2 : -__builtin_huge_valf();
       mx = fmaxf(mx, x[r]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const bool first = (m_run == -__builtin_huge_valf());
     const bool move = !first && (mx > m_run + AT_RESCALE);
     if (__ballot(move)) {
@@ -243,8 +242,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(AttnArgs a) {
       pr[r] = exp2f(x[r] - base);
       psum += pr[r];
     }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = sum_xor32(sum_xor16(psum));
     l_run += psum;
     const f16x4 pa = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
 

@@ -144,6 +144,39 @@ __device__ __forceinline__ f16x2 fp8x2_to_f16(uint32_t w) {
 __device__ __forceinline__ uint32_t f16x2_bits(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ f16x2 bits_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
 
+// ------------------------------------------------------ cross-lane steps ----
+// VALU-only exchanges (no LDS round trip).  gfx950's v_permlane16_swap with
+// both operands = v returns {rows 0,0,2,2 ; rows 1,1,3,3} of v (16-lane rows),
+// v_permlane32_swap {lanes 0-31 twice ; lanes 32-63 twice}; combining the two
+// halves is an xor-16 / xor-32 reduction with the lower row's value first.
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Max over each aligned group of 8 lanes, in every lane of the group (DPP:
+// quad_perm xor 1, xor 2, then row_half_mirror, which pairs the two quads).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  return fmaxf(v, dpp_f<0x141>(v));
+}
+
 // Key of a float for descending selection: larger key = larger value.
 // -inf and NaN map to 0 (never selected); -0 maps like +0.
 __device__ __forceinline__ uint32_t select_key(float x) {

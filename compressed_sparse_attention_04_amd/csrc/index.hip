@@ -101,7 +101,7 @@ __device__ __forceinline__ float head_sum(f32x4 acc, const float w4[4]) {
   s = fmaf(w4[1], fmaxf(acc[1], 0.f), s);
   s = fmaf(w4[2], fmaxf(acc[2], 0.f), s);
   s = fmaf(w4[3], fmaxf(acc[3], 0.f), s);
-  return s + __shfl_xor(s, 16);
+  return sum_xor16(s);
 }
 
 // Store one fragment's scores / block maxima.  `v` is the lane's score or
@@ -111,9 +111,7 @@ __device__ __forceinline__ void store_frag(float v, int64_t q, int64_t col, int6
                                            bool owner) {
   if (scores && owner && col < ncols) scores[q * ncols + col] = v;
   if (block_max) {
-    float m = fmaxf(v, __shfl_xor(v, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    m = fmaxf(m, __shfl_xor(m, 4));
+    const float m = max8(v);
     int64_t blk = col >> 3;
     if (owner && (lane & 7) == 0 && blk < nblk) block_max[q * nblk + blk] = m;
   }
