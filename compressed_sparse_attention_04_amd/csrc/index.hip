@@ -216,71 +216,94 @@ __global__ __launch_bounds__(256) void score_query_kernel(ScoreArgs a, int64_t n
 // ---------------------------------------------------------------------------
 // Query tiles (prefill: many queries of one sequence share the keys).  A
 // block holds 64 queries of one sequence (16 per wave, as 8 two-query A
-// fragments kept in registers) and streams ST_COLS columns; every wave
-// runs 8 MFMAs per 16-key fragment.
+// fragments kept in registers) and streams ST_COLS columns in rounds of two
+// 16-key fragments.  Every thread loads one whole-line 16-byte chunk of the
+// round after next while the waves run 8 MFMAs per fragment of the current
+// round out of LDS (the staging layout of the query kernel, double-buffered,
+// one barrier a round), so the four waves share one copy of the keys.
 constexpr int ST_QUERIES = 64;
 constexpr int ST_COLS = 512;
+constexpr int ST_ROUND = 32;
 
-__global__ __launch_bounds__(256) void score_tile_kernel(ScoreArgs a, int64_t ncols) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t tiles_per_seq = (a.q_per_seq + ST_QUERIES - 1) / ST_QUERIES;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void score_tile_kernel(ScoreArgs a, int64_t ncols) {
+  __shared__ uint4 stage[2][2][128];   // [buffer][fragment][slot]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qps = (int)a.q_per_seq;
+  const int tiles_per_seq = (qps + ST_QUERIES - 1) / ST_QUERIES;
   const int64_t seq = blockIdx.y / tiles_per_seq;
-  const int64_t qs0 = (blockIdx.y % tiles_per_seq) * ST_QUERIES + 16 * wave;   // in-sequence index
-  const int64_t qend = (seq + 1) * a.q_per_seq;
-  const int64_t qbase = seq * a.q_per_seq + qs0;
+  const int qs0 = (int)(blockIdx.y % tiles_per_seq) * ST_QUERIES + 16 * wave;   // in-sequence index
+  const int64_t qseq0 = seq * a.q_per_seq;
   const int row = lane & 15;
   Frag16 afrag[8];
   float w4[8][4];
-  int64_t nvq[8];
-  int64_t my_q[8];
-  int64_t nv_max = 0;
+  int nvq[8];            // visible columns of the query of this lane's C rows
+  uint32_t live = 0;     // bit f: that query exists
+  int nv_max = 0;
 #pragma unroll
   for (int f = 0; f < 8; ++f) {
-    int64_t qa = qbase + 2 * f + (row >> 3);           // query of this lane's A row
-    afrag[f] = load_qfrag(a.q_fp8, qa, row & 7, qa < qend, lane);
-    int64_t qo = qbase + 2 * f + (lane >> 5);          // query of this lane's C rows
-    my_q[f] = qo;
-    bool live = qo < qend;
-    int nvp = live ? visible_count(a.q_pos[qo]) : 0;
-    nvq[f] = nvp < a.n_entries ? nvp : a.n_entries;
+    const int qa = qs0 + 2 * f + (row >> 3);            // query of this lane's A row
+    afrag[f] = load_qfrag(a.q_fp8, qseq0 + qa, row & 7, qa < qps, lane);
+    const int qo = qs0 + 2 * f + (lane >> 5);           // query of this lane's C rows
+    const bool ok = qo < qps;
+    live |= (uint32_t)ok << f;
+    const int nvp = ok ? visible_count(a.q_pos[qseq0 + qo]) : 0;
+    nvq[f] = nvp < a.n_entries ? nvp : (int)a.n_entries;
     nv_max = nvq[f] > nv_max ? nvq[f] : nv_max;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      int h = 4 * ((lane >> 4) & 1) + r;
-      w4[f][r] = live ? a.w[qo * IH + h] : 0.f;
+      const int h = 4 * ((lane >> 4) & 1) + r;
+      w4[f][r] = ok ? a.w[(qseq0 + qo) * IH + h] : 0.f;
     }
   }
   // wave-uniform bound on the visible columns of these 16 queries
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    int64_t o = __shfl_xor(nv_max, off);
+    const int o = __shfl_xor(nv_max, off);
     nv_max = o > nv_max ? o : nv_max;
   }
   const uint8_t* kbase = a.k_fp8 + seq * a.k_rows * ID;
   const int64_t nblk = (ncols + 7) >> 3;
   const int64_t c0 = (int64_t)blockIdx.x * ST_COLS;
   const bool owner = (lane & 16) == 0;
-  for (int fc = 0; fc < ST_COLS / 16; ++fc) {
-    int64_t cbase = c0 + 16 * fc;
-    if (cbase >= ncols) break;
-    int64_t col = cbase + (lane & 15);
-    if (cbase >= nv_max) {
-      // no query of this wave sees these columns
+  // this thread's chunk of every round: fragment fr, half h, staging slot 64 h + li
+  const int fr = tid >> 7, h = (tid >> 6) & 1, li = tid & 63;
+  const int n_row = 8 * h + (li >> 3);
+  const int chunk = stage_chunk(li, h);
+  auto load_round = [&](int r) {
+    const int64_t col = c0 + ST_ROUND * r + 16 * fr + n_row;
+    return col < ncols ? *reinterpret_cast<const uint4*>(kbase + col * ID + 16 * chunk)
+                       : make_uint4(0u, 0u, 0u, 0u);
+  };
+  constexpr int N_ROUNDS = ST_COLS / ST_ROUND;
+  stage[0][fr][64 * h + li] = load_round(0);
+  uint4 nxt = load_round(1);
+  for (int r = 0; r < N_ROUNDS; ++r) {
+    __syncthreads();   // round r is in buffer r & 1; the other buffer's readers are done
+    if (r + 1 < N_ROUNDS) stage[(r + 1) & 1][fr][64 * h + li] = nxt;
+    if (r + 2 < N_ROUNDS) nxt = load_round(r + 2);
+#pragma unroll 1
+    for (int f2 = 0; f2 < 2; ++f2) {
+      const int64_t cbase = c0 + ST_ROUND * r + 16 * f2;
+      if (cbase >= ncols) break;
+      const int64_t col = cbase + (lane & 15);
+      if (cbase >= nv_max) {
+        // no query of this wave sees these columns
 #pragma unroll
-      for (int f = 0; f < 8; ++f)
-        if (my_q[f] < qend)
-          store_frag(-__builtin_huge_valf(), my_q[f], col, ncols, nblk, a.scores, a.block_max, lane,
-                     owner);
-      continue;
-    }
-    const Frag16 b = to_frag(load_raw32(kbase + col * ID, col < ncols && col < nv_max, lane));
+        for (int f = 0; f < 8; ++f)
+          if ((live >> f) & 1u)
+            store_frag(-__builtin_huge_valf(), qseq0 + qs0 + 2 * f + (lane >> 5), col, ncols, nblk, a.scores,
+                       a.block_max, lane, owner);
+        continue;
+      }
+      const Frag16 b = to_frag(read_staged(stage[r & 1][f2], lane));
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      f32x4 acc = frag_mma(afrag[f], b);
-      float s = head_sum(acc, w4[f]);
-      float v = (col < nvq[f]) ? s : -__builtin_huge_valf();
-      if (my_q[f] < qend)
-        store_frag(v, my_q[f], col, ncols, nblk, a.scores, a.block_max, lane, owner);
+      for (int f = 0; f < 8; ++f) {
+        const f32x4 acc = frag_mma(afrag[f], b);
+        const float sc = head_sum(acc, w4[f]);
+        const float v = (col < nvq[f]) ? sc : -__builtin_huge_valf();
+        if ((live >> f) & 1u)
+          store_frag(v, qseq0 + qs0 + 2 * f + (lane >> 5), col, ncols, nblk, a.scores, a.block_max, lane, owner);
+      }
     }
   }
 }
