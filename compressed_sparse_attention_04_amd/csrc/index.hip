@@ -255,24 +255,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       w4[f][r] = ok ? a.w[(qseq0 + qo) * IH + h] : 0.f;
     }
   }
-  // wave-uniform bound on the visible columns of these 16 queries
+  // wave-uniform bounds on the visible columns of these 16 queries
+  int nv_min = 0x7FFFFFFF;
+#pragma unroll
+  for (int f = 0; f < 8; ++f)
+    if ((live >> f) & 1u) nv_min = nvq[f] < nv_min ? nvq[f] : nv_min;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    const int o = __shfl_xor(nv_max, off);
+    const int o = __shfl_xor(nv_max, off), p = __shfl_xor(nv_min, off);
     nv_max = o > nv_max ? o : nv_max;
+    nv_min = p < nv_min ? p : nv_min;
   }
   const uint8_t* kbase = a.k_fp8 + seq * a.k_rows * ID;
-  const int64_t nblk = (ncols + 7) >> 3;
-  const int64_t c0 = (int64_t)blockIdx.x * ST_COLS;
-  const bool owner = (lane & 16) == 0;
+  const int nblk = (int)((ncols + 7) >> 3);
+  const int nc = (int)ncols;                 // < 2^23 (checked by the launcher)
+  const int c0 = blockIdx.x * ST_COLS;
+  // Buffer views of this tile's score / block-max rows; stores with an offset
+  // past the live rows (or the OOB marker) are dropped by the hardware, which
+  // replaces per-lane branches.  Row of fragment f for this lane:
+  // 16 wave + 2 f + lane / 32 (the f part goes in the scalar offset).
+  const int tile_q0 = (int)(blockIdx.y % tiles_per_seq) * ST_QUERIES;
+  const int live_rows = (qps - tile_q0) < ST_QUERIES ? (qps - tile_q0) : ST_QUERIES;
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc(a.scores + (qseq0 + tile_q0) * ncols, (short)0, live_rows * nc * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t brs = a.block_max ?
+      __builtin_amdgcn_make_buffer_rsrc(a.block_max + (qseq0 + tile_q0) * (int64_t)nblk, (short)0, live_rows * nblk * 4,
+                                        0x00020000) : srs;
+  constexpr uint32_t OOB = 0x80000000u;
+  const int lrow = 16 * wave + (lane >> 5);
   // this thread's chunk of every round: fragment fr, half h, staging slot 64 h + li
   const int fr = tid >> 7, h = (tid >> 6) & 1, li = tid & 63;
   const int n_row = 8 * h + (li >> 3);
   const int chunk = stage_chunk(li, h);
   auto load_round = [&](int r) {
-    const int64_t col = c0 + ST_ROUND * r + 16 * fr + n_row;
-    return col < ncols ? *reinterpret_cast<const uint4*>(kbase + col * ID + 16 * chunk)
-                       : make_uint4(0u, 0u, 0u, 0u);
+    const int col = c0 + ST_ROUND * r + 16 * fr + n_row;
+    return col < nc ? *reinterpret_cast<const uint4*>(kbase + (int64_t)col * ID + 16 * chunk)
+                    : make_uint4(0u, 0u, 0u, 0u);
   };
   constexpr int N_ROUNDS = ST_COLS / ST_ROUND;
   stage[0][fr][64 * h + li] = load_round(0);
@@ -283,26 +301,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     if (r + 2 < N_ROUNDS) nxt = load_round(r + 2);
 #pragma unroll 1
     for (int f2 = 0; f2 < 2; ++f2) {
-      const int64_t cbase = c0 + ST_ROUND * r + 16 * f2;
-      if (cbase >= ncols) break;
-      const int64_t col = cbase + (lane & 15);
+      const int cbase = c0 + ST_ROUND * r + 16 * f2;
+      if (cbase >= nc) break;
+      const int col = cbase + (lane & 15);
+      const uint32_t vo_s = (col < nc && (lane & 16) == 0) ? (uint32_t)(lrow * nc + col) * 4u : OOB;
+      const uint32_t vo_b = (a.block_max && col < nc && (lane & 23) == 0) ? (uint32_t)(lrow * nblk + (col >> 3)) * 4u : OOB;
       if (cbase >= nv_max) {
         // no query of this wave sees these columns
 #pragma unroll
-        for (int f = 0; f < 8; ++f)
-          if ((live >> f) & 1u)
-            store_frag(-__builtin_huge_valf(), qseq0 + qs0 + 2 * f + (lane >> 5), col, ncols, nblk, a.scores,
-                       a.block_max, lane, owner);
+        for (int f = 0; f < 8; ++f) {
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-__builtin_huge_valf()), srs, vo_s, 2 * f * nc * 4, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-__builtin_huge_valf()), brs, vo_b, 2 * f * nblk * 4, 0);
+        }
         continue;
       }
+      const bool all_visible = cbase + 16 <= nv_min;
       const Frag16 b = to_frag(read_staged(stage[r & 1][f2], lane));
 #pragma unroll
       for (int f = 0; f < 8; ++f) {
         const f32x4 acc = frag_mma(afrag[f], b);
-        const float sc = head_sum(acc, w4[f]);
-        const float v = (col < nvq[f]) ? sc : -__builtin_huge_valf();
-        if ((live >> f) & 1u)
-          store_frag(v, qseq0 + qs0 + 2 * f + (lane >> 5), col, ncols, nblk, a.scores, a.block_max, lane, owner);
+        float v = head_sum(acc, w4[f]);
+        if (!all_visible) v = (col < nvq[f]) ? v : -__builtin_huge_valf();
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srs, vo_s, 2 * f * nc * 4, 0);
+        if (a.block_max)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max8(v)), brs, vo_b, 2 * f * nblk * 4, 0);
       }
     }
   }
@@ -319,7 +341,7 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t st) {
   if (a.pool) {
     dim3 grid((unsigned)((ncols + SQ_COLS - 1) / SQ_COLS), (unsigned)Q);
     hipLaunchKernelGGL(score_query_kernel<true>, grid, dim3(256), 0, st, a, ncols);
-  } else if (a.q_per_seq >= 32) {
+  } else if (a.q_per_seq >= 32 && ncols < (int64_t(1) << 23)) {   // 32-bit buffer offsets
     int64_t tiles = (a.q_per_seq + ST_QUERIES - 1) / ST_QUERIES;
     dim3 grid((unsigned)((ncols + ST_COLS - 1) / ST_COLS), (unsigned)(a.n_seq * tiles));
     hipLaunchKernelGGL(score_tile_kernel, grid, dim3(256), 0, st, a, ncols);
