@@ -94,14 +94,36 @@ __device__ __forceinline__ Frag16 load_qfrag(const uint8_t* q_fp8, int64_t q, in
   return to_frag(load_raw32(q_fp8 + (q * IH + head) * ID, live, lane));
 }
 
+// ReLU on the bit pattern: a float with the sign bit set is a negative int32,
+// so max(bits, 0) maps every negative (and -0) to +0 and keeps the rest; one
+// integer max, where fmaxf would also have to quiet its inputs.
+__device__ __forceinline__ float relu(float x) {
+  const int b = __float_as_int(x);
+  return __int_as_float(b > 0 ? b : 0);
+}
+
 // Weighted ReLU head sum of one accumulator fragment; lanes 0-15 end with the
 // score of the first query (rows 0-7), lanes 32-47 with the second (rows 8-15).
+// The head weights are >= 0, so every score is >= +0 (or -inf where masked).
 __device__ __forceinline__ float head_sum(f32x4 acc, const float w4[4]) {
-  float s = w4[0] * fmaxf(acc[0], 0.f);
-  s = fmaf(w4[1], fmaxf(acc[1], 0.f), s);
-  s = fmaf(w4[2], fmaxf(acc[2], 0.f), s);
-  s = fmaf(w4[3], fmaxf(acc[3], 0.f), s);
+  float s = w4[0] * relu(acc[0]);
+  s = fmaf(w4[1], relu(acc[1]), s);
+  s = fmaf(w4[2], relu(acc[2]), s);
+  s = fmaf(w4[3], relu(acc[3]), s);
   return sum_xor16(s);
+}
+
+// Max over aligned groups of 8 lanes for scores (>= +0 or -inf): on that
+// set the float order is the int32 order of the bit patterns, so the DPP
+// steps are integer maxes.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) { return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false); }
+__device__ __forceinline__ float score_max8(float v) {
+  int b = __float_as_int(v), o;
+  o = dpp_i<0xB1>(b); b = b > o ? b : o;
+  o = dpp_i<0x4E>(b); b = b > o ? b : o;
+  o = dpp_i<0x141>(b); b = b > o ? b : o;
+  return __int_as_float(b);
 }
 
 // Store one fragment's scores / block maxima.  `v` is the lane's score or
@@ -111,7 +133,7 @@ __device__ __forceinline__ void store_frag(float v, int64_t q, int64_t col, int6
                                            bool owner) {
   if (scores && owner && col < ncols) scores[q * ncols + col] = v;
   if (block_max) {
-    const float m = max8(v);
+    const float m = score_max8(v);
     int64_t blk = col >> 3;
     if (owner && (lane & 7) == 0 && blk < nblk) block_max[q * nblk + blk] = m;
   }
@@ -324,7 +346,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
         if (!all_visible) v = (col < nvq[f]) ? v : -__builtin_huge_valf();
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srs, vo_s, 2 * f * nc * 4, 0);
         if (a.block_max)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max8(v)), brs, vo_b, 2 * f * nblk * 4, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score_max8(v)), brs, vo_b, 2 * f * nblk * 4, 0);
       }
     }
   }
