@@ -34,7 +34,7 @@ constexpr int AT_WAVES = 4;
 constexpr int AT_THREADS = 64 * AT_WAVES;
 constexpr int AT_QCH = D / AT_WAVES;             // channels per wave
 constexpr int AT_KPITCH = AT_QCH * 2 + 16;       // bytes per LDS key row of one wave (fp16 + pad)
-constexpr int AT_DEPTH = 4;                      // tiles of key bytes in flight
+constexpr int AT_DEPTH = 2;                      // tiles of key bytes in flight
 
 struct AttnArgs {
   const float* q;
@@ -132,7 +132,8 @@ struct AttnLds {
   f32x4 s[2][AT_WAVES][64];                   // partial S, double-buffered by tile parity
 };
 
-__global__ __launch_bounds__(AT_THREADS) void attn_kernel(AttnArgs a) {
+// Four waves per SIMD (four blocks per CU): registers capped at 128 per lane.
+__global__ __launch_bounds__(AT_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnLds lds;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -342,7 +343,9 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
 namespace {
 void attn_plan(int64_t Q, int32_t k, int* n_splits, int* tiles_per_split) {
   int n_tiles = (k + NWIN + AT_TILE - 1) / AT_TILE;
-  int64_t want = Q >= 512 ? 1 : (512 + Q - 1) / Q;       // aim at ~512 blocks of 4 waves
+  // ~512 blocks: more splits buy little once every CU has work, while each
+  // split adds a 32 KiB partial output to write and combine
+  int64_t want = Q >= 512 ? 1 : (512 + Q - 1) / Q;
   int max_split = (n_tiles + 1) / 2;                      // at least 2 tiles per split
   max_split = max_split < AT_MAX_SPLITS ? max_split : AT_MAX_SPLITS;
   int s = (int)(want < max_split ? want : max_split);
