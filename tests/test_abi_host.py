@@ -115,6 +115,21 @@ def test_layer_validation(lib):
     assert lib.csa_layer_workspace_size(7, ctypes.byref(a)) == 0
 
 
+def test_layer_pool_size_validation(lib):
+    """Pool sizes outside [top_k, 4096] are rejected before anything is launched."""
+    a = _lib.CsaLayerArgs()
+    for f in ["codes", "scales", "k_fp8", "win", "q_pos", "q_attn", "q_idx", "w_idx", "pool_blocks",
+              "idx", "out"]:
+        setattr(a, f, 1 << 20)
+    a.kv_rows = a.k_rows = a.n_entries = 1000
+    a.win_cap, a.n_seq, a.q_per_seq = 128, 2, 1
+    a.sm_scale, a.top_k, a.build_pool = 0.044, 512, 1
+    a.ws, a.ws_bytes = 1 << 20, 1 << 40
+    for nb in (4097, 5000, 511, 0):
+        a.n_pool_blocks = nb
+        assert lib.csa_layer_full(ctypes.byref(a), None) in (UNSUPPORTED, INVALID), nb
+
+
 @pytest.mark.skipif(__import__("torch").cuda.is_available(),
                     reason="would launch on fake pointers; host-only check")
 def test_valid_layer_args_pass_validation(lib):
