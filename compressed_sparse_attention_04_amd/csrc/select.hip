@@ -567,8 +567,14 @@ __global__ __launch_bounds__(256) void block_max_kernel(const float* __restrict_
 
 namespace {
 // Block shapes: 1024 threads (four waves per SIMD hide the latency of each
-// step) with 16 keys each for rows up to 16K keys, 32 up to 32K.
+// step) with 16 keys each for rows up to 16K keys, 32 up to 32K.  Many rows
+// (prefill chunks) are throughput-bound instead: single selections then use
+// 256 threads with 64 keys each, which fit four blocks per CU and spend a
+// quarter of the per-row wave time on the block-wide steps (the two-phase
+// pool kernel at that shape holds too many registers for it to pay).
 constexpr int SEL_NT = 1024, SEL_PER_S = 16, SEL_PER_L = 32;
+constexpr int SEL_NT_T = 256, SEL_PER_T = 64;
+constexpr int64_t SEL_MANY_ROWS = 1024;
 static_assert(SEL_NT * SEL_PER_L == SEL_CHUNK_MAX, "block shape");
 
 int64_t chunks_of(int64_t n) { return (n + SEL_CHUNK_MAX - 1) / SEL_CHUNK_MAX; }
@@ -585,7 +591,10 @@ template <int MODE>
 void launch_single(int64_t n, int64_t Q, const float* scores, int64_t ncols, const uint32_t* ck,
                    const int32_t* cc, int64_t n_in, const int32_t* col_blocks, int64_t nblk_map, int32_t k,
                    int32_t* idx, hipStream_t st) {
-  if (n <= SEL_NT * SEL_PER_S)
+  if (Q >= SEL_MANY_ROWS && n <= SEL_NT_T * SEL_PER_T)
+    hipLaunchKernelGGL((select_kernel<MODE, true, SEL_NT_T, SEL_PER_T>), dim3(1, (unsigned)Q), dim3(SEL_NT_T), 0,
+                       st, scores, ncols, ck, cc, n_in, col_blocks, nblk_map, k, idx, nullptr, nullptr);
+  else if (n <= SEL_NT * SEL_PER_S)
     hipLaunchKernelGGL((select_kernel<MODE, true, SEL_NT, SEL_PER_S>), dim3(1, (unsigned)Q), dim3(SEL_NT), 0,
                        st, scores, ncols, ck, cc, n_in, col_blocks, nblk_map, k, idx, nullptr, nullptr);
   else

@@ -59,7 +59,8 @@ def test_full_layer_sizes(n_ent, top_k, n_pool, build_pool):
             check_attn(go[s], ref.out)
 
 
-@pytest.mark.parametrize("Q,ncols,k", [(2, 100000, 1), (1, 100000, 4096), (3, 7, 4096)])
+@pytest.mark.parametrize("Q,ncols,k", [(2, 100000, 1), (1, 100000, 4096), (3, 7, 4096), (1100, 5000, 512),
+                                       (1030, 16384, 512)])   # 1,024+ rows: the many-rows block shape
 def test_topk_extreme_k(Q, ncols, k):
     rng = np.random.default_rng(ncols + k)
     sc = rng.standard_normal((Q, ncols)).astype(np.float32)
