@@ -247,6 +247,10 @@ constexpr int ST_QUERIES = 64;
 constexpr int ST_COLS = 512;
 constexpr int ST_ROUND = 32;
 
+// BM: also write the 8-column block maxima (a template parameter, so that the
+// unrolled fragment loop has no branch and the MFMAs of one query fragment
+// overlap the epilogue of another).
+template <bool BM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void score_tile_kernel(ScoreArgs a, int64_t ncols) {
   __shared__ uint4 stage[2][2][128];   // [buffer][fragment][slot]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int live_rows = (qps - tile_q0) < ST_QUERIES ? (qps - tile_q0) : ST_QUERIES;
   const __amdgpu_buffer_rsrc_t srs =
       __builtin_amdgcn_make_buffer_rsrc(a.scores + (qseq0 + tile_q0) * ncols, (short)0, live_rows * nc * 4, 0x00020000);
-  const __amdgpu_buffer_rsrc_t brs = a.block_max ?
+  const __amdgpu_buffer_rsrc_t brs = BM ?
       __builtin_amdgcn_make_buffer_rsrc(a.block_max + (qseq0 + tile_q0) * (int64_t)nblk, (short)0, live_rows * nblk * 4,
                                         0x00020000) : srs;
   constexpr uint32_t OOB = 0x80000000u;
@@ -327,13 +331,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       if (cbase >= nc) break;
       const int col = cbase + (lane & 15);
       const uint32_t vo_s = (col < nc && (lane & 16) == 0) ? (uint32_t)(lrow * nc + col) * 4u : OOB;
-      const uint32_t vo_b = (a.block_max && col < nc && (lane & 23) == 0) ? (uint32_t)(lrow * nblk + (col >> 3)) * 4u : OOB;
+      const uint32_t vo_b = (BM && col < nc && (lane & 23) == 0) ? (uint32_t)(lrow * nblk + (col >> 3)) * 4u : OOB;
       if (cbase >= nv_max) {
         // no query of this wave sees these columns
 #pragma unroll
         for (int f = 0; f < 8; ++f) {
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-__builtin_huge_valf()), srs, vo_s, 2 * f * nc * 4, 0);
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-__builtin_huge_valf()), brs, vo_b, 2 * f * nblk * 4, 0);
+          if (BM) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-__builtin_huge_valf()), brs, vo_b, 2 * f * nblk * 4, 0);
         }
         continue;
       }
@@ -345,8 +349,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
         float v = head_sum(acc, w4[f]);
         if (!all_visible) v = (col < nvq[f]) ? v : -__builtin_huge_valf();
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srs, vo_s, 2 * f * nc * 4, 0);
-        if (a.block_max)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score_max8(v)), brs, vo_b, 2 * f * nblk * 4, 0);
+        if (BM) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score_max8(v)), brs, vo_b, 2 * f * nblk * 4, 0);
       }
     }
   }
@@ -366,7 +369,8 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t st) {
   } else if (a.q_per_seq >= 32 && ncols < (int64_t(1) << 23)) {   // 32-bit buffer offsets
     int64_t tiles = (a.q_per_seq + ST_QUERIES - 1) / ST_QUERIES;
     dim3 grid((unsigned)((ncols + ST_COLS - 1) / ST_COLS), (unsigned)(a.n_seq * tiles));
-    hipLaunchKernelGGL(score_tile_kernel, grid, dim3(256), 0, st, a, ncols);
+    if (a.block_max) hipLaunchKernelGGL(score_tile_kernel<true>, grid, dim3(256), 0, st, a, ncols);
+    else hipLaunchKernelGGL(score_tile_kernel<false>, grid, dim3(256), 0, st, a, ncols);
   } else {
     dim3 grid((unsigned)((ncols + SQ_COLS - 1) / SQ_COLS), (unsigned)Q);
     hipLaunchKernelGGL(score_query_kernel<false>, grid, dim3(256), 0, st, a, ncols);
