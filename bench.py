@@ -138,24 +138,38 @@ def time_kernel(fn, reps):
     return t0.elapsed_time(t1) / reps
 
 
-def dense_score_call(wl, st, block_max):
-    """The Full layer's dense indexer launch, with the step's own inputs."""
+# The Full layer fuses its Top-K into a selection kernel that rescores the
+# best blocks, so its dense scan writes block maxima only, whenever the
+# layer fits that kernel (at most 32,768 blocks, a pool of at most 4,096
+# blocks, top_k at most 1,024 and no larger than the pool).
+FUSED_MAX_BLOCKS, FUSED_MAX_POOL, FUSED_MAX_K = 32768, 4096, 1024
+
+
+def dense_score_call(wl, st):
+    """The Full layer's dense indexer launch, with the step's own inputs and
+    the outputs the step's launch writes."""
     import torch
+    import workloads as W
     from compressed_sparse_attention_04_amd import ops
     cfg, t = wl.cfg, wl.tensors
     li = cfg.layers.index("F")
     Q, nc = cfg.n_queries, st.n_entries
-    scores = torch.empty((Q, nc), dtype=torch.float32, device="cuda")
-    bm = torch.empty((Q, (nc + 7) // 8), dtype=torch.float32, device="cuda") if block_max else None
+    nblk = (nc + 7) // 8
+    nb = W.POOL_BLOCKS if cfg.build_pool else W.TOP_K
+    fused = nblk <= FUSED_MAX_BLOCKS and nb <= FUSED_MAX_POOL and W.TOP_K <= FUSED_MAX_K and nb >= W.TOP_K
+    scores = None if fused else torch.empty((Q, nc), dtype=torch.float32, device="cuda")
+    bm = torch.empty((Q, nblk), dtype=torch.float32, device="cuda") if (fused or cfg.build_pool) else None
     lib = ops._lib.load()
     args = (ops._p(t["q_fp8"][li]), ops._p(t["w_idx"][li]), ops._p(t["q_pos"]), cfg.n_seq, st.q_per_seq,
-            ops._p(t["k_fp8"]), t["k_fp8"].shape[1], nc, None, 0, ops._p(scores), ops._p(bm))
+            ops._p(t["k_fp8"]), t["k_fp8"].shape[1], nc, None, 0,
+            None if scores is None else ops._p(scores), None if bm is None else ops._p(bm))
 
     def fn():
         rc = lib.csa_index_score(*args, ops._stream())
         if rc:
             raise RuntimeError(lib.csa_last_error().decode())
-    return fn, scores, bm
+    out_bytes = (0 if scores is None else Q * nc * 4) + (0 if bm is None else Q * nblk * 4)
+    return fn, out_bytes
 
 
 def source_digest(files):
@@ -203,14 +217,11 @@ def measure_config(cid, steps, warmup, use_graph, kernel_reps):
     else:
         res["tokens_per_s"] = cfg.n_queries / (ms * 1e-3)
     # dominant kernel: the Full layer's dense indexer launch
-    fn, _, _ = dense_score_call(wl, st, block_max=cfg.build_pool and cfg.kind == "decode")
+    fn, out_bytes = dense_score_call(wl, st)
     kms = time_kernel(fn, kernel_reps)
     res["indexer_ms"] = kms
     if cfg.kind == "decode":
-        nc = st.n_entries
-        per = visible_sum(cfg) * 128 + cfg.n_queries * nc * 4
-        if cfg.build_pool:
-            per += cfg.n_queries * ((nc + 7) // 8) * 4
+        per = visible_sum(cfg) * 128 + out_bytes
         res["indexer_bytes"] = per
         res["indexer_gbps"] = per / (kms * 1e-3) / 1e9
     else:
@@ -290,7 +301,7 @@ def main():
     main_res = measure_config(args.config, args.steps, args.warmup, not args.no_graph,
                               kernel_reps=max(5, args.steps))
     cfg = W.CONFIGS[args.config]
-    digest = source_digest(["index.hip", "common.h"])
+    digest = source_digest(["index.hip", "index_core.h", "common.h"])
     if cfg.kind == "decode":
         key = "score_query_dense_" + cfg.name
         achieved = main_res["indexer_gbps"]

@@ -56,10 +56,14 @@ size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 // whenever P >= K (a block ranked above the block of a Top-K entry e has a
 // max >= s(e), equality only at a lower block id, whose entry then ties with
 // and precedes e).  P is the pool when one is built, else K blocks.
+//
+// When the pool, top_k and the row fit one block (full_select_supported) the
+// Full layer writes no scores at all: the dense scan emits only the block
+// maxima, and the fused selection rescores the entries of the top_k blocks.
 struct LayerPlan {
   int64_t Q = 0, ncols = 0, nblk = 0;
   size_t off_scores = 0, off_bm = 0, off_blocks = 0, off_sel = 0, off_attn = 0, total = 0;
-  bool pooled = false;
+  bool pooled = false, fused_full = false;
 };
 
 LayerPlan plan_layer(int32_t mode, const csa_layer_args* a) {
@@ -69,19 +73,24 @@ LayerPlan plan_layer(int32_t mode, const csa_layer_args* a) {
   if (mode == CSA_MODE_FULL || mode == CSA_MODE_REINDEX) {
     p.pooled = (mode == CSA_MODE_REINDEX) && a->pool_blocks != nullptr;
     p.ncols = p.pooled ? (int64_t)CSA_BLOCK * a->n_pool_blocks : a->n_entries;
-    p.off_scores = off;
-    off += round_up((size_t)(p.Q * p.ncols) * sizeof(float));
+    const int32_t nb = a->build_pool ? a->n_pool_blocks : a->top_k;
+    p.nblk = (p.ncols + 7) / 8;
+    p.fused_full = mode == CSA_MODE_FULL && full_select_supported(p.nblk, nb, a->top_k);
+    if (!p.fused_full) {
+      p.off_scores = off;
+      off += round_up((size_t)(p.Q * p.ncols) * sizeof(float));
+    }
     size_t sel = 0;
     if (mode == CSA_MODE_FULL) {
-      p.nblk = (p.ncols + 7) / 8;
       p.off_bm = off;
       off += round_up((size_t)(p.Q * p.nblk) * sizeof(float));
-      const int32_t nb = a->build_pool ? a->n_pool_blocks : a->top_k;
-      if (!a->build_pool) {
-        p.off_blocks = off;
-        off += round_up((size_t)(p.Q * nb) * sizeof(int32_t));
+      if (!p.fused_full) {
+        if (!a->build_pool) {
+          p.off_blocks = off;
+          off += round_up((size_t)(p.Q * nb) * sizeof(int32_t));
+        }
+        sel = pool_topk_workspace_bytes(p.Q, p.nblk, nb, a->top_k);
       }
-      sel = pool_topk_workspace_bytes(p.Q, p.nblk, nb, a->top_k);
     } else {
       sel = topk_workspace_bytes(p.Q, p.ncols, a->top_k);
     }
@@ -367,7 +376,7 @@ static csa_status run_attention(const char* fn, const csa_layer_args* a, const L
 static csa_status run_index(const char* fn, int32_t mode, const csa_layer_args* a, const LayerPlan& p,
                             hipStream_t st) {
   char* ws = reinterpret_cast<char*>(a->ws);
-  float* scores = reinterpret_cast<float*>(ws + p.off_scores);
+  float* scores = p.fused_full ? nullptr : reinterpret_cast<float*>(ws + p.off_scores);
   float* bm = (mode == CSA_MODE_FULL) ? reinterpret_cast<float*>(ws + p.off_bm) : nullptr;
   ScoreArgs s{a->q_idx, a->w_idx, a->q_pos, a->n_seq, a->q_per_seq, a->k_fp8, a->k_rows, a->n_entries,
               p.pooled ? a->pool_blocks : nullptr, a->n_pool_blocks, scores, bm};
@@ -378,6 +387,11 @@ static csa_status run_index(const char* fn, int32_t mode, const csa_layer_args* 
                                   a->idx, ws + p.off_sel, st),
                       fn);
   // Full: best blocks (the pool, or top_k blocks), then Top-K among their entries
+  if (p.fused_full)
+    return hip_status(launch_full_select(bm, p.nblk, p.Q, a->build_pool ? a->n_pool_blocks : a->top_k,
+                                         a->build_pool ? a->pool_blocks : nullptr, a->top_k, a->idx, a->q_idx,
+                                         a->w_idx, a->q_pos, a->q_per_seq, a->k_fp8, a->k_rows, a->n_entries, st),
+                      fn);
   int32_t* blocks = a->build_pool ? a->pool_blocks : reinterpret_cast<int32_t*>(ws + p.off_blocks);
   const int32_t nb = a->build_pool ? a->n_pool_blocks : a->top_k;
   return hip_status(launch_pool_topk(bm, p.nblk, scores, p.ncols, p.Q, nb, blocks, a->top_k, a->idx,

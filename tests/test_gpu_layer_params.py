@@ -1,10 +1,14 @@
 """GPU parity of the Full-layer entry point at non-default Top-K and pool
 sizes, and of the kernels at the extremes of their size range.
 
-Top-K 64 / 2048 / 4096 and pools of 2,048 and 4,096 blocks (the largest the
-entry point accepts) go through the fused pool + Top-K kernel (rows of more
-than 32,768 blocks take its chunked path, covered by the layer tests); the
-compression chain runs with RoPE on 0, 64 and 512 channels.
+Top-K 64 / 512 / 1024 / 2048 / 4096 and pools of 1,024 to 4,096 blocks (the
+largest the entry point accepts): Top-K up to 1,024 with a pool at least that
+large goes through the selection that rescores the best blocks, larger Top-K
+through the pool + Top-K kernel over written scores (rows of more than 32,768
+blocks take its chunked path, covered by the layer tests).  Keys with one
+value, or a few distinct rows, make every block max tie, which exercises the
+lower-id rule across the block and entry selections.  The compression chain
+runs with RoPE on 0, 64 and 512 channels.
 """
 
 import numpy as np
@@ -24,15 +28,19 @@ def t_(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-@pytest.mark.parametrize("n_ent,top_k,n_pool,build_pool", [(20000, 2048, 4096, True), (45000, 512, 4096, True),
-                                                           (20000, 64, 2048, True), (3000, 4096, 2048, False),
-                                                           (40000, 2048, 2048, False)])
-def test_full_layer_sizes(n_ent, top_k, n_pool, build_pool):
+def _full_layer(n_ent, top_k, n_pool, build_pool, keys="normal"):
     rng = np.random.default_rng(n_ent + top_k + n_pool)
     n_seq, win_cap = 2, 128
     codes = rng.integers(0, 256, (n_seq, n_ent, 256)).astype(np.uint8)
     scales = rng.integers(0x28, 0x31, (n_seq, n_ent, 32)).astype(np.uint8)
-    k8 = formats.e4m3_encode(rng.standard_normal((n_seq, n_ent, 128)))
+    if keys == "normal":
+        k8 = formats.e4m3_encode(rng.standard_normal((n_seq, n_ent, 128)))
+    elif keys == "const":
+        k8 = np.broadcast_to(formats.e4m3_encode(rng.standard_normal((n_seq, 1, 128))), (n_seq, n_ent, 128))
+    else:   # a few distinct rows
+        rows = formats.e4m3_encode(rng.standard_normal((n_seq, 4, 128)))
+        k8 = rows[np.arange(n_seq)[:, None], rng.integers(0, 4, (n_seq, n_ent))]
+    k8 = np.ascontiguousarray(k8)
     q8 = formats.e4m3_encode(rng.standard_normal((n_seq, 8, 128)))
     w = rng.random((n_seq, 8)).astype(np.float32)
     q_attn = rng.standard_normal((n_seq, 16, 512)).astype(np.float32)
@@ -57,6 +65,23 @@ def test_full_layer_sizes(n_ent, top_k, n_pool, build_pool):
         if check_topk_set(gi[s], ref.scores, ref.idx, top_k) == 0:
             assert np.array_equal(np.sort(gi[s]), np.sort(ref.idx))
             check_attn(go[s], ref.out)
+
+
+@pytest.mark.parametrize("n_ent,top_k,n_pool,build_pool", [(20000, 2048, 4096, True), (45000, 512, 4096, True),
+                                                           (20000, 64, 2048, True), (3000, 4096, 2048, False),
+                                                           (40000, 2048, 2048, False), (45000, 1024, 4096, True),
+                                                           (45000, 512, 1024, False)])
+def test_full_layer_sizes(n_ent, top_k, n_pool, build_pool):
+    _full_layer(n_ent, top_k, n_pool, build_pool)
+
+
+@pytest.mark.parametrize("n_ent,top_k,n_pool,build_pool,keys", [(3000, 1024, 1024, True, "const"),
+                                                                (45000, 512, 2048, True, "few"),
+                                                                (45000, 512, 2048, True, "const"),
+                                                                (45000, 512, 1024, False, "const"),
+                                                                (20000, 2048, 2048, False, "few")])
+def test_full_layer_ties(n_ent, top_k, n_pool, build_pool, keys):
+    _full_layer(n_ent, top_k, n_pool, build_pool, keys)
 
 
 @pytest.mark.parametrize("Q,ncols,k", [(2, 100000, 1), (1, 100000, 4096), (3, 7, 4096), (1100, 5000, 512),
