@@ -6,10 +6,11 @@
 // dequantized before attention (no FP4 matmul), the SWA window stays FP8 and
 // covers n_win = 128 tokens.
 //
-// Work item = (query, split of its key slots); one block of four waves per
-// work item, wave w owning channels 128 w .. 128 w + 127.  Key slots 0..k-1
-// are the selected entries, slots k..k+127 the window tokens p-127..p.  Per
-// 16-slot tile:
+// Work item = (query, split of its key slots); one block of KG key groups of
+// four waves per work item, wave w of a group owning channels 128 w .. 128 w
+// + 127, and group kg taking the split's tiles kg, kg + KG, ...  Key slots
+// 0..k-1 are the selected entries, slots k..k+127 the window tokens
+// p-127..p.  Per 16-slot tile:
 //   1. lane (j, g) of wave w loads channels 128 w + 32 g .. + 31 of key j
 //      (16 FP4 code bytes + 2 E4M3 scale bytes, or 32 E4M3 window bytes) and
 //      dequantizes them to fp16 in registers (exact);
@@ -22,15 +23,17 @@
 //      (8 x v_mfma 16x16x16).  Output channel of N-tile n in lane column c is
 //      128 w + 8 c + n, so every lane reads 16 contiguous bytes per key.
 // Key bytes are loaded AT_DEPTH tiles ahead of use and slot ids 2 AT_DEPTH
-// tiles ahead.  With several splits per query the partial (O, max, sum)
-// triples are combined by attn_combine_kernel.
+// tiles ahead.  The key groups of a block merge their (O, max, sum) through
+// LDS at the end, so a split writes one partial however many groups it has;
+// with several splits per query the partials are combined by
+// attn_combine_kernel.
 #include "common.h"
 #include "kernels.h"
 
 namespace csa {
 
 constexpr int AT_TILE = 16;
-constexpr int AT_WAVES = 4;
+constexpr int AT_WAVES = 4;                      // waves of one key group
 constexpr int AT_THREADS = 64 * AT_WAVES;
 constexpr int AT_QCH = D / AT_WAVES;             // channels per wave
 constexpr int AT_KPITCH = AT_QCH * 2 + 16;       // bytes per LDS key row of one wave (fp16 + pad)
@@ -127,16 +130,26 @@ __device__ __forceinline__ f16x8 key_slice(const RawKey& r, int s) {
 // and O is rarely rescaled.
 constexpr float AT_RESCALE = 8.0f;
 
+template <int KG>
 struct AttnLds {
-  uint8_t k[AT_WAVES][AT_TILE * AT_KPITCH];   // fp16 key slices, per wave
-  f32x4 s[2][AT_WAVES][64];                   // partial S, double-buffered by tile parity
+  union {
+    struct {
+      uint8_t k[KG * AT_WAVES][AT_TILE * AT_KPITCH];   // fp16 key slices, per wave
+      f32x4 s[2][KG][AT_WAVES][64];                      // partial S, double-buffered by tile parity
+    } loop;
+    struct {
+      float o[KG > 1 ? KG - 1 : 1][AT_WAVES][32][64];     // scaled O of groups 1..KG-1
+      float ml[KG][2][HEADS];                            // (max, sum) per group and head
+    } red;
+  };
 };
 
-// Four waves per SIMD (four blocks per CU): registers capped at 128 per lane.
-__global__ __launch_bounds__(AT_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) AttnLds lds;
+// Four waves per SIMD: registers capped at 128 per lane.
+template <int KG>
+__global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu(4))) void attn_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) AttnLds<KG> lds;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = (tid >> 6) & (AT_WAVES - 1), kg = tid >> 8;
   const int j = lane & 15;      // key slot (loads, S rows), head (Q, softmax), channel group (P V)
   const int g = lane >> 4;      // 32-channel group (loads), key group of 4 (S, P)
   const int64_t qi = blockIdx.y;
@@ -148,9 +161,13 @@ __global__ __launch_bounds__(AT_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
   const int t_begin = split * a.tiles_per_split;
   int t_end = t_begin + a.tiles_per_split;
   t_end = t_end < n_tiles ? t_end : n_tiles;
+  // group kg takes tiles t_begin + kg + KG i; every group runs n_iter rounds
+  // (a round past t_end is all padding), so the block barriers line up
+  const int n_iter = (t_end - t_begin + KG - 1) / KG;
   const uint8_t* codes_seq = a.codes + seq * a.kv_rows * CODE_BYTES;
   const uint8_t* scales_seq = a.scales + seq * a.kv_rows * SCALE_BYTES;
   const uint8_t* win_seq = a.win + seq * a.win_cap * D;
+  auto tile = [&](int i) { return t_begin + kg + KG * i; };
 
   // Q: head j, channels 128 w + 32 g .. + 31 (issued first: nothing depends on it)
   float4 qraw[8];
@@ -161,11 +178,11 @@ __global__ __launch_bounds__(AT_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
   }
   int32_t id_ahead[AT_DEPTH];
 #pragma unroll
-  for (int i = 0; i < AT_DEPTH; ++i) id_ahead[i] = slot_id(a, qi, t_begin + AT_DEPTH + i, t_end, j);
+  for (int i = 0; i < AT_DEPTH; ++i) id_ahead[i] = slot_id(a, qi, tile(AT_DEPTH + i), t_end, j);
   RawKey ring[AT_DEPTH];
 #pragma unroll
   for (int i = 0; i < AT_DEPTH; ++i)
-    ring[i] = load_key(a, t_begin + i, t_end, j, g, w, slot_id(a, qi, t_begin + i, t_end, j), p,
+    ring[i] = load_key(a, tile(i), t_end, j, g, w, slot_id(a, qi, tile(i), t_end, j), p,
                        codes_seq, scales_seq, win_seq);
   f16x8 qf[4];
 #pragma unroll
@@ -179,17 +196,17 @@ __global__ __launch_bounds__(AT_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
   for (int n = 0; n < 8; ++n) acc_o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_huge_valf(), l_run = 0.f;
-  uint8_t* krow = lds.k[w];
+  uint8_t* krow = lds.loop.k[AT_WAVES * kg + w];
 
-  for (int t = t_begin; t < t_end; ++t) {
+  for (int it = 0; it < n_iter; ++it) {
     const RawKey cur = ring[0];
 #pragma unroll
     for (int i = 0; i + 1 < AT_DEPTH; ++i) ring[i] = ring[i + 1];
-    ring[AT_DEPTH - 1] = load_key(a, t + AT_DEPTH, t_end, j, g, w, id_ahead[0], p, codes_seq, scales_seq,
-                                  win_seq);
+    ring[AT_DEPTH - 1] = load_key(a, tile(it + AT_DEPTH), t_end, j, g, w, id_ahead[0], p, codes_seq,
+                                  scales_seq, win_seq);
 #pragma unroll
     for (int i = 0; i + 1 < AT_DEPTH; ++i) id_ahead[i] = id_ahead[i + 1];
-    id_ahead[AT_DEPTH - 1] = slot_id(a, qi, t + 2 * AT_DEPTH, t_end, j);
+    id_ahead[AT_DEPTH - 1] = slot_id(a, qi, tile(it + 2 * AT_DEPTH), t_end, j);
 
     // ---- 2. partial S^T over this wave's channels; slices to LDS row j ------
     __builtin_amdgcn_wave_barrier();   // the previous tile's LDS reads come first
@@ -200,13 +217,13 @@ __global__ __launch_bounds__(AT_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
       *reinterpret_cast<f16x8*>(krow + j * AT_KPITCH + 64 * g + 16 * s) = av;
       sacc = mfma_f16_16x16x32(av, qf[s], sacc);
     }
-    const int par = (t - t_begin) & 1;
-    lds.s[par][w][lane] = sacc;
+    const int par = it & 1;
+    lds.loop.s[par][kg][w][lane] = sacc;
     __syncthreads();
-    f32x4 S = lds.s[par][0][lane];
+    f32x4 S = lds.loop.s[par][kg][0][lane];
 #pragma unroll
     for (int v = 1; v < AT_WAVES; ++v) {
-      const f32x4 o = lds.s[par][v][lane];
+      const f32x4 o = lds.loop.s[par][kg][v][lane];
       S[0] += o[0]; S[1] += o[1]; S[2] += o[2]; S[3] += o[3];
     }
 
@@ -270,14 +287,76 @@ __global__ __launch_bounds__(AT_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
     }
   }
 
-  // ---- epilogue: lane holds O[head 4g + r][channel 128 w + 8 j + n] ----------
+  // ---- merge the key groups: O, max and sum per head over the groups --------
+  // lane holds O[head 4g + r][channel 128 w + 8 j + n]; m_run, l_run are head j's
+  float lsum[4];   // sum of head 4 g + r over the groups
+  if constexpr (KG > 1) {
+    __syncthreads();                                   // loop LDS is free
+    if (w == 0 && lane < 16) {
+      lds.red.ml[kg][0][j] = m_run;
+      lds.red.ml[kg][1][j] = l_run;
+    }
+    __syncthreads();
+    float mine[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * g + r;
+      float M = lds.red.ml[0][0][h];
+#pragma unroll
+      for (int v = 1; v < KG; ++v) M = fmaxf(M, lds.red.ml[v][0][h]);
+      float L = 0.f;
+#pragma unroll
+      for (int v = 0; v < KG; ++v) {
+        const float mv = lds.red.ml[v][0][h];
+        const float sv = (mv == -__builtin_huge_valf()) ? 0.f : exp2f(mv - M);
+        L = fmaf(sv, lds.red.ml[v][1][h], L);
+        if (v == kg) mine[r] = sv;
+      }
+      lsum[r] = L;
+    }
+    // head j's merged max and sum (what a partial carries)
+    {
+      float M = lds.red.ml[0][0][j];
+#pragma unroll
+      for (int v = 1; v < KG; ++v) M = fmaxf(M, lds.red.ml[v][0][j]);
+      float L = 0.f;
+#pragma unroll
+      for (int v = 0; v < KG; ++v) {
+        const float mv = lds.red.ml[v][0][j];
+        L = fmaf((mv == -__builtin_huge_valf()) ? 0.f : exp2f(mv - M), lds.red.ml[v][1][j], L);
+      }
+      m_run = M;
+      l_run = L;
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      acc_o[n][0] *= mine[0]; acc_o[n][1] *= mine[1];
+      acc_o[n][2] *= mine[2]; acc_o[n][3] *= mine[3];
+    }
+    if (kg > 0) {
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lds.red.o[kg - 1][w][4 * n + r][lane] = acc_o[n][r];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int v = 0; v < KG - 1; ++v)
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc_o[n][r] += lds.red.o[v][w][4 * n + r][lane];
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lsum[r] = __shfl(l_run, 4 * g + r);
+  }
+
+  // ---- epilogue (group 0) ---------------------------------------------------
   if (a.n_splits == 1) {
     float inv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float l = __shfl(l_run, 4 * g + r);
-      inv[r] = l > 0.f ? 1.0f / l : 0.f;
-    }
+    for (int r = 0; r < 4; ++r) inv[r] = lsum[r] > 0.f ? 1.0f / lsum[r] : 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float4* dst = reinterpret_cast<float4*>(a.out + (qi * HEADS + 4 * g + r) * D + AT_QCH * w + 8 * j);
@@ -341,27 +420,41 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
 }
 
 namespace {
-void attn_plan(int64_t Q, int32_t k, int* n_splits, int* tiles_per_split) {
-  int n_tiles = (k + NWIN + AT_TILE - 1) / AT_TILE;
-  // ~512 blocks: more splits buy little once every CU has work, while each
-  // split adds a 32 KiB partial output to write and combine
-  int64_t want = Q >= 512 ? 1 : (512 + Q - 1) / Q;
-  int max_split = (n_tiles + 1) / 2;                      // at least 2 tiles per split
+struct AttnPlan {
+  int kg, n_splits, tiles_per_split;
+};
+
+// Below 512 queries (decode batches) a query's slots go to 4 splits of two
+// key groups each: the first tile's dependent gather (slot id, then the
+// entry bytes) dominates a block's time, so each group takes several tiles,
+// and four partials per query keep the combine small.  From 512 queries on,
+// one group and one split per query (no partials).
+AttnPlan attn_plan(int64_t Q, int32_t k) {
+  const int n_tiles = (k + NWIN + AT_TILE - 1) / AT_TILE;
+  int kg = 1, want = 1;
+  if (Q < 512) {
+    kg = 2;
+    want = 4;
+  }
+  // at least KG tiles (one per group) per split
+  int max_split = n_tiles / kg;
+  max_split = max_split < 1 ? 1 : max_split;
   max_split = max_split < AT_MAX_SPLITS ? max_split : AT_MAX_SPLITS;
-  int s = (int)(want < max_split ? want : max_split);
+  int s = want < max_split ? want : max_split;
   s = s < 1 ? 1 : s;
-  int tps = (n_tiles + s - 1) / s;
-  *tiles_per_split = tps;
-  *n_splits = (n_tiles + tps - 1) / tps;
+  AttnPlan pl;
+  pl.kg = kg;
+  pl.tiles_per_split = (n_tiles + s - 1) / s;
+  pl.n_splits = (n_tiles + pl.tiles_per_split - 1) / pl.tiles_per_split;
+  return pl;
 }
 }  // namespace
 
 size_t attn_workspace_bytes(int64_t Q, int32_t k) {
-  int ns, tps;
-  attn_plan(Q, k, &ns, &tps);
-  if (ns <= 1) return 0;
-  size_t po = (size_t)Q * ns * HEADS * D * sizeof(float);
-  size_t pm = (size_t)Q * ns * 2 * HEADS * sizeof(float);
+  const AttnPlan pl = attn_plan(Q, k);
+  if (pl.n_splits <= 1) return 0;
+  size_t po = (size_t)Q * pl.n_splits * HEADS * D * sizeof(float);
+  size_t pm = (size_t)Q * pl.n_splits * 2 * HEADS * sizeof(float);
   return po + pm;
 }
 
@@ -377,13 +470,17 @@ hipError_t launch_sparse_attn(const float* q, const int32_t* q_pos, int64_t n_se
   a.idx = idx; a.k = k; a.win = win; a.win_cap = win_cap;
   a.c_log2 = sm_scale * 1.4426950408889634f;
   a.out = out;
-  attn_plan(Q, k, &a.n_splits, &a.tiles_per_split);
+  const AttnPlan pl = attn_plan(Q, k);
+  a.n_splits = pl.n_splits;
+  a.tiles_per_split = pl.tiles_per_split;
   a.part_o = nullptr; a.part_ml = nullptr;
   if (a.n_splits > 1) {
     a.part_o = reinterpret_cast<float*>(ws);
     a.part_ml = a.part_o + (size_t)Q * a.n_splits * HEADS * D;
   }
-  hipLaunchKernelGGL(attn_kernel, dim3(a.n_splits, (unsigned)Q), dim3(AT_THREADS), 0, st, a);
+  const dim3 grid(a.n_splits, (unsigned)Q);
+  if (pl.kg == 2) hipLaunchKernelGGL(attn_kernel<2>, grid, dim3(AT_THREADS * 2), 0, st, a);
+  else hipLaunchKernelGGL(attn_kernel<1>, grid, dim3(AT_THREADS), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(HEADS, (unsigned)Q), dim3(128), 0, st, a.part_o, a.part_ml,
