@@ -6,8 +6,10 @@ Default workload (the headline): decode, batch 32 x 1,048,576-token context
 Reindex layers.  A step is the whole hot path on one batch: window append,
 compression + MXFP4 store of the entry the newest tokens complete, Full-layer
 scoring / Top-512 / pool, three Reindex rescorings / Top-512, four sparse
-attentions.  Secondary lines: the 128K decode (Full + 5 Reuse) and the 256K
-prefill (Full, Reuse, Reuse, Reindex, Reuse) with its indexer TFLOPS.
+attentions.  Secondary lines: the 128K decode (Full + 5 Reuse), the 256K
+prefill (Full, Reuse, Reuse, Reindex, Reuse) with its indexer TFLOPS, and one
+decode token through the whole V4.1 CSA2 schedule (38 layers in four groups,
+each group with its own 1M-context global KV, every layer its own window).
 
 Inputs are synthetic and seeded (workloads module) and already resident in
 HBM when timing starts.  Each step is replayed from a captured HIP graph of
@@ -69,7 +71,8 @@ def algorithmic_bytes(cfg):
     b += len(cfg.layers) * (S * per_seq_attn + Q * 2 * 16 * 512 * 4)   # + queries and outputs
     new_tok = 1 if cfg.kind == "decode" else cfg.chunk
     b += S * cfg.new_entries * (4 * 512 * 4 + 288) + 4 * 512 * 512 * 4   # compress
-    b += S * new_tok * (512 * 4 + 512)                                  # window
+    n_win = len(cfg.layers) if cfg.window_per_layer else 1
+    b += n_win * S * new_tok * (512 * 4 + 512)                          # window append
     return b
 
 
@@ -232,6 +235,50 @@ def measure_config(cid, steps, warmup, use_graph, kernel_reps):
     return res
 
 
+def measure_schedule(name, steps, warmup, use_graph):
+    """One decode token through every group of a layer schedule."""
+    import torch
+    import workloads as W
+    from compressed_sparse_attention_04_amd.step import from_schedule
+    cfgs = W.v41_schedule(**W.SCHEDULES[name])
+    log(f"[bench] schedule {name}: building {len(cfgs)} groups")
+    wls = [W.make_workload(c, device="cuda") for c in cfgs]
+    sch = from_schedule(wls)
+    sch.setup()
+    torch.cuda.synchronize()
+    run = capture(sch, use_graph)
+    ms = time_step([run], steps, warmup)
+    log(f"[bench] schedule {name}: {ms:.3f} ms/step")
+    alg = sum(algorithmic_bytes(c) for c in cfgs)
+    res = {"ms_per_step": round(ms, 4), "tokens_per_s": round(cfgs[0].n_seq / (ms * 1e-3), 1),
+           "hbm_gbps": round(alg / (ms * 1e-3) / 1e9, 1), "layers": sum(len(c.layers) for c in cfgs),
+           "groups": ["".join(c.layers) for c in cfgs]}
+    del run, sch, wls
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def copy_peak_gbs(reps=10):
+    """Read + write bandwidth of a plain 1 GiB device copy (the practical HBM
+    ceiling beside the 8 TB/s peak)."""
+    import torch
+    src = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * src.numel() * 4 * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
 # ------------------------------------------------------------ CPU baseline ----
 
 def cpu_baseline(cid, n_sample):
@@ -312,6 +359,11 @@ def main():
                     "kernel": "score_query_kernel<false> (Full-layer dense indexer)",
                     "algorithmic_bytes_per_launch": main_res["indexer_bytes"],
                     "avg_launch_ms": round(main_res["indexer_ms"], 4)}
+        cp = copy_peak_gbs()
+        # a STREAM-style copy (read + write of 1 GiB): mixed traffic runs slower
+        # than this read-only scan, so the fraction can exceed 1
+        roofline["stream_copy_gbs"] = round(cp, 1)
+        roofline["frac_of_stream_copy"] = round(achieved / cp, 4)
         value, unit = main_res["tokens_per_s"], "tokens/s"
     else:
         key = "score_tile_" + cfg.name
@@ -352,6 +404,9 @@ def main():
             else:
                 e["indexer_gbps"] = round(r["indexer_gbps"], 1)
             sec[r["workload"]] = e
+        for name in W.SCHEDULES:
+            sec[name] = measure_schedule(name, max(3, args.steps // 2), max(1, args.warmup // 2),
+                                         not args.no_graph)
         out["secondary"] = sec
     if args.calib_copy:
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")

@@ -8,6 +8,9 @@ A step, in order (P3 §02 layer modes; P3 §03 window / MXFP4 store):
 ``setup()`` fills the state that exists before the step (prior entries when
 they are built from token latents, and the 127 window tokens before the
 step's first token); it is not part of the timed work.
+
+A schedule (``ScheduleStep``) runs several groups in order, each with its own
+global KV; a decode token passes through every group (P3 §01, §02).
 """
 
 import math
@@ -29,12 +32,15 @@ class LayerStep:
     x_tail: float32 [S, 127 + n_step, 512] -- the 127 tokens before the step
     and the step's n_step tokens.  The last 4 * new_entries rows of x_tail are
     compressed into entries prior_entries .. prior_entries + new_entries - 1.
+    x_win: optional float32 [L, S, 127 + n_step, 512] -- every layer's own
+    window latents (laid out like x_tail); without it the group's layers
+    share one window built from x_tail.
     """
 
     def __init__(self, *, kind, layers, build_pool, x_tail, w, rope_cs, codes, scales, k_fp8, q_pos,
                  q_attn, q_fp8, w_idx, prior_entries, new_entries, first_pos, x_prior=None,
                  rope_prior=None, top_k=ops.TOP_K, n_pool_blocks=ops.POOL_BLOCKS, rope_dim=64,
-                 eps=1e-6):
+                 eps=1e-6, x_win=None):
         dev = codes.device
         S, cap = codes.shape[0], codes.shape[1]
         self.kind, self.layers = kind, list(layers)
@@ -48,10 +54,18 @@ class LayerStep:
         self.codes, self.scales, self.k_fp8 = codes, scales, k_fp8
         self.rope_dim, self.eps = rope_dim, eps
         self.win_cap = N_WIN if kind == "decode" else self.n_step + N_WIN
-        self.win = torch.zeros((S, self.win_cap, D), dtype=torch.uint8, device=dev)
-        # position of x_tail row 0 of every sequence
-        self.pos_tail = first_pos.to(torch.int32).contiguous()
-        self.pos_step = (first_pos + (N_WIN - 1)).to(torch.int32).contiguous()
+        L = len(self.layers)
+        # windows: one per layer ([L * S] rings appended in one call), or one per group
+        self.x_win = x_win
+        self.n_win = L if x_win is not None else 1
+        if x_win is not None and tuple(x_win.shape) != (L, S, x_tail.shape[1], D):
+            raise ValueError("x_win must be [layers, sequences, 127 + n_step, 512]")
+        self.win_all = torch.zeros((self.n_win, S, self.win_cap, D), dtype=torch.uint8, device=dev)
+        self.wins = [self.win_all[li if x_win is not None else 0] for li in range(L)]
+        self.win = self.wins[0]
+        # position of x_tail row 0 of every sequence (repeated for every window)
+        self.pos_tail = first_pos.to(torch.int32).repeat(self.n_win).contiguous()
+        self.pos_step = (first_pos + (N_WIN - 1)).to(torch.int32).repeat(self.n_win).contiguous()
         self.n_entries = prior_entries + new_entries
         self.outs, self.idxs, self.calls = [], [], []
         self.pool = None
@@ -60,7 +74,7 @@ class LayerStep:
         idx_latest = None
         for li, mode in enumerate(self.layers):
             out = torch.empty((self.Q, HEADS, D), dtype=torch.float32, device=dev)
-            common = dict(codes=codes, scales=scales, k_fp8=k_fp8, win=self.win, q_pos=q_pos,
+            common = dict(codes=codes, scales=scales, k_fp8=k_fp8, win=self.wins[li], q_pos=q_pos,
                           q_attn=q_attn[li], out=out, n_seq=S, q_per_seq=self.q_per_seq,
                           n_entries=self.n_entries, top_k=top_k, n_pool_blocks=n_pool_blocks,
                           alloc_ws=False)
@@ -98,12 +112,18 @@ class LayerStep:
                                    x_seq_stride=self.x_prior.shape[1] * D, out_seq_stride=self.cap,
                                    rope_dim=self.rope_dim, eps=self.eps)
         tail = self.x_tail.shape[1]
-        ops.csa_window_append(self.x_tail, self.pos_tail, self.win, self.S, N_WIN - 1,
+        ops.csa_window_append(self._win_src(), self.pos_tail, self._win_rings(), self.n_win * self.S, N_WIN - 1,
                               x_seq_stride=tail * D)
+
+    def _win_src(self):
+        return self.x_tail if self.x_win is None else self.x_win
+
+    def _win_rings(self):
+        return self.win_all.view(self.n_win * self.S, self.win_cap, D)
 
     def step(self):
         tail = self.x_tail.shape[1]
-        ops.csa_window_append(self.x_tail, self.pos_step, self.win, self.S, self.n_step,
+        ops.csa_window_append(self._win_src(), self.pos_step, self._win_rings(), self.n_win * self.S, self.n_step,
                               x_seq_stride=tail * D, x_offset=(N_WIN - 1) * D)
         ops.csa_compress_quant(self.x_tail, self.w, self.rope_cs, self.codes, self.scales,
                                n_seq=self.S, n_per_seq=self.new, x_seq_stride=tail * D,
@@ -126,4 +146,33 @@ def from_workload(wl, device=None):
                      w=t["w"], rope_cs=t["rope_cs"], codes=t["codes"], scales=t["scales"],
                      k_fp8=t["k_fp8"], q_pos=t["q_pos"], q_attn=t["q_attn"], q_fp8=t["q_fp8"],
                      w_idx=t["w_idx"], prior_entries=cfg.prior_entries, new_entries=cfg.new_entries,
-                     first_pos=first, x_prior=t.get("x_prior"), rope_prior=t.get("rope_prior"))
+                     first_pos=first, x_prior=t.get("x_prior"), rope_prior=t.get("rope_prior"),
+                     x_win=t.get("x_win"))
+
+
+class ScheduleStep:
+    """Groups of layers run in order on one stream (P3 §02 schedule); every
+    group is a LayerStep with its own global KV.  One workspace serves all."""
+
+    def __init__(self, groups):
+        self.groups = list(groups)
+        big = max((c.ws_need for g in self.groups for c in g.calls), default=0)
+        dev = self.groups[0].codes.device
+        self.ws = torch.empty(big, dtype=torch.uint8, device=dev) if big else None
+        for g in self.groups:
+            g.ws = self.ws
+            for c in g.calls:
+                c.set_workspace(self.ws)
+
+    def setup(self):
+        for g in self.groups:
+            g.setup()
+
+    def step(self):
+        for g in self.groups:
+            g.step()
+
+
+def from_schedule(wls, device=None):
+    """ScheduleStep for a list of group workloads."""
+    return ScheduleStep([from_workload(wl, device) for wl in wls])

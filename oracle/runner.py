@@ -58,13 +58,15 @@ class OracleStep:
         self.cache(s)
         return self._e64[s]
 
-    def window(self, s, p):
-        """E4M3 bytes of the window tokens of a query at position p."""
+    def window(self, s, p, li=0):
+        """E4M3 bytes of the window tokens of a query at position p (layer li's
+        own window when every layer has one, else the group's)."""
         cfg = self.cfg
-        x_tail = self.cache(s)[3]
+        t = self.wl.tensors
+        x = _np(t["x_win"][li][s]) if "x_win" in t else self.cache(s)[3]
         first = (cfg.ctx_tokens - 128) if cfg.kind == "decode" else (cfg.ctx_tokens - 127)
         pos = window_positions(p)
-        return window_encode(x_tail[pos - first])
+        return window_encode(x[pos - first])
 
     def query(self, qi):
         """Per-layer oracle results for query qi: list of LayerState."""
@@ -72,10 +74,13 @@ class OracleStep:
         s = qi // cfg.chunk
         p = int(t["q_pos"][qi])
         codes, scales, k_fp8, _ = self.cache(s)
-        win = self.window(s, p)
+        per_layer = "x_win" in t
+        win = None if per_layer else self.window(s, p)
         n_entries = cfg.entries_total
         res, idx, pool = [], None, None
         for li, mode in enumerate(cfg.layers):
+            if per_layer:
+                win = self.window(s, p, li)
             qa = _np(t["q_attn"][li][qi])
             if mode == "F":
                 st = layer_full(codes, scales, k_fp8, _np(t["q_fp8"][li][qi]),

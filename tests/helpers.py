@@ -101,4 +101,44 @@ def cache_flips(gpu_codes, gpu_scales, ref_codes, ref_scales, ref_e64, rows, tol
     return flipped
 
 
-from oracle.runner import OracleStep  # noqa: E402,F401
+from oracle.runner import OracleStep  # noqa: E402
+
+
+def check_queries(wl, st, queries):
+    """Returns (near-tie swaps, compared outputs, outputs skipped for cache flips)."""
+    ref = OracleStep(wl)
+    cfg = wl.cfg
+    swaps, compared, flip_skips = 0, 0, 0
+    pool_gpu = np_(st.pool) if st.pool is not None else None
+    flips = {}
+    for qi in queries:
+        s = qi // cfg.chunk
+        if s not in flips:
+            rc, rs, _, _ = ref.cache(s)
+            computed = range(0 if not cfg.synthetic_cache else cfg.prior_entries, cfg.entries_total)
+            flips[s] = cache_flips(np_(st.codes[s]), np_(st.scales[s]), rc, rs, ref.e64(s), computed)
+        res = ref.query(qi)
+        same_set = True
+        for li, mode in enumerate(cfg.layers):
+            r = res[li]
+            gi = np_(st.idxs[li][qi])
+            if mode == "F":
+                n = check_topk_set(gi, r.scores, r.idx, 512)
+                if cfg.build_pool:
+                    assert np.array_equal(pool_gpu[qi], r.pool), f"pool differs at query {qi}"
+                same_set = n == 0
+            elif mode == "I":
+                nv = oracle.visible_entries(int(wl.tensors["q_pos"][qi]), cfg.entries_total)
+                ids = oracle.pooled_entries(r.pool, nv) if r.pool is not None else np.arange(nv)
+                n = check_topk_set(gi, r.scores, r.idx, 512, ids=ids)
+                same_set = n == 0
+            swaps += 0 if same_set else 1
+            if same_set:
+                assert np.array_equal(np.sort(gi), np.sort(r.idx))
+                if flips[s] & set(int(v) for v in gi if v >= 0):
+                    flip_skips += 1          # keys are not the same dequantized values
+                    continue
+                check_attn(np_(st.outs[li][qi]), r.out)
+                compared += 1
+    return swaps, compared, flip_skips
+

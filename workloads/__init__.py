@@ -48,6 +48,7 @@ class Config:
     build_pool: bool
     synthetic_cache: bool     # prior entries drawn as MXFP4 bytes
     extra: dict = field(default_factory=dict)
+    window_per_layer: bool = False   # every layer its own window (else one per group)
 
     @property
     def n_queries(self):
@@ -89,6 +90,35 @@ def small_config(kind="decode", n_seq=2, ctx_tokens=1024, chunk=1, layers=("F",)
     """A reduced workload of the same structure (tests)."""
     return Config(cid, f"small_{kind}", kind, n_seq, ctx_tokens, chunk, list(layers),
                   build_pool, synthetic_cache)
+
+
+# The V4.1 CSA2 layer schedule (P3 §02, layer modes): the 18 CSA2 encoder
+# layers form three groups of one Full layer and five Reuse layers; the 20
+# decoder layers are a Full layer and three Reuse layers, then four times a
+# Reindex layer and three Reuse layers, and the decoder's Full layer builds
+# the block pool its Reindex layers search.  Every group has its own global
+# KV (entries and indexer keys, from its Full layer); every layer has its own
+# 128-token window (P3 §03: the window state is per layer).
+V41_ENCODER_GROUP = ["F"] + ["U"] * 5
+V41_DECODER_GROUP = ["F", "U", "U", "U"] + ["I", "U", "U", "U"] * 4
+V41_GROUPS = [(V41_ENCODER_GROUP, False)] * 3 + [(V41_DECODER_GROUP, True)]
+
+
+def v41_schedule(kind="decode", n_seq=2, ctx_tokens=4096, chunk=1, synthetic_cache=False, cid=200,
+                 name="v41"):
+    """Workload configs of the four groups of the schedule (decode: a new token
+    passes through every layer)."""
+    return [Config(cid + 10 * g, f"{name}_g{g}", kind, n_seq, ctx_tokens, chunk, list(layers), pool,
+                   synthetic_cache, window_per_layer=True)
+            for g, (layers, pool) in enumerate(V41_GROUPS)]
+
+
+# The schedule at the 1M-context decode shape (batch 32): 38 layers, four
+# global KV caches of 262,144 entries per sequence.
+SCHEDULES = {
+    "decode_b32_1m_v41_38layers": dict(kind="decode", n_seq=32, ctx_tokens=1048576, synthetic_cache=True,
+                                       cid=300, name="decode_b32_1m_v41"),
+}
 
 
 # ------------------------------------------------------------ primitives ----
@@ -174,6 +204,8 @@ def make_workload(cfg, device="cpu"):
       q_pos      int32 [Q]
       q_fp8 / w_idx   per layer (None for Reuse): uint8 [Q, 8, 128] / fp32 [Q, 8]
       q_attn     per layer fp32 [Q, 16, 512] ~ N(0,1)
+      x_win      (window_per_layer only) fp32 [L, S, 127 + n_step, 512]: every
+                 layer's own window latents, laid out like x_tail
     """
     S, chunk = cfg.n_seq, cfg.chunk
     cap = cfg.entries_total
@@ -212,6 +244,8 @@ def make_workload(cfg, device="cpu"):
                            device=device)
         t["q_pos"] = pos.repeat(S)
     Q = cfg.n_queries
+    if cfg.window_per_layer:
+        t["x_win"] = normal((len(cfg.layers), S, tail, D), cid, 80, device)
     t["q_attn"] = [normal((Q, H, D), cid, 5 + li, device) for li in range(len(cfg.layers))]
     t["q_fp8"], t["w_idx"] = [], []
     for li, mode in enumerate(cfg.layers):
