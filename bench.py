@@ -259,6 +259,28 @@ def measure_schedule(name, steps, warmup, use_graph):
     return res
 
 
+def measure_window_rebuild(n_layers=38, n_seq=32, reps=20):
+    """Window rebuild after a prefix-cache hit: every layer's ring of every
+    sequence from its last 128 tokens (one launch).  HBM-bound: 128 x 512 x 4
+    bytes read + 128 x 512 bytes written per ring."""
+    import torch
+    from compressed_sparse_attention_04_amd import ops
+    n_ring = n_layers * n_seq
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    x = torch.randn((n_ring, 128, 512), generator=g, device="cuda")
+    p_last = torch.full((n_ring,), 1048575, dtype=torch.int32, device="cuda")
+    win = torch.empty((n_ring, 128, 512), dtype=torch.uint8, device="cuda")
+    fn = lambda: ops.csa_window_rebuild(x, p_last, win, n_ring, 128)   # noqa: E731
+    ms = time_kernel(fn, reps)
+    alg = n_ring * 128 * 512 * 5
+    gbs = alg / (ms * 1e-3) / 1e9
+    del x, win
+    torch.cuda.empty_cache()
+    return {"ms": round(ms, 4), "rings": n_ring, "algorithmic_bytes": alg, "gbps": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def copy_peak_gbs(reps=10):
     """Read + write bandwidth of a plain 1 GiB device copy (the practical HBM
     ceiling beside the 8 TB/s peak)."""
@@ -407,6 +429,7 @@ def main():
         for name in W.SCHEDULES:
             sec[name] = measure_schedule(name, max(3, args.steps // 2), max(1, args.warmup // 2),
                                          not args.no_graph)
+        sec["window_rebuild_b32_38layers"] = measure_window_rebuild()
         out["secondary"] = sec
     if args.calib_copy:
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")

@@ -43,6 +43,7 @@ SIGNATURES = {
     "csa_compress_quant": (c_i32, [c_void_p, c_i64, c_i64, c_i64, c_void_p, c_void_p, c_i32, c_f32,
                                    c_void_p, c_void_p, c_i64, c_void_p, c_void_p, c_size, c_void_p]),
     "csa_window_append": (c_i32, [c_void_p, c_i64, c_i64, c_i64, c_void_p, c_void_p, c_i64, c_void_p]),
+    "csa_window_rebuild": (c_i32, [c_void_p, c_i64, c_i64, c_i64, c_void_p, c_void_p, c_i64, c_void_p]),
     "csa_index_score": (c_i32, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_i64, c_i64,
                                 c_void_p, c_i32, c_void_p, c_void_p, c_void_p]),
     "csa_topk_workspace_size": (c_size, [c_i64, c_i64, c_i32]),

@@ -191,6 +191,22 @@ csa_status csa_window_append(const float* x, int64_t n_seq, int64_t n_tok, int64
   return hip_status(launch_window_append(x, n_seq, n_tok, x_seq_stride, pos0, win, win_cap, stream), fn);
 }
 
+csa_status csa_window_rebuild(const float* x, int64_t n_ring, int64_t n_tok, int64_t x_ring_stride,
+                              const int32_t* p_last, uint8_t* win, int64_t win_cap, hipStream_t stream) {
+  const char* fn = "csa_window_rebuild";
+  CHECK(n_ring >= 0, CSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (n_ring == 0) return CSA_OK;
+  CHECK_PTR(x); CHECK_PTR(p_last); CHECK_PTR(win);
+  CHECK(win_cap >= NWIN && win_cap < ((int64_t)1 << 24), CSA_ERR_UNSUPPORTED, "%s: win_cap must be in [128, 2^24)",
+        fn);
+  CHECK(n_tok >= 1 && n_tok <= win_cap, CSA_ERR_INVALID_ARG, "%s: need 1 <= n_tok <= win_cap", fn);
+  CHECK(x_ring_stride % 4 == 0, CSA_ERR_ALIGNMENT, "%s: x_ring_stride must be a multiple of 4", fn);
+  CHECK(n_ring == 1 || x_ring_stride >= n_tok * D, CSA_ERR_INVALID_ARG, "%s: x_ring_stride too small", fn);
+  CHECK(n_ring * win_cap < ((int64_t)1 << 26), CSA_ERR_UNSUPPORTED, "%s: too many ring rows", fn);
+  CHECK_ALIGN(x, 16); CHECK_ALIGN(p_last, 4); CHECK_ALIGN(win, 16);
+  return hip_status(launch_window_rebuild(x, n_ring, n_tok, x_ring_stride, p_last, win, win_cap, stream), fn);
+}
+
 // ------------------------------------------------------------------ a3 ----
 static csa_status check_score(const char* fn, const ScoreArgs& s) {
   CHECK(s.n_seq >= 0 && s.q_per_seq >= 0, CSA_ERR_INVALID_ARG, "%s: negative size", fn);

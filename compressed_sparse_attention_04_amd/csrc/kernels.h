@@ -13,6 +13,8 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_
                              hipStream_t st);
 hipError_t launch_window_append(const float* x, int64_t n_seq, int64_t n_tok, int64_t x_seq_stride,
                                 const int32_t* pos0, uint8_t* win, int64_t win_cap, hipStream_t st);
+hipError_t launch_window_rebuild(const float* x, int64_t n_ring, int64_t n_tok, int64_t x_ring_stride,
+                                 const int32_t* p_last, uint8_t* win, int64_t win_cap, hipStream_t st);
 size_t compress_workspace_bytes(int64_t n);
 hipError_t launch_compress_quant(const float* x, int64_t n_seq, int64_t n_per_seq,
                                  int64_t x_seq_stride, const float* w, const float* rope_cs,

@@ -95,6 +95,39 @@ __global__ __launch_bounds__(256) void window_append_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------
+// Window rebuild from the latest tokens: 32 lanes per ring row, 16 channels
+// per lane.  Row j of ring r holds the token at the latest position t <= p
+// with t = j (mod win_cap) when that token is one of the n_tok given
+// (t >= p - n_tok + 1, t >= 0), else zeros.
+__global__ __launch_bounds__(256) void window_rebuild_kernel(const float* __restrict__ x,
+                                                             int64_t n_ring, int64_t n_tok,
+                                                             int64_t x_ring_stride,
+                                                             const int32_t* __restrict__ p_last,
+                                                             uint8_t* __restrict__ win,
+                                                             int64_t win_cap) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = t >> 5;
+  const int lane = (int)(t & 31);
+  if (row >= n_ring * win_cap) return;
+  const int64_t r = row / win_cap, j = row % win_cap;
+  const int64_t p = p_last[r];
+  const int64_t pos = p - (((p - j) % win_cap) + win_cap) % win_cap;   // latest position <= p in row j
+  const int64_t i = pos - (p - n_tok + 1);                                // its index among the tokens
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (pos >= 0 && i >= 0) {
+    const float4* src = reinterpret_cast<const float4*>(x + r * x_ring_stride + i * D + 16 * lane);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 f = src[k];
+      w[k] = e4m3_encode(f.x) | (e4m3_encode(f.y) << 8) | (e4m3_encode(f.z) << 16) |
+             (e4m3_encode(f.w) << 24);
+    }
+  }
+  uint8_t* dst = win + row * D + 16 * lane;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// ---------------------------------------------------------------------------
 // Compression GEMM on the fp64 matrix cores: Y[i, o] = sum_k Xc[i, k] Wc[o, k]
 // with Xc[i] = the 4 token rows of entry i (2048 contiguous floats) and
 // Wc[o, i*512 + c] = W_i[o, c].  Every fp32 x fp32 product is exact in fp64,
@@ -261,6 +294,16 @@ hipError_t launch_window_append(const float* x, int64_t n_seq, int64_t n_tok, in
   int64_t blocks = (tokens * 32 + 255) / 256;
   hipLaunchKernelGGL(window_append_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, n_seq, n_tok,
                      x_seq_stride, pos0, win, win_cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_rebuild(const float* x, int64_t n_ring, int64_t n_tok, int64_t x_ring_stride,
+                                 const int32_t* p_last, uint8_t* win, int64_t win_cap, hipStream_t st) {
+  const int64_t rows = n_ring * win_cap;
+  if (rows == 0) return hipSuccess;
+  const int64_t blocks = (rows * 32 + 255) / 256;
+  hipLaunchKernelGGL(window_rebuild_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, n_ring, n_tok,
+                     x_ring_stride, p_last, win, win_cap);
   return hipGetLastError();
 }
 

@@ -164,6 +164,23 @@ def csa_window_append(x, pos0, win, n_seq, n_tok, x_seq_stride=None, x_offset=0,
           _stream(stream))
 
 
+def csa_window_rebuild(x, p_last, win, n_ring, n_tok, x_ring_stride=None, x_offset=0, stream=None):
+    """Rebuild n_ring E4M3 window rings win [n_ring, cap, 512] from their last
+    n_tok float32 tokens (token i of ring r at element x_offset + r *
+    x_ring_stride + i * 512, the last one at position p_last[r])."""
+    _need(x, "x", torch.float32)
+    dev = x.device
+    _need(p_last, "p_last", torch.int32, dev, shape=(n_ring,))
+    _need(win, "win", torch.uint8, dev)
+    if win.dim() != 3 or win.shape[0] != n_ring or win.shape[2] != D:
+        raise ValueError("win must be [n_ring, win_cap, 512]")
+    xs = x_ring_stride if x_ring_stride is not None else n_tok * D
+    if n_ring and (x_offset < 0 or x_offset + (n_ring - 1) * xs + n_tok * D > x.numel()):
+        raise ValueError("x is too small")
+    _call("csa_window_rebuild", _ptr_off(x, x_offset), n_ring, n_tok, xs, _p(p_last), _p(win), win.shape[1],
+          _stream(stream))
+
+
 # ------------------------------------------------------------------ a3 ----
 
 def csa_index_score(q_fp8, w, q_pos, k_fp8, n_seq, q_per_seq, n_entries, pool_blocks=None,

@@ -130,6 +130,33 @@ csa_status csa_window_append(const float* x, int64_t n_seq, int64_t n_tok, int64
                              const int32_t* pos0, uint8_t* win, int64_t win_cap,
                              hipStream_t stream);
 
+/* ---------------------------------------------------------------- f2 ----
+ * csa_window_rebuild: rebuild n_ring window rings from their latest tokens
+ * (P3 §03, SWA Bounded Replay: the window state is not kept in the
+ * persistent cache; after a prefix-cache hit only the last n_win = 128
+ * tokens are replayed).  One ring per (layer, sequence).
+ *   x        float32: token i (0 <= i < n_tok) of ring r at
+ *            x + r * x_ring_stride + i * 512; the last token (i = n_tok - 1)
+ *            sits at position p_last[r] (>= 0), token i at
+ *            p_last[r] - (n_tok - 1 - i)
+ *   p_last   int32 [n_ring] (device)
+ *   win      uint8 [n_ring, win_cap, 512] out (device), win_cap >= 128: row j
+ *            of ring r gets RNE_E4M3FN (saturating, as csa_window_append) of
+ *            the token at the latest position t <= p_last[r] with
+ *            t = j (mod win_cap), when that token is among the n_tok given
+ *            and t >= 0; every other row is zeroed.  With
+ *            n_tok = min(128, p_last + 1) and win_cap = 128 the ring is
+ *            byte-identical to appending every token of the history to a
+ *            zeroed ring; with a larger win_cap the rows of the last 128
+ *            positions are.
+ *   1 <= n_tok <= win_cap; x_ring_stride a multiple of 4 and >= n_tok * 512
+ *   when n_ring > 1; x, win 16-byte aligned.  The whole ring is written
+ *   (no earlier contents are kept).
+ */
+csa_status csa_window_rebuild(const float* x, int64_t n_ring, int64_t n_tok, int64_t x_ring_stride,
+                              const int32_t* p_last, uint8_t* win, int64_t win_cap,
+                              hipStream_t stream);
+
 /* ---------------------------------------------------------------- a3 ----
  * csa_index_score: indexer scores of Q = n_seq * q_per_seq queries (P3 §02:
  * Full layers score every causally visible position; Reindex layers rescore

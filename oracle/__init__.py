@@ -45,7 +45,7 @@ from .compressor import compress, rope_rotate, compress_rope_fp32
 from .indexer import visible_entries, index_scores, pooled_entries
 from .select import topk, block_pool
 from .attention import window_positions, sparse_attention
-from .layer import LayerState, layer_full, layer_reindex, layer_reuse, window_encode
+from .layer import LayerState, layer_full, layer_reindex, layer_reuse, window_encode, window_rebuild
 
 __all__ = [
     "E2M1_VALUES", "e4m3_decode", "e4m3_encode", "e2m1_decode", "e2m1_encode",
@@ -54,5 +54,5 @@ __all__ = [
     "visible_entries", "index_scores", "pooled_entries",
     "topk", "block_pool",
     "window_positions", "sparse_attention",
-    "LayerState", "layer_full", "layer_reindex", "layer_reuse", "window_encode",
+    "LayerState", "layer_full", "layer_reindex", "layer_reuse", "window_encode", "window_rebuild",
 ]

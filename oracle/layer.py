@@ -43,6 +43,23 @@ def window_encode(x_tokens):
     return e4m3_encode(np.asarray(x_tokens, dtype=np.float32))
 
 
+def window_rebuild(x_last, p_last, win_cap):
+    """SWA Bounded Replay (P3 §03): the window ring rebuilt from the latest
+    tokens only.  x_last float32 [n_tok, 512] are the tokens at positions
+    p_last - n_tok + 1 .. p_last (n_tok <= win_cap); the token at position t
+    goes to row t % win_cap, rows no given token reaches stay zero.  Returns
+    uint8 [win_cap, 512]."""
+    x_last = np.asarray(x_last, dtype=np.float32)
+    n_tok = x_last.shape[0]
+    assert 1 <= n_tok <= win_cap
+    ring = np.zeros((win_cap, x_last.shape[1]), dtype=np.uint8)
+    for i in range(n_tok):
+        t = p_last - (n_tok - 1 - i)
+        if t >= 0:
+            ring[t % win_cap] = window_encode(x_last[i])
+    return ring
+
+
 def layer_full(codes, scales, k_fp8, q_fp8, w, q_attn, q_pos, win_fp8, sm_scale,
                build_pool=False, k=TOP_K, n_blocks=POOL_BLOCKS, n_entries=None):
     """Full mode for one query: score all visible entries, Top-K, attention."""

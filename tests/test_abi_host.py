@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
@@ -148,3 +148,18 @@ def test_valid_layer_args_pass_validation(lib):
         assert fn(ctypes.byref(a), None) == 5, lib.csa_last_error()
     a.ws_bytes = need[0] - 1
     assert lib.csa_layer_full(ctypes.byref(a), None) == WORKSPACE
+
+
+def test_window_rebuild_validation(lib):
+    """csa_window_rebuild rejects bad sizes, capacities and alignment before
+    anything is launched."""
+    f = lib.csa_window_rebuild
+    P = 1 << 20
+    # (n_ring, n_tok, x_ring_stride, x, p_last, win, win_cap)
+    assert f(P, 2, 0, 128 * 512, P, P, 128, None) == INVALID           # n_tok < 1
+    assert f(P, 2, 129, 129 * 512, P, P, 128, None) == INVALID         # n_tok > win_cap
+    assert f(P, 2, 128, 128 * 512, P, P, 64, None) == UNSUPPORTED      # win_cap < 128
+    assert f(P, 2, 128, 100 * 512, P, P, 128, None) == INVALID         # overlapping rings
+    assert f(P + 4, 2, 128, 128 * 512, P, P, 128, None) == ALIGN       # x not 16-byte aligned
+    assert f(None, 2, 128, 128 * 512, P, P, 128, None) != 0            # null pointer
+    assert f(P, 0, 128, 128 * 512, P, P, 128, None) == 0               # nothing to do

@@ -297,3 +297,40 @@ def test_sparse_attn_dense_case_and_empty_selection():
     torch.cuda.synchronize()
     check_attn(np_(out), _attn_ref(codes, scales, win, q, idx, pos, 1, 128))
     check_attn(np_(out2), _attn_ref(codes, scales, win, q, none, pos, 1, 128))
+
+
+# ------------------------------------------------------------------ f2 ----
+
+@pytest.mark.parametrize("cap,n_tok_rule", [(128, "full"), (192, "full"), (128, "short")])
+def test_window_rebuild_bit_exact(cap, n_tok_rule):
+    """csa_window_rebuild vs the oracle's rebuild for rings at positions that
+    cover an empty history, a partial window, the wrap and large positions."""
+    ps = [0, 3, 126, 127, 128, 129, 1000, 4095, 262143, (1 << 22) + 5]
+    n_tok = 128 if n_tok_rule == "full" else 50
+    rng = np.random.default_rng(cap + n_tok)
+    x = (rng.standard_normal((len(ps), n_tok, 512)) * 40).astype(np.float32)
+    x[0, -1, :8] = [0.0, -0.0, 1e-9, 500.0, -500.0, 448.0, 464.0, 2.0 ** -9]
+    win = torch.full((len(ps), cap, 512), 0xAB, dtype=torch.uint8, device=DEV)
+    ops.csa_window_rebuild(torch.from_numpy(x).to(DEV), torch.tensor(ps, dtype=torch.int32, device=DEV), win,
+                           len(ps), n_tok)
+    got = np_(win)
+    for r, p in enumerate(ps):
+        n = min(n_tok, p + 1)
+        ref = oracle.window_rebuild(x[r, n_tok - n:], p, cap)
+        assert np.array_equal(got[r], ref), (r, p)
+
+
+def test_window_rebuild_then_append_matches_rebuild_later():
+    """Rebuild at position p, append token p+1 with csa_window_append: the ring
+    equals the rebuild at p+1 (decode continues from a rebuilt window)."""
+    rng = np.random.default_rng(5)
+    n_ring, p = 6, 10_000
+    x = torch.from_numpy(rng.standard_normal((n_ring, 129, 512)).astype(np.float32)).to(DEV)
+    pl = torch.full((n_ring,), p, dtype=torch.int32, device=DEV)
+    a = torch.empty((n_ring, 128, 512), dtype=torch.uint8, device=DEV)
+    b = torch.empty_like(a)
+    ops.csa_window_rebuild(x, pl, a, n_ring, 128, x_ring_stride=129 * 512)
+    ops.csa_window_append(x, pl + 1, a, n_ring, 1, x_seq_stride=129 * 512, x_offset=128 * 512)
+    ops.csa_window_rebuild(x, pl + 1, b, n_ring, 128, x_ring_stride=129 * 512, x_offset=512)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
