@@ -281,6 +281,41 @@ def measure_window_rebuild(n_layers=38, n_seq=32, reps=20):
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def measure_kv_io(n_seq=4, entries=262144):
+    """Global-KV file round trip: save then load n_seq sequences of a
+    1M-context cache (416 B per entry) through a 64 MiB pinned stage, in the
+    temporary directory.  Wall-clock GB/s; bounded by the file system."""
+    import tempfile
+    import torch
+    from compressed_sparse_attention_04_amd import ops
+    codes = torch.randint(0, 256, (n_seq, entries, 256), dtype=torch.uint8, device="cuda")
+    scales = torch.randint(0, 256, (n_seq, entries, 32), dtype=torch.uint8, device="cuda")
+    keys = torch.randint(0, 256, (n_seq, entries, 128), dtype=torch.uint8, device="cuda")
+    stage = ops.kv_stage()
+    nbytes = n_seq * entries * 416
+    fd, path = tempfile.mkstemp(suffix=".csakv")
+    os.close(fd)
+    try:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ops.csa_kv_save(path, codes, scales, keys, entries, stage=stage)
+        t1 = time.perf_counter()
+        c2, s2, k2 = torch.empty_like(codes), torch.empty_like(scales), torch.empty_like(keys)
+        t2 = time.perf_counter()
+        n = ops.csa_kv_load(path, c2, s2, k2, stage=stage)
+        t3 = time.perf_counter()
+        same = n == entries and torch.equal(c2, codes) and torch.equal(s2, scales) and torch.equal(k2, keys)
+        return {"bytes": nbytes, "save_gbps": round(nbytes / (t1 - t0) / 1e9, 2),
+                "load_gbps": round(nbytes / (t3 - t2) / 1e9, 2), "round_trip_exact": bool(same)}
+    except Exception as e:   # a full or read-only temporary directory: report, do not fail the bench
+        return {"error": str(e)[:200]}
+    finally:
+        if os.path.exists(path):
+            os.remove(path)
+        del codes, scales, keys
+        torch.cuda.empty_cache()
+
+
 def copy_peak_gbs(reps=10):
     """Read + write bandwidth of a plain 1 GiB device copy (the practical HBM
     ceiling beside the 8 TB/s peak)."""
@@ -430,6 +465,7 @@ def main():
             sec[name] = measure_schedule(name, max(3, args.steps // 2), max(1, args.warmup // 2),
                                          not args.no_graph)
         sec["window_rebuild_b32_38layers"] = measure_window_rebuild()
+        sec["kv_file_round_trip_1m_4seq"] = measure_kv_io()
         out["secondary"] = sec
     if args.calib_copy:
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")

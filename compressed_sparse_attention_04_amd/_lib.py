@@ -44,6 +44,11 @@ SIGNATURES = {
                                    c_void_p, c_void_p, c_i64, c_void_p, c_void_p, c_size, c_void_p]),
     "csa_window_append": (c_i32, [c_void_p, c_i64, c_i64, c_i64, c_void_p, c_void_p, c_i64, c_void_p]),
     "csa_window_rebuild": (c_i32, [c_void_p, c_i64, c_i64, c_i64, c_void_p, c_void_p, c_i64, c_void_p]),
+    "csa_kv_save": (c_i32, [ctypes.c_char_p, c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_i64, c_void_p, c_size,
+                            c_void_p]),
+    "csa_kv_load": (c_i32, [ctypes.c_char_p, c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_void_p, c_size,
+                            c_void_p]),
+    "csa_kv_file_info": (c_i32, [ctypes.c_char_p, c_void_p, c_void_p]),
     "csa_index_score": (c_i32, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_i64, c_i64,
                                 c_void_p, c_i32, c_void_p, c_void_p, c_void_p]),
     "csa_topk_workspace_size": (c_size, [c_i64, c_i64, c_i32]),

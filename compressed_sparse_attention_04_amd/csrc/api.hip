@@ -1,6 +1,7 @@
 // C-ABI entry points of libcsa: host-side validation, workspace layout and
-// launch sequencing.  No entry point allocates, frees or synchronizes; every
-// check runs before the first launch, so an error enqueues nothing.
+// launch sequencing.  No entry point here allocates, frees or synchronizes;
+// every check runs before the first launch, so an error enqueues nothing.
+// (The global-KV file pair in kvio.hip blocks on its copies and file I/O.)
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -9,14 +10,14 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "status.h"
 
-using namespace csa;
+namespace csa {
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
-csa_status fail(csa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 csa_status fail(csa_status s, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -31,6 +32,14 @@ csa_status hip_status(hipError_t e, const char* where) {
   if (e == hipSuccess) return CSA_OK;
   return fail(CSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
+
+const char* last_error() { return g_last_error.c_str(); }
+
+}  // namespace csa
+
+using namespace csa;
+
+namespace {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -115,11 +124,12 @@ const char* csa_status_string(csa_status s) {
     case CSA_ERR_ALIGNMENT: return "misaligned pointer";
     case CSA_ERR_WORKSPACE: return "workspace too small";
     case CSA_ERR_HIP: return "HIP error";
+    case CSA_ERR_IO: return "file error";
     default: return "unknown status";
   }
 }
 
-const char* csa_last_error(void) { return g_last_error.c_str(); }
+const char* csa_last_error(void) { return csa::last_error(); }
 
 int32_t csa_version(void) { return 100; }
 

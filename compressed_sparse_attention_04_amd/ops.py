@@ -7,6 +7,7 @@ the current HIP stream.  All computation happens in the library's kernels.
 """
 
 import ctypes
+import os
 import math
 
 import torch
@@ -179,6 +180,51 @@ def csa_window_rebuild(x, p_last, win, n_ring, n_tok, x_ring_stride=None, x_offs
         raise ValueError("x is too small")
     _call("csa_window_rebuild", _ptr_off(x, x_offset), n_ring, n_tok, xs, _p(p_last), _p(win), win.shape[1],
           _stream(stream))
+
+
+# ------------------------------------------------------------------ f4 ----
+
+KV_STAGE_BYTES = 64 << 20
+
+
+def kv_stage(nbytes=KV_STAGE_BYTES):
+    """A pinned host staging buffer for csa_kv_save / csa_kv_load."""
+    return torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+
+
+def _kv_bufs(codes, scales, k_fp8):
+    _need(codes, "codes", torch.uint8)
+    dev = codes.device
+    S, rows = codes.shape[0], codes.shape[1]
+    _need(codes, "codes", torch.uint8, dev, shape=(S, rows, D // 2))
+    _need(scales, "scales", torch.uint8, dev, shape=(S, rows, D // 16))
+    _need(k_fp8, "k_fp8", torch.uint8, dev, shape=(S, rows, IDX_DIM))
+    return S, rows
+
+
+def csa_kv_save(path, codes, scales, k_fp8, n_entries, stage=None, stream=None):
+    """Write the first n_entries rows of every sequence's global KV to path."""
+    S, rows = _kv_bufs(codes, scales, k_fp8)
+    stage = kv_stage() if stage is None else stage
+    _call("csa_kv_save", os.fsencode(path), _p(codes), _p(scales), _p(k_fp8), S, rows, n_entries,
+          ctypes.c_void_p(stage.data_ptr()), stage.numel(), _stream(stream))
+
+
+def csa_kv_load(path, codes, scales, k_fp8, stage=None, stream=None):
+    """Read a global-KV file into the buffers; returns its n_entries."""
+    S, rows = _kv_bufs(codes, scales, k_fp8)
+    stage = kv_stage() if stage is None else stage
+    n = ctypes.c_int64(0)
+    _call("csa_kv_load", os.fsencode(path), _p(codes), _p(scales), _p(k_fp8), S, rows, ctypes.byref(n),
+          ctypes.c_void_p(stage.data_ptr()), stage.numel(), _stream(stream))
+    return n.value
+
+
+def csa_kv_file_info(path):
+    """(n_seq, n_entries) of a global-KV file (header and size checked)."""
+    a, b = ctypes.c_int64(0), ctypes.c_int64(0)
+    _call("csa_kv_file_info", os.fsencode(path), ctypes.byref(a), ctypes.byref(b))
+    return a.value, b.value
 
 
 # ------------------------------------------------------------------ a3 ----

@@ -64,7 +64,9 @@ enum {
   CSA_ERR_UNSUPPORTED = 2, /* size outside what the kernels are built for */
   CSA_ERR_ALIGNMENT = 3,   /* pointer or row not aligned as required */
   CSA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
-  CSA_ERR_HIP = 5          /* a HIP launch failed; csa_last_error has the text */
+  CSA_ERR_HIP = 5,         /* a HIP launch failed; csa_last_error has the text */
+  CSA_ERR_IO = 6           /* file open / read / write failed, or a file's header,
+                              size or checksum is not what it must be */
 };
 
 /* Static text of a status code. */
@@ -156,6 +158,45 @@ csa_status csa_window_append(const float* x, int64_t n_seq, int64_t n_tok, int64
 csa_status csa_window_rebuild(const float* x, int64_t n_ring, int64_t n_tok, int64_t x_ring_stride,
                               const int32_t* p_last, uint8_t* win, int64_t win_cap,
                               hipStream_t stream);
+
+/* ---------------------------------------------------------------- f4 ----
+ * Global-KV files (P3 §03: the global KV -- MXFP4 entries and indexer keys --
+ * is what the persistent cache keeps; the window is rebuilt by replay).  One
+ * file holds n_seq sequences' first n_entries rows of codes [.., 256], scales
+ * [.., 32] and k_fp8 [.., 128], in device buffers laid out [n_seq, seq_rows,
+ * row bytes].  Layout: a 64-byte header -- magic "CSA2GKV1", u32 version 1,
+ * u32 header bytes 64, i64 n_seq, i64 n_entries, u32 row bytes 256 / 32 / 128,
+ * u32 flags 0, u64 checksum, u64 reserved 0, little-endian -- then, for each
+ * sequence, its code rows, scale rows and key rows.  The checksum is FNV-1a
+ * over the payload read as little-endian 64-bit words (offset basis
+ * 0xcbf29ce484222325, prime 0x100000001b3, one xor and one multiply per word).
+ *
+ * Unlike every other entry point, save and load block the calling thread
+ * until the copies (on `stream`, after the work already queued there) and the
+ * file I/O are done.  They copy through `stage`, a caller-provided host
+ * buffer of stage_bytes >= 8 KiB, 16-byte aligned (pinned memory lets the
+ * copies overlap the file I/O); the library allocates nothing.
+ *
+ * csa_kv_save: writes (or truncates and rewrites) `path`.  0 <= n_entries <=
+ *   seq_rows.  CSA_ERR_IO if the file cannot be created or written.
+ * csa_kv_load: reads a file written by csa_kv_save into the buffers; the file
+ *   must hold n_seq sequences and at most seq_rows entries each
+ *   (CSA_ERR_INVALID_ARG otherwise, nothing copied); *n_entries_out = the
+ *   file's n_entries; rows past it are left as they are.  CSA_ERR_IO for a
+ *   bad header, a size that does not match it, a read error, or a checksum
+ *   mismatch -- in the last case the buffers already hold the file's
+ *   (damaged) rows.
+ * csa_kv_file_info: host only; checks the header and the file size and
+ *   returns the file's n_seq and n_entries (CSA_ERR_IO as above, checksum
+ *   not verified).
+ */
+csa_status csa_kv_save(const char* path, const uint8_t* codes, const uint8_t* scales, const uint8_t* k_fp8,
+                       int64_t n_seq, int64_t seq_rows, int64_t n_entries, void* stage, size_t stage_bytes,
+                       hipStream_t stream);
+csa_status csa_kv_load(const char* path, uint8_t* codes, uint8_t* scales, uint8_t* k_fp8, int64_t n_seq,
+                       int64_t seq_rows, int64_t* n_entries_out, void* stage, size_t stage_bytes,
+                       hipStream_t stream);
+csa_status csa_kv_file_info(const char* path, int64_t* n_seq, int64_t* n_entries);
 
 /* ---------------------------------------------------------------- a3 ----
  * csa_index_score: indexer scores of Q = n_seq * q_per_seq queries (P3 §02:

@@ -1,0 +1,100 @@
+"""GPU round trip of the global-KV files (P3 §03: the global KV is what the
+persistent cache keeps, the window is rebuilt by replay): the bytes written
+are the device rows with the documented header and checksum, loading restores
+them bit-exactly, a damaged file is reported, and decoding resumed from a
+loaded cache plus a rebuilt window reproduces the original step's indices and
+outputs bit for bit."""
+
+import os
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from compressed_sparse_attention_04_amd import ops
+from compressed_sparse_attention_04_amd.ops import CsaError
+from compressed_sparse_attention_04_amd.step import from_workload
+from helpers import np_
+from test_kvio_host import fnv_words
+
+pytestmark = pytest.mark.gpu
+
+
+def run_step(cfg):
+    wl = W.make_workload(cfg, device="cuda")
+    st = from_workload(wl)
+    st.setup()
+    st.step()
+    torch.cuda.synchronize()
+    return wl, st
+
+
+CFG = W.small_config("decode", n_seq=3, ctx_tokens=4 * 20004, layers=("F", "I", "U"), build_pool=True,
+                     synthetic_cache=True, cid=401)
+
+
+def test_save_file_layout_and_checksum(tmp_path):
+    wl, st = run_step(CFG)
+    n = st.n_entries
+    path = tmp_path / "kv.bin"
+    ops.csa_kv_save(path, st.codes, st.scales, st.k_fp8, n, stage=ops.kv_stage(1 << 20))   # many chunks
+    data = path.read_bytes()
+    hdr = struct.unpack("<8sIIqqIIIIQQ", data[:64])
+    assert hdr[:9] == (b"CSA2GKV1", 1, 64, 3, n, 256, 32, 128, 0) and hdr[10] == 0
+    payload = data[64:]
+    assert len(payload) == 3 * n * (256 + 32 + 128)
+    assert hdr[9] == fnv_words(payload)
+    off = 0
+    for s in range(3):
+        for arr, w in ((st.codes, 256), (st.scales, 32), (st.k_fp8, 128)):
+            assert payload[off:off + n * w] == np_(arr[s, :n]).tobytes()
+            off += n * w
+    assert ops.csa_kv_file_info(path) == (3, n)
+
+
+def test_load_restores_and_resume_is_bit_identical(tmp_path):
+    wl, st = run_step(CFG)
+    n = st.n_entries
+    path = tmp_path / "kv.bin"
+    ops.csa_kv_save(path, st.codes, st.scales, st.k_fp8, n)
+    # restore into buffers with room to spare; rows past n stay untouched
+    rows = st.cap + 5
+    codes = torch.full((3, rows, 256), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((3, rows, 32), 0xAB, dtype=torch.uint8, device="cuda")
+    keys = torch.full((3, rows, 128), 0xAB, dtype=torch.uint8, device="cuda")
+    assert ops.csa_kv_load(path, codes, scales, keys, stage=ops.kv_stage(3 << 20)) == n
+    assert torch.equal(codes[:, :n], st.codes[:, :n]) and torch.equal(scales[:, :n], st.scales[:, :n])
+    assert torch.equal(keys[:, :n], st.k_fp8[:, :n])
+    assert bool((codes[:, n:] == 0xAB).all()) and bool((keys[:, n:] == 0xAB).all())
+    # resume: the loaded global KV plus the window rebuilt from the last 128 tokens
+    t2 = dict(wl.tensors)
+    t2["codes"], t2["scales"], t2["k_fp8"] = (codes[:, :st.cap].contiguous(), scales[:, :st.cap].contiguous(),
+                                              keys[:, :st.cap].contiguous())
+    st2 = from_workload(W.Workload(wl.cfg, t2))
+    p_last = wl.tensors["q_pos"].clone()
+    ops.csa_window_rebuild(wl.tensors["x_tail"], p_last, st2.win_all.view(3, 128, 512), 3, 128,
+                           x_ring_stride=wl.tensors["x_tail"].shape[1] * 512)
+    assert torch.equal(st2.win_all[0], st.win_all[0])
+    for call in st2.calls:
+        call()
+    torch.cuda.synchronize()
+    for li in range(len(CFG.layers)):
+        assert torch.equal(st2.idxs[li], st.idxs[li]), li
+        assert torch.equal(st2.outs[li], st.outs[li]), li
+    assert torch.equal(st2.pool, st.pool)
+
+
+def test_damaged_file_is_reported(tmp_path):
+    wl, st = run_step(CFG)
+    n = st.n_entries
+    path = tmp_path / "kv.bin"
+    ops.csa_kv_save(path, st.codes, st.scales, st.k_fp8, n)
+    data = bytearray(path.read_bytes())
+    data[64 + 12345] ^= 0x10
+    path.write_bytes(bytes(data))
+    codes, scales, keys = torch.empty_like(st.codes), torch.empty_like(st.scales), torch.empty_like(st.k_fp8)
+    with pytest.raises(CsaError) as e:
+        ops.csa_kv_load(path, codes, scales, keys)
+    assert e.value.status == 6 and "checksum" in e.value.message
