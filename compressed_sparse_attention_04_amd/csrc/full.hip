@@ -66,8 +66,7 @@ __global__ __launch_bounds__(FS_THREADS) void full_select_kernel(FullSelArgs a) 
     const float* row = a.block_max + q * a.nblk;
     {
       uint32_t key[PER];
-#pragma unroll
-      for (int u = 0; u < PER; ++u) key[u] = pw + 64 * u < a.nblk ? select_key(row[pw + 64 * u]) : 0u;
+      load_keys<PER>(row, pw, (int)a.nblk, key);
       const uint32_t n_pool = block_select<FS_THREADS, PER>(s, key, (uint32_t)NB, [&](int p, uint32_t, uint32_t slot) {
         pool[slot] = p;
         if (a.pool_out) a.pool_out[q * NB + slot] = p;
@@ -84,11 +83,18 @@ __global__ __launch_bounds__(FS_THREADS) void full_select_kernel(FullSelArgs a) 
       constexpr int PP = SEL_POOL_MAX / FS_THREADS;
       const int pp = 64 * PP * wv + lane;
       uint32_t key[PP];
+      {
+        int32_t b[PP];
+        float v[PP];
 #pragma unroll
-      for (int u = 0; u < PP; ++u) {
-        const int i = pp + 64 * u;
-        const int32_t b = i < NB ? pool[i] : -1;
-        key[u] = b >= 0 ? select_key(row[b]) : 0u;
+        for (int u = 0; u < PP; ++u) {
+          const int i = pp + 64 * u;
+          b[u] = i < NB ? pool[i] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < PP; ++u) v[u] = row[b[u] >= 0 ? b[u] : 0];   // unconditional: loads overlap
+#pragma unroll
+        for (int u = 0; u < PP; ++u) key[u] = b[u] >= 0 ? select_key(v[u]) : 0u;
       }
       const uint32_t n_top = block_select<FS_THREADS, PP>(s, key, (uint32_t)K, [&](int i, uint32_t, uint32_t slot) {
         top[slot] = pool[i];
@@ -114,51 +120,57 @@ __global__ __launch_bounds__(FS_THREADS) void full_select_kernel(FullSelArgs a) 
     const uint8_t* kbase = a.k_fp8 + seq * a.k_rows * ID;
     uint4* stage = stage_all[wv];
     const int n_frag = (K + 1) / 2;   // two blocks per 16-entry fragment; wave wv takes f = wv + 16 i
-    auto load_frag = [&](int f, uint4& v0, uint4& v1) {
-      uint4 v[2];
+    if (nv == 0) {   // nothing visible: every rescored slot is empty (and no row may be read)
+      for (int i = tid; i < 16 * n_frag; i += FS_THREADS) sc[i] = -__builtin_huge_valf();
+    } else {
+      // unconditional loads, an empty slot reading entry 0 (nv >= 1 here): its
+      // score is replaced by -inf below, and a column of an MFMA fragment
+      // affects only its own output column, so its bytes do not matter
+      auto load_frag = [&](int f, uint4& v0, uint4& v1) {
+        uint4 v[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int bi = 2 * f + h;
-        const int32_t blk = (f < n_frag && bi < K) ? top[bi] : -1;
-        const int64_t e = 8 * (int64_t)blk + (lane >> 3);
-        v[h] = (blk >= 0 && e < nv) ? load16<false>(kbase + e * ID + 16 * stage_chunk(lane, h))
-                                    : make_uint4(0u, 0u, 0u, 0u);
-      }
-      v0 = v[0];
-      v1 = v[1];
-    };
-    // groups of FS_GROUP fragments per wave, the next group's loads in flight
-    constexpr int FS_GROUP = 4;
-    const int n_mine = (n_frag - wv + FS_WAVES - 1) / FS_WAVES;
-    uint4 cur[FS_GROUP][2], nxt[FS_GROUP][2];
+        for (int h = 0; h < 2; ++h) {
+          const int bi = 2 * f + h;
+          const int32_t blk = (f < n_frag && bi < K) ? top[bi] : -1;
+          const int64_t e = 8 * (int64_t)blk + (lane >> 3);
+          v[h] = load16<false>(kbase + ((blk >= 0 && e < nv) ? e : 0) * ID + 16 * stage_chunk(lane, h));
+        }
+        v0 = v[0];
+        v1 = v[1];
+      };
+      // groups of FS_GROUP fragments per wave, the next group's loads in flight
+      constexpr int FS_GROUP = 4;
+      const int n_mine = (n_frag - wv + FS_WAVES - 1) / FS_WAVES;
+      uint4 cur[FS_GROUP][2], nxt[FS_GROUP][2];
 #pragma unroll
-    for (int u = 0; u < FS_GROUP; ++u) load_frag(wv + FS_WAVES * u, cur[u][0], cur[u][1]);
-    for (int g0 = 0; g0 < n_mine; g0 += FS_GROUP) {
-      if (g0 + FS_GROUP < n_mine) {
+      for (int u = 0; u < FS_GROUP; ++u) load_frag(wv + FS_WAVES * u, cur[u][0], cur[u][1]);
+      for (int g0 = 0; g0 < n_mine; g0 += FS_GROUP) {
+        if (g0 + FS_GROUP < n_mine) {
 #pragma unroll
-        for (int u = 0; u < FS_GROUP; ++u)
-          load_frag(wv + FS_WAVES * (g0 + FS_GROUP + u), nxt[u][0], nxt[u][1]);
-      }
+          for (int u = 0; u < FS_GROUP; ++u)
+            load_frag(wv + FS_WAVES * (g0 + FS_GROUP + u), nxt[u][0], nxt[u][1]);
+        }
 #pragma unroll
-      for (int u = 0; u < FS_GROUP; ++u) {
-        const int f = wv + FS_WAVES * (g0 + u);
-        if (g0 + u >= n_mine) break;
-        __builtin_amdgcn_wave_barrier();
-        stage[lane] = cur[u][0];
-        stage[64 + lane] = cur[u][1];
-        __builtin_amdgcn_wave_barrier();
-        const f32x4 acc = frag_mma(afrag, to_frag(read_staged(stage, lane)));
-        const float sco = head_sum(acc, w4);
-        // lane n < 16 holds column n: entry 8 top[2 f + n / 8] + n % 8
-        const int bi = 2 * f + ((lane & 15) >> 3);
-        const int32_t blk = bi < K ? top[bi] : -1;
-        const int64_t e = 8 * (int64_t)blk + (lane & 7);
-        if (lane < 16) sc[16 * f + lane] = (blk >= 0 && e < nv) ? sco : -__builtin_huge_valf();
-      }
+        for (int u = 0; u < FS_GROUP; ++u) {
+          const int f = wv + FS_WAVES * (g0 + u);
+          if (g0 + u >= n_mine) break;
+          __builtin_amdgcn_wave_barrier();
+          stage[lane] = cur[u][0];
+          stage[64 + lane] = cur[u][1];
+          __builtin_amdgcn_wave_barrier();
+          const f32x4 acc = frag_mma(afrag, to_frag(read_staged(stage, lane)));
+          const float sco = head_sum(acc, w4);
+          // lane n < 16 holds column n: entry 8 top[2 f + n / 8] + n % 8
+          const int bi = 2 * f + ((lane & 15) >> 3);
+          const int32_t blk = bi < K ? top[bi] : -1;
+          const int64_t e = 8 * (int64_t)blk + (lane & 7);
+          if (lane < 16) sc[16 * f + lane] = (blk >= 0 && e < nv) ? sco : -__builtin_huge_valf();
+        }
 #pragma unroll
-      for (int u = 0; u < FS_GROUP; ++u) {
-        cur[u][0] = nxt[u][0];
-        cur[u][1] = nxt[u][1];
+        for (int u = 0; u < FS_GROUP; ++u) {
+          cur[u][0] = nxt[u][0];
+          cur[u][1] = nxt[u][1];
+        }
       }
     }
   }
@@ -170,7 +182,9 @@ __global__ __launch_bounds__(FS_THREADS) void full_select_kernel(FullSelArgs a) 
     const int pw = 64 * PER2 * wv + lane;
     uint32_t key[PER2];
 #pragma unroll
-    for (int u = 0; u < PER2; ++u) key[u] = pw + 64 * u < n ? select_key(sc[pw + 64 * u]) : 0u;
+    for (int u = 0; u < PER2; ++u) key[u] = select_key(sc[pw + 64 * u < n ? pw + 64 * u : 0]);
+#pragma unroll
+    for (int u = 0; u < PER2; ++u) key[u] = pw + 64 * u < n ? key[u] : 0u;
     const uint32_t n_sel = block_select<FS_THREADS, PER2>(s, key, (uint32_t)K, [&](int p, uint32_t, uint32_t slot) {
       a.idx[q * K + slot] = 8 * top[p >> 3] + (p & 7);
     });

@@ -56,27 +56,12 @@ __global__ __launch_bounds__(NT) void select_kernel(
 
   uint32_t key[PER];   // 0 = not selectable
   if (MODE == 0) {
-    const float* row = scores + q * ncols + start;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) key[u] = pw + 64 * u < n ? select_key(row[pw + 64 * u]) : 0u;
+    load_keys<PER>(scores + q * ncols + start, pw, n, key);
   } else if (MODE == 2) {
-    const float* row = scores + q * ncols;
-    const int32_t* map = col_blocks + q * nblk_map;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int pp = pw + 64 * u;
-      key[u] = 0u;
-      if (pp < n) {
-        const int64_t pos = start + pp;
-        const int32_t blk = map[pos >> 3];
-        const int64_t e = 8 * (int64_t)blk + (pos & 7);
-        if (blk >= 0 && e < ncols) key[u] = select_key(row[e]);
-      }
-    }
+    const int32_t* map = col_blocks + q * nblk_map + (start >> 3);   // start is a multiple of 8
+    gather_keys<PER>(scores + q * ncols, ncols, pw, n, [&](int slot) { return map[slot]; }, key);
   } else {
-    const uint32_t* row = cand_keys + q * n_in + start;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) key[u] = pw + 64 * u < n ? row[pw + 64 * u] : 0u;
+    load_raw_keys<PER>(cand_keys + q * n_in + start, pw, n, key);
   }
 
   const uint32_t n_sel = block_select<NT, PER>(s, key, (uint32_t)K, [&](int p, uint32_t k, uint32_t slot) {
@@ -122,8 +107,7 @@ __global__ __launch_bounds__(NT) void pool_topk_kernel(
     const int pw = 64 * PER * wv + lane;
     const float* row = block_max + q * nblk;
     uint32_t key[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) key[u] = pw + 64 * u < nblk ? select_key(row[pw + 64 * u]) : 0u;
+    load_keys<PER>(row, pw, (int)nblk, key);
     const uint32_t n_sel = block_select<NT, PER>(s, key, (uint32_t)NB, [&](int p, uint32_t, uint32_t slot) {
       pool[slot] = p;
       if (pool_out) pool_out[q * NB + slot] = p;
@@ -138,16 +122,7 @@ __global__ __launch_bounds__(NT) void pool_topk_kernel(
   const int n = 8 * NB;
   const float* row = scores + q * ncols;
   uint32_t key[PER2];
-#pragma unroll
-  for (int u = 0; u < PER2; ++u) {
-    const int pp = pw + 64 * u;
-    key[u] = 0u;
-    if (pp < n) {
-      const int32_t blk = pool[pp >> 3];
-      const int64_t e = 8 * (int64_t)blk + (pp & 7);
-      if (blk >= 0 && e < ncols) key[u] = select_key(row[e]);
-    }
-  }
+  gather_keys<PER2>(row, ncols, pw, n, [&](int slot) { return pool[slot]; }, key);
   const uint32_t n_sel = block_select<NT, PER2>(s, key, (uint32_t)K, [&](int p, uint32_t, uint32_t slot) {
     idx[q * K + slot] = 8 * pool[p >> 3] + (p & 7);
   });

@@ -27,6 +27,76 @@ struct SelShared {
   uint32_t bstar, rem, n_cand, T, take_eq, tlo;
 };
 
+// Key loads.  Every load below is issued unconditionally, from a clamped
+// in-range address, and the bounds are applied to the loaded values: with a
+// bound check around each load the compiler waits for every load in turn,
+// which turns PER loads into PER round trips.
+//
+// key[u] = select_key(row[p]) for p = pw + 64 u < n, else 0 (n >= 0).
+template <int PER>
+__device__ __forceinline__ void load_keys(const float* __restrict__ row, int pw, int n, uint32_t (&key)[PER]) {
+  if (n <= 0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) key[u] = 0u;
+    return;
+  }
+  float v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int p = pw + 64 * u;
+    v[u] = row[p < n ? p : n - 1];
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) key[u] = (pw + 64 * u < n) ? select_key(v[u]) : 0u;
+}
+
+// key[u] = row[p] (already a key) for p = pw + 64 u < n, else 0.
+template <int PER>
+__device__ __forceinline__ void load_raw_keys(const uint32_t* __restrict__ row, int pw, int n, uint32_t (&key)[PER]) {
+  if (n <= 0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) key[u] = 0u;
+    return;
+  }
+  uint32_t v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int p = pw + 64 * u;
+    v[u] = row[p < n ? p : n - 1];
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) key[u] = (pw + 64 * u < n) ? v[u] : 0u;
+}
+
+// Pooled positions: position p = pw + 64 u (< n) is entry 8 b + (p & 7) of
+// row with b = block_of(p >> 3) (b < 0: no block); entries >= ncols are not
+// selectable.  block_of is called for in-range block slots only.
+template <int PER, class BlockOf>
+__device__ __forceinline__ void gather_keys(const float* __restrict__ row, int64_t ncols, int pw, int n,
+                                            BlockOf block_of, uint32_t (&key)[PER]) {
+  if (n <= 0 || ncols <= 0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) key[u] = 0u;
+    return;
+  }
+  int64_t e[PER];
+  bool ok[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int p = pw + 64 * u;
+    const int pc = p < n ? p : 0;
+    const int32_t b = block_of(pc >> 3);
+    const int64_t ee = 8 * (int64_t)b + (pc & 7);
+    ok[u] = p < n && b >= 0 && ee < ncols;
+    e[u] = ok[u] ? ee : 0;
+  }
+  float v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) v[u] = row[e[u]];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) key[u] = ok[u] ? select_key(v[u]) : 0u;
+}
+
 // Value of a valid (non-zero) key: the inverse of select_key.
 __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
