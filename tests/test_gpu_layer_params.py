@@ -138,3 +138,58 @@ def test_compress_quant_rope_widths(rope_dim, n_seq, n_per):
         assert ulps.max() <= 1, ulps.max()
         c2, s2 = mxfp4.quantize(e_gpu[s])
         assert np.array_equal(np_(codes)[s], c2) and np.array_equal(np_(scales)[s], s2)
+
+
+@pytest.mark.parametrize("n_ent,top_k,n_pool,keys", [(45000, 512, 2048, "normal"), (45000, 1024, 4096, "normal"),
+                                                     (20000, 64, 1024, "normal"), (45000, 512, 2048, "const"),
+                                                     (45000, 512, 2048, "few"), (20000, 2048, 2048, "normal"),
+                                                     (20000, 1024, 512, "normal"), (3000, 512, 2048, "normal")])
+def test_reindex_layer_sizes(n_ent, top_k, n_pool, keys):
+    """Reindex inside a pool of 512 to 4,096 blocks with Top-K 64 to 2,048 (a
+    pool smaller than Top-K included) and tie-heavy keys.  Pools hold random
+    ascending blocks, -1 padded, with a partially visible last block; the
+    selected ids come out ascending."""
+    rng = np.random.default_rng(n_ent + 3 * top_k + n_pool)
+    n_seq, win_cap = 2, 128
+    codes = rng.integers(0, 256, (n_seq, n_ent, 256)).astype(np.uint8)
+    scales = rng.integers(0x28, 0x31, (n_seq, n_ent, 32)).astype(np.uint8)
+    if keys == "normal":
+        k8 = formats.e4m3_encode(rng.standard_normal((n_seq, n_ent, 128)))
+    elif keys == "const":
+        k8 = np.broadcast_to(formats.e4m3_encode(rng.standard_normal((n_seq, 1, 128))), (n_seq, n_ent, 128))
+    else:
+        rows = formats.e4m3_encode(rng.standard_normal((n_seq, 4, 128)))
+        k8 = rows[np.arange(n_seq)[:, None], rng.integers(0, 4, (n_seq, n_ent))]
+    k8 = np.ascontiguousarray(k8)
+    q8 = formats.e4m3_encode(rng.standard_normal((n_seq, 8, 128)))
+    w = rng.random((n_seq, 8)).astype(np.float32)
+    q_attn = rng.standard_normal((n_seq, 16, 512)).astype(np.float32)
+    win = formats.e4m3_encode(rng.standard_normal((n_seq, win_cap, 512)))
+    pos = np.array([4 * n_ent - 1 - 40 * s for s in range(n_seq)], np.int32)
+    n_blk = (n_ent + 7) // 8
+    pool = np.full((n_seq, n_pool), -1, np.int32)
+    for s in range(n_seq):
+        m = min(n_pool - 5, n_blk) if n_pool > 5 else n_pool
+        b = np.sort(rng.choice(n_blk, m, replace=False))
+        b[-1] = n_blk - 1
+        b = np.unique(b)
+        pool[s, :len(b)] = b
+    idx = torch.empty((n_seq, top_k), dtype=torch.int32, device=DEV)
+    out = torch.empty((n_seq, 16, 512), dtype=torch.float32, device=DEV)
+    call = ops.LayerCall(ops.MODE_REINDEX, codes=t_(codes), scales=t_(scales), k_fp8=t_(k8), win=t_(win),
+                         q_pos=t_(pos), q_attn=t_(q_attn), idx=idx, out=out, n_seq=n_seq, q_per_seq=1,
+                         n_entries=n_ent, q_idx=t_(q8), w_idx=t_(w), pool_blocks=t_(pool), top_k=top_k,
+                         n_pool_blocks=n_pool)
+    call()
+    torch.cuda.synchronize()
+    gi, go = np_(idx), np_(out)
+    for s in range(n_seq):
+        wp = oracle.window_positions(pos[s])
+        ref = oracle.layer_reindex(codes[s], scales[s], k8[s], pool[s], q8[s], w[s], q_attn[s], pos[s],
+                                   win[s, wp % win_cap], SM, k=top_k, n_entries=n_ent)
+        nv = oracle.visible_entries(pos[s], n_ent)
+        ids = oracle.pooled_entries(pool[s], nv)
+        if check_topk_set(gi[s], ref.scores, ref.idx, top_k, ids=ids) == 0:
+            assert np.array_equal(np.sort(gi[s]), np.sort(ref.idx))
+            assert np.array_equal(gi[s][gi[s] >= 0], np.sort(gi[s][gi[s] >= 0]))   # ascending ids
+            check_attn(go[s], ref.out)
