@@ -407,13 +407,13 @@ def main():
     cfg = W.CONFIGS[args.config]
     digest = source_digest(["index.hip", "index_core.h", "common.h"])
     if cfg.kind == "decode":
-        key = "score_query_dense_" + cfg.name
+        key = "score_scan_" + cfg.name
         achieved = main_res["indexer_gbps"]
         traffic = counter_traffic(key, digest)
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": None if traffic is None else int(traffic),
-                    "kernel": "score_query_kernel<false> (Full-layer dense indexer)",
+                    "kernel": "score_scan_kernel (Full-layer dense indexer)",
                     "algorithmic_bytes_per_launch": main_res["indexer_bytes"],
                     "avg_launch_ms": round(main_res["indexer_ms"], 4)}
         cp = copy_peak_gbs()

@@ -26,15 +26,14 @@ namespace csa {
 using namespace idxf;
 
 // ---------------------------------------------------------------------------
-// One query per block (decode, and every pooled call): the block covers
-// SQ_COLS columns, each of its 4 waves SQ_COLS / 4 of them, 16 per MFMA.
-// Key rows stream through whole-line loads (non-temporal for the dense scan,
-// whose rows are read once) and a per-wave LDS staging slot.
+// Pooled scoring, one query per block: the block covers SQ_COLS pooled
+// columns, each of its 4 waves SQ_COLS / 4 of them, 16 per MFMA.  Key rows
+// (1 KiB pool blocks) stream through whole-line loads and a per-wave LDS
+// staging slot.
 constexpr int SQ_COLS = 1024;
 constexpr int SQ_UNROLL = 4;
 
-template <bool POOLED>
-__global__ __launch_bounds__(256) void score_query_kernel(ScoreArgs a, int64_t ncols) {
+__global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t ncols) {
   __shared__ uint4 stage_all[4][128];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint4* stage = stage_all[wave];
@@ -54,23 +53,19 @@ __global__ __launch_bounds__(256) void score_query_kernel(ScoreArgs a, int64_t n
   const int64_t nblk = (ncols + 7) >> 3;
   const int64_t c_wave = (int64_t)blockIdx.x * SQ_COLS + wave * (SQ_COLS / 4);
   constexpr int NFRAG = SQ_COLS / 4 / 16;
-  // pooled: lane i < 2 NFRAG holds the pool block of half i (8 columns from
+  // lane i < 2 NFRAG holds the pool block of half i (8 columns from
   // c_wave + 8 i); every half reads it back as a wave-uniform value
   int32_t my_blk = -1;
-  if (POOLED && lane < 2 * NFRAG && c_wave + 8 * lane < ncols)
+  if (lane < 2 * NFRAG && c_wave + 8 * lane < ncols)
     my_blk = a.pool[q * a.n_pool_blocks + ((c_wave + 8 * lane) >> 3)];
   auto half_blk = [&](int i) { return __builtin_amdgcn_readlane(my_blk, i); };
   // half h of fragment f: one whole-line load of 8 rows (lane / 8 picks the row)
   auto load_half = [&](int f, int h) {
     const int64_t col = c_wave + 16 * f + 8 * h + (lane >> 3);
-    int64_t e = col;
-    bool ok = col < ncols;
-    if (POOLED) {
-      const int32_t blk = half_blk(2 * f + h);
-      ok = ok && blk >= 0;
-      e = 8 * (int64_t)blk + (col & 7);
-    }
-    return (ok && e < nv) ? load16<!POOLED>(kbase + e * ID + 16 * stage_chunk(lane, h)) : make_uint4(0u, 0u, 0u, 0u);
+    const int32_t blk = half_blk(2 * f + h);
+    const int64_t e = 8 * (int64_t)blk + (col & 7);
+    return (col < ncols && blk >= 0 && e < nv) ? load16<false>(kbase + e * ID + 16 * stage_chunk(lane, h))
+                                               : make_uint4(0u, 0u, 0u, 0u);
   };
   auto load_frag = [&](int f, uint4& v0, uint4& v1) {
     v0 = load_half(f, 0);
@@ -79,15 +74,10 @@ __global__ __launch_bounds__(256) void score_query_kernel(ScoreArgs a, int64_t n
   // validity of the lane's output column c_wave + 16 f + lane % 16
   auto col_valid = [&](int f) {
     const int64_t col = c_wave + 16 * f + (lane & 15);
-    bool ok = col < ncols;
-    int64_t e = col;
-    if (POOLED) {
-      const int32_t b0 = half_blk(2 * f), b1 = half_blk(2 * f + 1);
-      const int32_t blk = (lane & 8) ? b1 : b0;
-      ok = ok && blk >= 0;
-      e = 8 * (int64_t)blk + (col & 7);
-    }
-    return ok && e < nv;
+    const int32_t b0 = half_blk(2 * f), b1 = half_blk(2 * f + 1);
+    const int32_t blk = (lane & 8) ? b1 : b0;
+    const int64_t e = 8 * (int64_t)blk + (col & 7);
+    return col < ncols && blk >= 0 && e < nv;
   };
   // software pipeline: the next SQ_UNROLL fragments load while these compute
   uint4 cur[SQ_UNROLL][2], nxt[SQ_UNROLL][2];
@@ -109,7 +99,7 @@ __global__ __launch_bounds__(256) void score_query_kernel(ScoreArgs a, int64_t n
       float s = head_sum(acc, w4);
       int64_t col = c_wave + 16 * (f0 + u) + (lane & 15);
       float v = col_valid(f0 + u) ? s : -__builtin_huge_valf();
-      store_frag(v, q, col, ncols, nblk, a.scores, POOLED ? nullptr : a.block_max, lane, lane < 16);
+      store_frag(v, q, col, ncols, nblk, a.scores, nullptr, lane, lane < 16);
     }
 #pragma unroll
     for (int u = 0; u < SQ_UNROLL; ++u) {
@@ -117,6 +107,97 @@ __global__ __launch_bounds__(256) void score_query_kernel(ScoreArgs a, int64_t n
       cur[u][1] = nxt[u][1];
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Dense scan of one query per block row, persistent over column chunks: block
+// (b, q) takes the SQ_COLS-column chunks b, b + gridDim.x, ... of query q, so
+// the query fragment, the weights and the visible count are loaded once per
+// block, and each wave runs one software pipeline over all its fragments
+// (256 columns per chunk, SC_GROUP fragments per group, two register sets
+// used in turn so that no register with a load in flight is copied).  Key
+// loads are unconditional: a column past the visible entries reads entry 0
+// and its score is replaced by -inf (an MFMA column only reaches its own
+// output column), so the compiler can count the loads in flight instead of
+// waiting for all of them.
+constexpr int SC_GROUP = 4;
+constexpr int SC_BLOCKS = 2048;   // two rounds of four 4-wave blocks per compute unit
+
+__global__ __launch_bounds__(256) void score_scan_kernel(ScoreArgs a, int64_t ncols) {
+  __shared__ uint4 stage_all[4][128];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint4* stage = stage_all[wave];
+  const int64_t q = blockIdx.y;
+  const int64_t seq = q / a.q_per_seq;
+  const int nv_pos = visible_count(a.q_pos[q]);
+  const int64_t nv = nv_pos < a.n_entries ? nv_pos : a.n_entries;
+  const int row = lane & 15;
+  const Frag16 afrag = load_qfrag(a.q_fp8, q, row, row < IH, lane);
+  float w4[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) w4[r] = (lane < 32) ? a.w[q * IH + 4 * (lane >> 4) + r] : 0.f;
+  const uint8_t* kbase = a.k_fp8 + seq * a.k_rows * ID;
+  const int64_t nblk = (ncols + 7) >> 3;
+  constexpr int NFRAG = SQ_COLS / 4 / 16;   // fragments of a wave per chunk
+  // outputs through buffer stores: no branch around a store, so the compiler
+  // can count the memory operations in flight (stores count with the loads)
+  constexpr uint32_t OOB = 0x80000000u;
+  float* const any_out = a.scores ? a.scores : a.block_max;
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      a.scores ? (void*)(a.scores + q * ncols) : (void*)any_out, (short)0, a.scores ? (int)(ncols * 4) : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+      a.block_max ? (void*)(a.block_max + q * nblk) : (void*)any_out, (short)0, a.block_max ? (int)(nblk * 4) : 0,
+      0x00020000);
+  const int64_t n_chunks = (ncols + SQ_COLS - 1) / SQ_COLS;
+  const int64_t my_chunks = blockIdx.x < n_chunks ? (n_chunks - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  const int n_groups = (int)(my_chunks * (NFRAG / SC_GROUP));
+  // first column of fragment g of this wave's stream
+  auto frag_col = [&](int g) {
+    const int64_t chunk = blockIdx.x + (int64_t)gridDim.x * (g / NFRAG);
+    return chunk * SQ_COLS + wave * (SQ_COLS / 4) + 16 * (g % NFRAG);
+  };
+  auto load_group = [&](int grp, uint4 (&v)[SC_GROUP][2]) {
+#pragma unroll
+    for (int u = 0; u < SC_GROUP; ++u) {
+      const int64_t c0 = frag_col(grp * SC_GROUP + u);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t col = c0 + 8 * h + (lane >> 3);
+        const int64_t e = (grp < n_groups && col < ncols && col < nv) ? col : 0;
+        v[u][h] = load16<true>(kbase + e * ID + 16 * stage_chunk(lane, h));
+      }
+    }
+  };
+  auto compute_group = [&](int grp, const uint4 (&v)[SC_GROUP][2]) {
+#pragma unroll
+    for (int u = 0; u < SC_GROUP; ++u) {
+      __builtin_amdgcn_wave_barrier();   // the previous fragment's staged reads come first
+      stage[lane] = v[u][0];
+      stage[64 + lane] = v[u][1];
+      __builtin_amdgcn_wave_barrier();   // stores before the transposed reads (LDS keeps wave order)
+      const f32x4 acc = frag_mma(afrag, to_frag(read_staged(stage, lane)));
+      const float sc = head_sum(acc, w4);
+      const int64_t col = frag_col(grp * SC_GROUP + u) + (lane & 15);
+      const float v_out = (col < ncols && col < nv) ? sc : -__builtin_huge_valf();
+      const float m_out = score_max8(v_out);
+      // lanes 0-15 own the scores, lanes 0 and 8 the block maxima; other
+      // lanes (and a missing output) store out of range, which is dropped
+      const uint32_t vo_s = (lane < 16 && col < ncols) ? (uint32_t)col * 4u : OOB;
+      const uint32_t vo_b = (lane < 16 && (lane & 7) == 0 && (col >> 3) < nblk) ? (uint32_t)(col >> 3) * 4u : OOB;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v_out), srs, vo_s, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_out), brs, vo_b, 0, 0);
+    }
+  };
+  uint4 ra[SC_GROUP][2], rb[SC_GROUP][2];
+  if (n_groups > 0) load_group(0, ra);
+  int grp = 0;
+  for (; grp + 1 < n_groups; grp += 2) {
+    load_group(grp + 1, rb);
+    compute_group(grp, ra);
+    if (grp + 2 < n_groups) load_group(grp + 2, ra);
+    compute_group(grp + 1, rb);
+  }
+  if (grp < n_groups) compute_group(grp, ra);
 }
 
 // ---------------------------------------------------------------------------
@@ -149,20 +230,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   int nvq[8];            // visible columns of the query of this lane's C rows
   uint32_t live = 0;     // bit f: that query exists
   int nv_max = 0;
+  {
+    // every load first, from clamped (existing) queries, then the conversions:
+    // a load under a branch, or a use right after it, would cost one round
+    // trip per query pair
+    Raw32 rq[8];
+    int32_t pq[8];
+    float wq[8][4];
 #pragma unroll
-  for (int f = 0; f < 8; ++f) {
-    const int qa = qs0 + 2 * f + (row >> 3);            // query of this lane's A row
-    afrag[f] = load_qfrag(a.q_fp8, qseq0 + qa, row & 7, qa < qps, lane);
-    const int qo = qs0 + 2 * f + (lane >> 5);           // query of this lane's C rows
-    const bool ok = qo < qps;
-    live |= (uint32_t)ok << f;
-    const int nvp = ok ? visible_count(a.q_pos[qseq0 + qo]) : 0;
-    nvq[f] = nvp < a.n_entries ? nvp : (int)a.n_entries;
-    nv_max = nvq[f] > nv_max ? nvq[f] : nv_max;
+    for (int f = 0; f < 8; ++f) {
+      const int qa = qs0 + 2 * f + (row >> 3);          // query of this lane's A row
+      const int qo = qs0 + 2 * f + (lane >> 5);         // query of this lane's C rows
+      const int64_t qac = qseq0 + (qa < qps ? qa : qps - 1), qoc = qseq0 + (qo < qps ? qo : qps - 1);
+      rq[f] = load_raw32(a.q_fp8 + (qac * IH + (row & 7)) * ID, true, lane);
+      pq[f] = a.q_pos[qoc];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * ((lane >> 4) & 1) + r;
-      w4[f][r] = ok ? a.w[(qseq0 + qo) * IH + h] : 0.f;
+      for (int r = 0; r < 4; ++r) wq[f][r] = a.w[qoc * IH + 4 * ((lane >> 4) & 1) + r];
+    }
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const int qa = qs0 + 2 * f + (row >> 3);
+      const int qo = qs0 + 2 * f + (lane >> 5);
+      const bool ok = qo < qps;
+      const Raw32 z = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+      afrag[f] = to_frag(qa < qps ? rq[f] : z);
+      live |= (uint32_t)ok << f;
+      const int nvp = ok ? visible_count(pq[f]) : 0;
+      nvq[f] = nvp < a.n_entries ? nvp : (int)a.n_entries;
+      nv_max = nvq[f] > nv_max ? nvq[f] : nv_max;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w4[f][r] = ok ? wq[f][r] : 0.f;
     }
   }
   // wave-uniform bounds on the visible columns of these 16 queries
@@ -252,15 +349,22 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t st) {
   if (Q == 0 || ncols == 0) return hipSuccess;
   if (a.pool) {
     dim3 grid((unsigned)((ncols + SQ_COLS - 1) / SQ_COLS), (unsigned)Q);
-    hipLaunchKernelGGL(score_query_kernel<true>, grid, dim3(256), 0, st, a, ncols);
+    hipLaunchKernelGGL(score_pool_kernel, grid, dim3(256), 0, st, a, ncols);
   } else if (a.q_per_seq >= 32 && ncols < (int64_t(1) << 23)) {   // 32-bit buffer offsets
     int64_t tiles = (a.q_per_seq + ST_QUERIES - 1) / ST_QUERIES;
     dim3 grid((unsigned)((ncols + ST_COLS - 1) / ST_COLS), (unsigned)(a.n_seq * tiles));
     if (a.block_max) hipLaunchKernelGGL(score_tile_kernel<true>, grid, dim3(256), 0, st, a, ncols);
     else hipLaunchKernelGGL(score_tile_kernel<false>, grid, dim3(256), 0, st, a, ncols);
   } else {
-    dim3 grid((unsigned)((ncols + SQ_COLS - 1) / SQ_COLS), (unsigned)Q);
-    hipLaunchKernelGGL(score_query_kernel<false>, grid, dim3(256), 0, st, a, ncols);
+    // about SC_BLOCKS blocks, every block of a query with the same number of chunks
+    const int64_t n_chunks = (ncols + SQ_COLS - 1) / SQ_COLS;
+    int64_t per_q = (SC_BLOCKS + Q - 1) / Q;
+    per_q = per_q < n_chunks ? per_q : n_chunks;
+    const int64_t chunks_per_block = (n_chunks + per_q - 1) / per_q;
+    per_q = (n_chunks + chunks_per_block - 1) / chunks_per_block;
+    dim3 grid((unsigned)per_q, (unsigned)Q);
+    if (ncols >= ((int64_t)1 << 29)) return hipErrorInvalidValue;   // 32-bit buffer offsets
+    hipLaunchKernelGGL(score_scan_kernel, grid, dim3(256), 0, st, a, ncols);
   }
   return hipGetLastError();
 }
