@@ -334,3 +334,18 @@ def test_window_rebuild_then_append_matches_rebuild_later():
     ops.csa_window_rebuild(x, pl + 1, b, n_ring, 128, x_ring_stride=129 * 512, x_offset=512)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_index_score_pooled_nothing_visible():
+    """Pooled scoring with no visible entry (no entries at all, or a query
+    before the first complete entry): every column is -inf."""
+    rng = np.random.default_rng(9)
+    q8 = formats.e4m3_encode(rng.standard_normal((2, 8, 128)))
+    w = rng.random((2, 8)).astype(np.float32)
+    k8 = formats.e4m3_encode(rng.standard_normal((2, 64, 128)))
+    pool = np.tile(np.arange(8, dtype=np.int32), (2, 1))
+    for n_entries, pos in [(0, [100, 200]), (64, [2, 1])]:
+        sc, _ = ops.csa_index_score(t_(q8), t_(w), t_(np.array(pos, np.int32)), t_(k8), 2, 1, n_entries,
+                                    pool_blocks=t_(pool))
+        torch.cuda.synchronize()
+        assert np.isneginf(np_(sc)).all()
