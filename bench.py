@@ -316,6 +316,37 @@ def measure_kv_io(n_seq=4, entries=262144):
         torch.cuda.empty_cache()
 
 
+def probe_peaks():
+    """What this GPU sustains: fp16 MFMA TFLOP/s (independent chains of the
+    indexer's instruction) and read GB/s (the indexer's whole-line
+    non-temporal loads over 2 GiB), timed with HIP events."""
+    import torch
+    from compressed_sparse_attention_04_amd import ops
+    lib = ops._lib.load()
+    out = torch.zeros(4, device="cuda")
+    st = ops._stream()
+    blocks, iters = 512, 300     # two waves per SIMD, 32 independent chains each (~6e14 flops)
+
+    def mfma():
+        rc = lib.csa_probe_mfma_f16(ops._p(out), blocks, iters, st)
+        if rc:
+            raise RuntimeError(lib.csa_last_error().decode())
+    ms = time_kernel(mfma, 5)
+    flops = blocks * 4 * iters * 32 * 2 * 16 * 16 * 32
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+
+    def read():
+        rc = lib.csa_probe_read(ops._p(buf), buf.numel(), ops._p(out), st)
+        if rc:
+            raise RuntimeError(lib.csa_last_error().decode())
+    ms_r = time_kernel(read, 10)
+    res = {"mfma_f16_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "read_gbs": round(buf.numel() / (ms_r * 1e-3) / 1e9, 1)}
+    del buf
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_peak_gbs(reps=10):
     """Read + write bandwidth of a plain 1 GiB device copy (the practical HBM
     ceiling beside the 8 TB/s peak)."""
@@ -421,6 +452,10 @@ def main():
         # than this read-only scan, so the fraction can exceed 1
         roofline["stream_copy_gbs"] = round(cp, 1)
         roofline["frac_of_stream_copy"] = round(achieved / cp, 4)
+        pk = probe_peaks()
+        roofline["read_probe_gbs"] = pk["read_gbs"]          # the scan's own loads, nothing else
+        roofline["frac_of_read_probe"] = round(achieved / pk["read_gbs"], 4)
+        main_res["mfma_probe_tflops"] = pk["mfma_f16_tflops"]
         value, unit = main_res["tokens_per_s"], "tokens/s"
     else:
         key = "score_tile_" + cfg.name
@@ -457,6 +492,9 @@ def main():
             if "indexer_tflops" in r:
                 e["indexer_tflops"] = round(r["indexer_tflops"], 1)
                 e["indexer_frac_f16_peak"] = round(r["indexer_tflops"] / F16_PEAK_TFLOPS, 4)
+                if "mfma_probe_tflops" in main_res:
+                    e["mfma_f16_probe_tflops"] = main_res["mfma_probe_tflops"]
+                    e["indexer_frac_f16_probe"] = round(r["indexer_tflops"] / main_res["mfma_probe_tflops"], 4)
                 e["indexer_frac_f8_peak"] = round(r["indexer_tflops"] / F8_PEAK_TFLOPS, 4)
             else:
                 e["indexer_gbps"] = round(r["indexer_gbps"], 1)

@@ -49,6 +49,8 @@ SIGNATURES = {
     "csa_kv_load": (c_i32, [ctypes.c_char_p, c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_void_p, c_size,
                             c_void_p]),
     "csa_kv_file_info": (c_i32, [ctypes.c_char_p, c_void_p, c_void_p]),
+    "csa_probe_mfma_f16": (c_i32, [c_void_p, c_i32, c_i32, c_void_p]),
+    "csa_probe_read": (c_i32, [c_void_p, c_i64, c_void_p, c_void_p]),
     "csa_index_score": (c_i32, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_i64, c_i64,
                                 c_void_p, c_i32, c_void_p, c_void_p, c_void_p]),
     "csa_topk_workspace_size": (c_size, [c_i64, c_i64, c_i32]),

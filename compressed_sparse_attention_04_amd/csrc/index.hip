@@ -309,29 +309,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     __syncthreads();   // round r is in buffer r & 1; the other buffer's readers are done
     if (r + 1 < N_ROUNDS) stage[(r + 1) & 1][fr][64 * h + li] = nxt;
     if (r + 2 < N_ROUNDS) nxt = load_round(r + 2);
-#pragma unroll 1
+    // Each key fragment against the wave's 8 query pairs: 8 independent
+    // accumulators with the k-steps interleaved across them (a chain of
+    // dependent MFMAs on one accumulator would wait on each result), then
+    // the 8 epilogues.
+    const int rbase = c0 + ST_ROUND * r;
+    if (rbase >= nc) continue;   // uniform; the round's barrier above is shared
+#pragma unroll
     for (int f2 = 0; f2 < 2; ++f2) {
-      const int cbase = c0 + ST_ROUND * r + 16 * f2;
-      if (cbase >= nc) break;
+      const int cbase = rbase + 16 * f2;
+      const Frag16 b = to_frag(read_staged(stage[r & 1][f2], lane));
+      f32x4 acc[8];
+#pragma unroll
+      for (int f = 0; f < 8; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int f = 0; f < 8; ++f) acc[f] = mfma_f16_16x16x32(afrag[f].s[ks], b.s[ks], acc[f]);
       const int col = cbase + (lane & 15);
       const uint32_t vo_s = (has_sc && col < nc && (lane & 16) == 0) ? (uint32_t)(lrow * nc + col) * 4u : OOB;
       const uint32_t vo_b = (BM && col < nc && (lane & 23) == 0) ? (uint32_t)(lrow * nblk + (col >> 3)) * 4u : OOB;
-      if (cbase >= nv_max) {
-        // no query of this wave sees these columns
-#pragma unroll
-        for (int f = 0; f < 8; ++f) {
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-__builtin_huge_valf()), srs, vo_s, 2 * f * nc * 4, 0);
-          if (BM) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-__builtin_huge_valf()), brs, vo_b, 2 * f * nblk * 4, 0);
-        }
-        continue;
-      }
+      // columns no query of this wave sees (or past the row) score -inf
+      const bool seen = cbase < nv_max;
       const bool all_visible = cbase + 16 <= nv_min;
-      const Frag16 b = to_frag(read_staged(stage[r & 1][f2], lane));
 #pragma unroll
       for (int f = 0; f < 8; ++f) {
-        const f32x4 acc = frag_mma(afrag[f], b);
-        float v = head_sum(acc, w4[f]);
-        if (!all_visible) v = (col < nvq[f]) ? v : -__builtin_huge_valf();
+        float v = head_sum(acc[f], w4[f]);
+        if (!all_visible) v = (seen && col < nvq[f]) ? v : -__builtin_huge_valf();
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srs, vo_s, 2 * f * nc * 4, 0);
         if (BM) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score_max8(v)), brs, vo_b, 2 * f * nblk * 4, 0);
       }

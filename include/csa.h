@@ -198,6 +198,19 @@ csa_status csa_kv_load(const char* path, uint8_t* codes, uint8_t* scales, uint8_
                        hipStream_t stream);
 csa_status csa_kv_file_info(const char* path, int64_t* n_seq, int64_t* n_entries);
 
+/* -------------------------------------------------------- measurement ----
+ * Probes of what the GPU sustains for the indexer's two resources (not part
+ * of the method; the benchmark reports the indexer against them beside the
+ * published peaks).
+ * csa_probe_mfma_f16: `blocks` blocks of 256 threads, every wave running
+ *   iters x 32 independent v_mfma_f32_16x16x32_f16 (16,384 multiply-adds
+ *   each); out: one float (device), written only to keep the work live.
+ * csa_probe_read: reads `bytes` (a multiple of 16, buf 16-byte aligned) with
+ *   whole-line non-temporal 16-byte loads; out as above.
+ */
+csa_status csa_probe_mfma_f16(float* out, int32_t blocks, int32_t iters, hipStream_t stream);
+csa_status csa_probe_read(const uint8_t* buf, int64_t bytes, float* out, hipStream_t stream);
+
 /* ---------------------------------------------------------------- a3 ----
  * csa_index_score: indexer scores of Q = n_seq * q_per_seq queries (P3 §02:
  * Full layers score every causally visible position; Reindex layers rescore
