@@ -225,17 +225,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int qs0 = (int)(blockIdx.y % tiles_per_seq) * ST_QUERIES + 16 * wave;   // in-sequence index
   const int64_t qseq0 = seq * a.q_per_seq;
   const int row = lane & 15;
+  // After the paired head sums (head_sum_pair over query pairs 2p and 2p+1),
+  // lane l holds the score of wave query 4p + vrow, vrow = 2 ((l / 16) & 1) + l / 32.
+  const int vrow = 2 * ((lane >> 4) & 1) + (lane >> 5);
   Frag16 afrag[8];
   float w4[8][4];
-  int nvq[8];            // visible columns of the query of this lane's C rows
-  uint32_t live = 0;     // bit f: that query exists
-  int nv_max = 0;
+  int nvs[4];            // visible columns of this lane's output query, per pair set
+  int nv_min = 0x7FFFFFFF;
   {
     // every load first, from clamped (existing) queries, then the conversions:
     // a load under a branch, or a use right after it, would cost one round
     // trip per query pair
     Raw32 rq[8];
-    int32_t pq[8];
+    int32_t pq[4];
     float wq[8][4];
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
@@ -243,56 +245,63 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       const int qo = qs0 + 2 * f + (lane >> 5);         // query of this lane's C rows
       const int64_t qac = qseq0 + (qa < qps ? qa : qps - 1), qoc = qseq0 + (qo < qps ? qo : qps - 1);
       rq[f] = load_raw32(a.q_fp8 + (qac * IH + (row & 7)) * ID, true, lane);
-      pq[f] = a.q_pos[qoc];
 #pragma unroll
       for (int r = 0; r < 4; ++r) wq[f][r] = a.w[qoc * IH + 4 * ((lane >> 4) & 1) + r];
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int qv = qs0 + 4 * p + vrow;
+      pq[p] = a.q_pos[qseq0 + (qv < qps ? qv : qps - 1)];
     }
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
       const int qa = qs0 + 2 * f + (row >> 3);
       const int qo = qs0 + 2 * f + (lane >> 5);
-      const bool ok = qo < qps;
       const Raw32 z = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
       afrag[f] = to_frag(qa < qps ? rq[f] : z);
-      live |= (uint32_t)ok << f;
-      const int nvp = ok ? visible_count(pq[f]) : 0;
-      nvq[f] = nvp < a.n_entries ? nvp : (int)a.n_entries;
-      nv_max = nvq[f] > nv_max ? nvq[f] : nv_max;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) w4[f][r] = ok ? wq[f][r] : 0.f;
+      for (int r = 0; r < 4; ++r) w4[f][r] = qo < qps ? wq[f][r] : 0.f;
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const bool ok = qs0 + 4 * p + vrow < qps;
+      const int nvp = ok ? visible_count(pq[p]) : 0;
+      nvs[p] = nvp < a.n_entries ? nvp : (int)a.n_entries;
+      if (ok) nv_min = nvs[p] < nv_min ? nvs[p] : nv_min;
     }
   }
-  // wave-uniform bounds on the visible columns of these 16 queries
-  int nv_min = 0x7FFFFFFF;
-#pragma unroll
-  for (int f = 0; f < 8; ++f)
-    if ((live >> f) & 1u) nv_min = nvq[f] < nv_min ? nvq[f] : nv_min;
+  // wave-uniform bound on the visible columns of these 16 queries (scalar,
+  // so the masking below is a branch, taken only on partly visible fragments)
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    const int o = __shfl_xor(nv_max, off), p = __shfl_xor(nv_min, off);
-    nv_max = o > nv_max ? o : nv_max;
-    nv_min = p < nv_min ? p : nv_min;
+    const int o = __shfl_xor(nv_min, off);
+    nv_min = o < nv_min ? o : nv_min;
   }
+  nv_min = __builtin_amdgcn_readfirstlane(nv_min);
   const uint8_t* kbase = a.k_fp8 + seq * a.k_rows * ID;
   const int nblk = (int)((ncols + 7) >> 3);
   const int nc = (int)ncols;                 // < 2^23 (checked by the launcher)
   const int c0 = blockIdx.x * ST_COLS;
-  // Buffer views of this tile's score / block-max rows; stores with an offset
-  // past the live rows (or the OOB marker) are dropped by the hardware, which
-  // replaces per-lane branches.  Row of fragment f for this lane:
-  // 16 wave + 2 f + lane / 32 (the f part goes in the scalar offset).
+  // Buffer views of this tile's score / block-max rows, one per pair set p
+  // (rows 4p .. of the tile, holding only the live rows from there on), so the
+  // hardware's bounds check drops the stores of absent queries and of the
+  // out-of-range marker; the offset is the lane's voffset alone.
   const int tile_q0 = (int)(blockIdx.y % tiles_per_seq) * ST_QUERIES;
   const int live_rows = (qps - tile_q0) < ST_QUERIES ? (qps - tile_q0) : ST_QUERIES;
-  // scores may be absent (block maxima only): an empty view drops every store
   const bool has_sc = a.scores != nullptr;
-  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      has_sc ? (void*)(a.scores + (qseq0 + tile_q0) * ncols) : (void*)a.block_max, (short)0,
-      has_sc ? live_rows * nc * 4 : 0, 0x00020000);
-  const __amdgpu_buffer_rsrc_t brs = BM ?
-      __builtin_amdgcn_make_buffer_rsrc(a.block_max + (qseq0 + tile_q0) * (int64_t)nblk, (short)0, live_rows * nblk * 4,
-                                        0x00020000) : srs;
+  __amdgpu_buffer_rsrc_t srs[4], brs[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int rows = live_rows - 4 * p > 0 ? live_rows - 4 * p : 0;
+    srs[p] = __builtin_amdgcn_make_buffer_rsrc(
+        has_sc ? (void*)(a.scores + (qseq0 + tile_q0 + 4 * p) * ncols) : (void*)a.k_fp8, (short)0,
+        has_sc ? rows * nc * 4 : 0, 0x00020000);
+    brs[p] = BM ? __builtin_amdgcn_make_buffer_rsrc(a.block_max + (qseq0 + tile_q0 + 4 * p) * (int64_t)nblk,
+                                                    (short)0, rows * nblk * 4, 0x00020000)
+                : srs[p];
+  }
   constexpr uint32_t OOB = 0x80000000u;
-  const int lrow = 16 * wave + (lane >> 5);
+  const int lrow = 16 * wave + vrow;
   // this thread's chunk of every round: fragment fr, half h, staging slot 64 h + li
   const int fr = tid >> 7, h = (tid >> 6) & 1, li = tid & 63;
   const int n_row = 8 * h + (li >> 3);
@@ -312,7 +321,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     // Each key fragment against the wave's 8 query pairs: 8 independent
     // accumulators with the k-steps interleaved across them (a chain of
     // dependent MFMAs on one accumulator would wait on each result), then
-    // the 8 epilogues.
+    // the epilogues, two query pairs per cross-lane swap.
     const int rbase = c0 + ST_ROUND * r;
     if (rbase >= nc) continue;   // uniform; the round's barrier above is shared
 #pragma unroll
@@ -327,17 +336,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
         for (int f = 0; f < 8; ++f) acc[f] = mfma_f16_16x16x32(afrag[f].s[ks], b.s[ks], acc[f]);
       const int col = cbase + (lane & 15);
-      const uint32_t vo_s = (has_sc && col < nc && (lane & 16) == 0) ? (uint32_t)(lrow * nc + col) * 4u : OOB;
-      const uint32_t vo_b = (BM && col < nc && (lane & 23) == 0) ? (uint32_t)(lrow * nblk + (col >> 3)) * 4u : OOB;
-      // columns no query of this wave sees (or past the row) score -inf
-      const bool seen = cbase < nv_max;
-      const bool all_visible = cbase + 16 <= nv_min;
+      const uint32_t vo_s = col < nc ? (uint32_t)(lrow * nc + col) * 4u : OOB;
+      const uint32_t vo_b = (col < nc && (lane & 7) == 0) ? (uint32_t)(lrow * nblk + (col >> 3)) * 4u : OOB;
+      float v[4];
 #pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        float v = head_sum(acc[f], w4[f]);
-        if (!all_visible) v = (seen && col < nvq[f]) ? v : -__builtin_huge_valf();
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srs, vo_s, 2 * f * nc * 4, 0);
-        if (BM) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score_max8(v)), brs, vo_b, 2 * f * nblk * 4, 0);
+      for (int p = 0; p < 4; ++p) v[p] = head_sum_pair(acc[2 * p], w4[2 * p], acc[2 * p + 1], w4[2 * p + 1]);
+      // columns a query does not see (or past the row) score -inf
+      if (cbase + 16 > nv_min) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) v[p] = col < nvs[p] ? v[p] : -__builtin_huge_valf();
+      }
+      if (has_sc) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[p]), srs[p], vo_s, 0, 0);
+      }
+      if (BM) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score_max8(v[p])), brs[p], vo_b, 0, 0);
       }
     }
   }

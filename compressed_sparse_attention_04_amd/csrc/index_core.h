@@ -86,22 +86,40 @@ __device__ __forceinline__ float relu(float x) {
   return __int_as_float(b > 0 ? b : 0);
 }
 
-// Weighted ReLU head sum of one accumulator fragment; lanes 0-15 end with the
-// score of the first query (rows 0-7), lanes 32-47 with the second (rows 8-15).
-// The head weights are >= 0, so every score is >= +0 (or -inf where masked).
-__device__ __forceinline__ float head_sum(f32x4 acc, const float w4[4]) {
+// Weighted ReLU head sum of one accumulator fragment.  head_part is the
+// lane's sum over its 4 rows; head_sum adds the other half of the 8 heads, so
+// lanes 0-15 end with the score of the first query (rows 0-7), lanes 32-47
+// with the second (rows 8-15).  The head weights are >= 0, so every score is
+// >= +0 (or -inf where masked).
+__device__ __forceinline__ float head_part(f32x4 acc, const float w4[4]) {
   float s = w4[0] * relu(acc[0]);
   s = fmaf(w4[1], relu(acc[1]), s);
   s = fmaf(w4[2], relu(acc[2]), s);
-  s = fmaf(w4[3], relu(acc[3]), s);
-  return sum_xor16(s);
+  return fmaf(w4[3], relu(acc[3]), s);
+}
+__device__ __forceinline__ float head_sum(f32x4 acc, const float w4[4]) {
+  return sum_xor16(head_part(acc, w4));
+}
+
+// Head sums of two accumulator fragments (query pairs A and B) with one
+// cross-lane swap: v_permlane16_swap exchanges the odd 16-lane rows of the
+// first operand with the even rows of the second, so the sum of the two
+// results holds, in 16-lane rows 0..3, the scores of A's first query, B's
+// first query, A's second query and B's second query.  Every score is the
+// same two partial sums added as in head_sum, so the bits are the same.
+__device__ __forceinline__ float head_sum_pair(f32x4 a, const float wa[4], f32x4 b, const float wb[4]) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(head_part(a, wa)),
+                                                  __float_as_uint(head_part(b, wb)), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Max over aligned groups of 8 lanes for scores (>= +0 or -inf): on that
 // set the float order is the int32 order of the bit patterns, so the DPP
 // steps are integer maxes.
+// (Every lane has a source lane under these controls, so a plain DPP move,
+// which the compiler folds into the max as its DPP operand, is enough.)
 template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) { return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_i(int v) { return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true); }
 __device__ __forceinline__ float score_max8(float v) {
   int b = __float_as_int(v), o;
   o = dpp_i<0xB1>(b); b = b > o ? b : o;
