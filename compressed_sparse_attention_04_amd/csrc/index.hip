@@ -203,21 +203,27 @@ __global__ __launch_bounds__(256) void score_scan_kernel(ScoreArgs a, int64_t nc
 // ---------------------------------------------------------------------------
 // Query tiles (prefill: many queries of one sequence share the keys).  A
 // block holds 64 queries of one sequence (16 per wave, as 8 two-query A
-// fragments kept in registers) and streams ST_COLS columns in rounds of two
-// 16-key fragments.  Every thread loads one whole-line 16-byte chunk of the
-// round after next while the waves run 8 MFMAs per fragment of the current
-// round out of LDS (the staging layout of the query kernel, double-buffered,
-// one barrier a round), so the four waves share one copy of the keys.
+// fragments kept in registers) and streams ST_COLS columns in rounds of four
+// 16-key fragments.  Every thread loads two whole-line 16-byte chunks of the
+// round after next while the waves run 8 MFMAs per k-step of each fragment of
+// the current round out of LDS (the staging layout of the query kernel,
+// double-buffered, one barrier a round), so the four waves share one copy of
+// the keys.  A fragment's epilogue overlaps the next fragment's MFMAs.  (With
+// 8 independent accumulator chains per wave the matrix pipe sustains about
+// 1.19 PFLOP/s on this instruction, 16 chains about 1.7; 16 chains, as two
+// key fragments x 8 query pairs or four x 4, did not fit the epilogue's
+// overlap and the 256 registers of two waves per SIMD and ran slower.)
 constexpr int ST_QUERIES = 64;
 constexpr int ST_COLS = 512;
-constexpr int ST_ROUND = 32;
+constexpr int ST_ROUND = 64;
+constexpr int ST_FR = ST_ROUND / 16;   // key fragments per round
 
 // BM: also write the 8-column block maxima (a template parameter, so that the
 // unrolled fragment loop has no branch and the MFMAs of one query fragment
 // overlap the epilogue of another).
 template <bool BM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void score_tile_kernel(ScoreArgs a, int64_t ncols) {
-  __shared__ uint4 stage[2][2][128];   // [buffer][fragment][slot]
+  __shared__ uint4 stage[2][ST_FR][128];   // [buffer][fragment][slot]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qps = (int)a.q_per_seq;
   const int tiles_per_seq = (qps + ST_QUERIES - 1) / ST_QUERIES;
@@ -302,22 +308,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
   constexpr uint32_t OOB = 0x80000000u;
   const int lrow = 16 * wave + vrow;
-  // this thread's chunk of every round: fragment fr, half h, staging slot 64 h + li
+  // this thread's chunks of every round: fragment 2 sub + fr (sub = 0, 1),
+  // half h, staging slot 64 h + li
   const int fr = tid >> 7, h = (tid >> 6) & 1, li = tid & 63;
   const int n_row = 8 * h + (li >> 3);
   const int chunk = stage_chunk(li, h);
-  auto load_round = [&](int r) {
-    const int col = c0 + ST_ROUND * r + 16 * fr + n_row;
+  auto load_round = [&](int r, int sub) {
+    const int col = c0 + ST_ROUND * r + 32 * sub + 16 * fr + n_row;
     return col < nc ? *reinterpret_cast<const uint4*>(kbase + (int64_t)col * ID + 16 * chunk)
                     : make_uint4(0u, 0u, 0u, 0u);
   };
   constexpr int N_ROUNDS = ST_COLS / ST_ROUND;
-  stage[0][fr][64 * h + li] = load_round(0);
-  uint4 nxt = load_round(1);
+  uint4 nxt[2];
+  stage[0][fr][64 * h + li] = load_round(0, 0);
+  stage[0][2 + fr][64 * h + li] = load_round(0, 1);
+  nxt[0] = load_round(1, 0);
+  nxt[1] = load_round(1, 1);
   for (int r = 0; r < N_ROUNDS; ++r) {
     __syncthreads();   // round r is in buffer r & 1; the other buffer's readers are done
-    if (r + 1 < N_ROUNDS) stage[(r + 1) & 1][fr][64 * h + li] = nxt;
-    if (r + 2 < N_ROUNDS) nxt = load_round(r + 2);
+    if (r + 1 < N_ROUNDS) {
+      stage[(r + 1) & 1][fr][64 * h + li] = nxt[0];
+      stage[(r + 1) & 1][2 + fr][64 * h + li] = nxt[1];
+    }
+    if (r + 2 < N_ROUNDS) {
+      nxt[0] = load_round(r + 2, 0);
+      nxt[1] = load_round(r + 2, 1);
+    }
     // Each key fragment against the wave's 8 query pairs: 8 independent
     // accumulators with the k-steps interleaved across them (a chain of
     // dependent MFMAs on one accumulator would wait on each result), then
@@ -325,7 +341,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int rbase = c0 + ST_ROUND * r;
     if (rbase >= nc) continue;   // uniform; the round's barrier above is shared
 #pragma unroll
-    for (int f2 = 0; f2 < 2; ++f2) {
+    for (int f2 = 0; f2 < ST_FR; ++f2) {
       const int cbase = rbase + 16 * f2;
       const Frag16 b = to_frag(read_staged(stage[r & 1][f2], lane));
       f32x4 acc[8];
