@@ -145,6 +145,40 @@ def test_index_score_dense(n_seq, q_per_seq, n_entries, pos_base):
     assert worst <= 2e-6, worst
 
 
+@pytest.mark.parametrize("n_seq,q_per_seq", [(2, 40), (3, 100)])
+def test_index_score_ragged_tiles_stay_in_bounds(n_seq, q_per_seq):
+    """Prefill tiles hold 64 queries; a sequence whose query count is not a
+    multiple of 64 ends in a partly filled tile.  Its absent rows must not be
+    written: guard rows around the score and block-max outputs keep their
+    bytes, and the live rows match the oracle."""
+    rng = np.random.default_rng(q_per_seq)
+    n_entries = 700
+    q8, k8, w, pos = _scores_case(rng, n_seq, q_per_seq, n_entries, n_entries, 4 * 660)
+    Q, nblk, G = n_seq * q_per_seq, (n_entries + 7) // 8, 64
+    guard = np.float32(np.uint32(0x7FC01234).view(np.float32))       # a NaN the kernel never writes
+    sc_all = torch.full((Q + 2 * G, n_entries), float(guard), dtype=torch.float32, device=DEV)
+    bm_all = torch.full((Q + 2 * G, nblk), float(guard), dtype=torch.float32, device=DEV)
+    sc_all.view(torch.int32).fill_(0x7FC01234)
+    bm_all.view(torch.int32).fill_(0x7FC01234)
+    qd, wd, pd, kd = t_(q8), t_(w), t_(pos), t_(k8)
+    lib = ops._lib.load()
+    rc = lib.csa_index_score(qd.data_ptr(), wd.data_ptr(), pd.data_ptr(), n_seq, q_per_seq, kd.data_ptr(),
+                             n_entries, n_entries, None, 0, sc_all[G].data_ptr(), bm_all[G].data_ptr(),
+                             ops._stream())
+    assert rc == 0, lib.csa_last_error()
+    torch.cuda.synchronize()
+    sc_bits, bm_bits = np_(sc_all.view(torch.int32)), np_(bm_all.view(torch.int32))
+    for rows in (slice(0, G), slice(G + Q, 2 * G + Q)):
+        assert np.all(sc_bits[rows] == 0x7FC01234) and np.all(bm_bits[rows] == 0x7FC01234)
+    sc = np_(sc_all)[G:G + Q]
+    for qi in range(Q):
+        s = qi // q_per_seq
+        nv = oracle.visible_entries(pos[qi], n_entries)
+        ref = oracle.index_scores(q8[qi], w[qi], k8[s, :nv])
+        assert np.all(np.abs(sc[qi, :nv] - ref) <= 2e-6 * np.maximum(1.0, np.abs(ref)))
+        assert np.all(np.isneginf(sc[qi, nv:]))
+
+
 def test_index_score_pooled_matches_dense_bitwise():
     rng = np.random.default_rng(5)
     n_seq, n_entries = 2, 2000
