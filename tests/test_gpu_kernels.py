@@ -308,8 +308,10 @@ def _attn_ref(codes, scales, win, q, idx, pos, q_per_seq, win_cap):
     return np.stack(outs)
 
 
+# From 512 queries on (prefill) the launch plan changes: one key group, one split.
 @pytest.mark.parametrize("n_seq,q_per_seq,k,p_base", [(4, 1, 512, 5000), (1, 300, 512, 2000),
-                                                      (2, 1, 77, 60), (1, 1, 512, 0)])
+                                                      (2, 1, 77, 60), (1, 1, 512, 0),
+                                                      (1, 523, 512, 50), (2, 300, 77, 3000)])
 def test_sparse_attn(n_seq, q_per_seq, k, p_base):
     rng = np.random.default_rng(k + p_base)
     rows, win_cap = 1200, 128 + (q_per_seq if q_per_seq > 1 else 0)
