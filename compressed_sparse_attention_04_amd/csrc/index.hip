@@ -29,7 +29,12 @@ using namespace idxf;
 // Pooled scoring, one query per block: the block covers SQ_COLS pooled
 // columns, each of its 4 waves SQ_COLS / 4 of them, 16 per MFMA.  Key rows
 // (1 KiB pool blocks) stream through whole-line loads and a per-wave LDS
-// staging slot.
+// staging slot, in groups of SQ_UNROLL fragments held in two register sets
+// used in turn (the next group loads while this one computes, and no
+// register with a load in flight is copied).  Loads are unconditional: a
+// column outside the pool's visible entries reads entry 0 and scores -inf.
+// Stores go through a buffer view of the query's row (out-of-range offsets
+// are dropped), so no branch surrounds a memory operation.
 constexpr int SQ_COLS = 1024;
 constexpr int SQ_UNROLL = 4;
 
@@ -50,62 +55,66 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
     w4[r] = (lane < 32) ? a.w[q * IH + h] : 0.f;
   }
   const uint8_t* kbase = a.k_fp8 + seq * a.k_rows * ID;
-  const int64_t nblk = (ncols + 7) >> 3;
   const int64_t c_wave = (int64_t)blockIdx.x * SQ_COLS + wave * (SQ_COLS / 4);
   constexpr int NFRAG = SQ_COLS / 4 / 16;
+  constexpr int NGRP = NFRAG / SQ_UNROLL;
   // lane i < 2 NFRAG holds the pool block of half i (8 columns from
   // c_wave + 8 i); every half reads it back as a wave-uniform value
   int32_t my_blk = -1;
   if (lane < 2 * NFRAG && c_wave + 8 * lane < ncols)
     my_blk = a.pool[q * a.n_pool_blocks + ((c_wave + 8 * lane) >> 3)];
   auto half_blk = [&](int i) { return __builtin_amdgcn_readlane(my_blk, i); };
+  // entry of column col in half i, or -1 when the column holds none
+  auto half_entry = [&](int i, int64_t col) -> int64_t {
+    const int32_t blk = half_blk(i);
+    const int64_t e = 8 * (int64_t)blk + (col & 7);
+    return (col < ncols && blk >= 0 && e < nv) ? e : -1;
+  };
   // half h of fragment f: one whole-line load of 8 rows (lane / 8 picks the row)
-  auto load_half = [&](int f, int h) {
-    const int64_t col = c_wave + 16 * f + 8 * h + (lane >> 3);
-    const int32_t blk = half_blk(2 * f + h);
-    const int64_t e = 8 * (int64_t)blk + (col & 7);
-    return (col < ncols && blk >= 0 && e < nv) ? load16<false>(kbase + e * ID + 16 * stage_chunk(lane, h))
-                                               : make_uint4(0u, 0u, 0u, 0u);
-  };
-  auto load_frag = [&](int f, uint4& v0, uint4& v1) {
-    v0 = load_half(f, 0);
-    v1 = load_half(f, 1);
-  };
-  // validity of the lane's output column c_wave + 16 f + lane % 16
-  auto col_valid = [&](int f) {
-    const int64_t col = c_wave + 16 * f + (lane & 15);
-    const int32_t b0 = half_blk(2 * f), b1 = half_blk(2 * f + 1);
-    const int32_t blk = (lane & 8) ? b1 : b0;
-    const int64_t e = 8 * (int64_t)blk + (col & 7);
-    return col < ncols && blk >= 0 && e < nv;
-  };
-  // software pipeline: the next SQ_UNROLL fragments load while these compute
-  uint4 cur[SQ_UNROLL][2], nxt[SQ_UNROLL][2];
-#pragma unroll
-  for (int u = 0; u < SQ_UNROLL; ++u) load_frag(u, cur[u][0], cur[u][1]);
-#pragma unroll
-  for (int f0 = 0; f0 < NFRAG; f0 += SQ_UNROLL) {
-    if (f0 + SQ_UNROLL < NFRAG) {
-#pragma unroll
-      for (int u = 0; u < SQ_UNROLL; ++u) load_frag(f0 + SQ_UNROLL + u, nxt[u][0], nxt[u][1]);
-    }
+  auto load_group = [&](int grp, uint4 (&v)[SQ_UNROLL][2]) {
 #pragma unroll
     for (int u = 0; u < SQ_UNROLL; ++u) {
+      const int f = grp * SQ_UNROLL + u;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t e = half_entry(2 * f + h, c_wave + 16 * f + 8 * h + (lane >> 3));
+        v[u][h] = load16<false>(kbase + (e < 0 ? 0 : e) * ID + 16 * stage_chunk(lane, h));
+      }
+    }
+  };
+  constexpr uint32_t OOB = 0x80000000u;
+  // (pooled mode always has a score array; an absent one gets an empty view)
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      a.scores ? (void*)(a.scores + q * ncols) : (void*)a.k_fp8, (short)0, a.scores ? (int)(ncols * 4) : 0,
+      0x00020000);
+  auto compute_group = [&](int grp, const uint4 (&v)[SQ_UNROLL][2]) {
+#pragma unroll
+    for (int u = 0; u < SQ_UNROLL; ++u) {
+      const int f = grp * SQ_UNROLL + u;
       __builtin_amdgcn_wave_barrier();   // the previous fragment's staged reads come first
-      stage[lane] = cur[u][0];
-      stage[64 + lane] = cur[u][1];
+      stage[lane] = v[u][0];
+      stage[64 + lane] = v[u][1];
       __builtin_amdgcn_wave_barrier();   // stores before the transposed reads (LDS keeps wave order)
-      f32x4 acc = frag_mma(afrag, to_frag(read_staged(stage, lane)));
-      float s = head_sum(acc, w4);
-      int64_t col = c_wave + 16 * (f0 + u) + (lane & 15);
-      float v = col_valid(f0 + u) ? s : -__builtin_huge_valf();
-      store_frag(v, q, col, ncols, nblk, a.scores, nullptr, lane, lane < 16);
+      const f32x4 acc = frag_mma(afrag, to_frag(read_staged(stage, lane)));
+      const float sc = head_sum(acc, w4);
+      // lane's output column c_wave + 16 f + lane % 16 (lanes 0-15 own it)
+      const int64_t col = c_wave + 16 * f + (lane & 15);
+      // (both halves' block ids are read wave-uniformly, then chosen per lane)
+      const int64_t e0 = half_entry(2 * f, col), e1 = half_entry(2 * f + 1, col);
+      const bool valid = ((lane & 8) ? e1 : e0) >= 0;
+      const float v_out = valid ? sc : -__builtin_huge_valf();
+      const uint32_t vo = (lane < 16 && col < ncols) ? (uint32_t)col * 4u : OOB;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v_out), srs, vo, 0, 0);
     }
+  };
+  uint4 ra[SQ_UNROLL][2], rb[SQ_UNROLL][2];
+  load_group(0, ra);
 #pragma unroll
-    for (int u = 0; u < SQ_UNROLL; ++u) {
-      cur[u][0] = nxt[u][0];
-      cur[u][1] = nxt[u][1];
-    }
+  for (int grp = 0; grp < NGRP; grp += 2) {
+    if (grp + 1 < NGRP) load_group(grp + 1, rb);
+    compute_group(grp, ra);
+    if (grp + 2 < NGRP) load_group(grp + 2, ra);
+    if (grp + 1 < NGRP) compute_group(grp + 1, rb);
   }
 }
 
