@@ -63,13 +63,28 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
   int32_t my_blk = -1;
   if (lane < 2 * NFRAG && c_wave + 8 * lane < ncols)
     my_blk = a.pool[q * a.n_pool_blocks + ((c_wave + 8 * lane) >> 3)];
-  auto half_blk = [&](int i) { return __builtin_amdgcn_readlane(my_blk, i); };
-  // entry of column col in half i, or -1 when the column holds none
-  auto half_entry = [&](int i, int64_t col) -> int64_t {
-    const int32_t blk = half_blk(i);
-    const int64_t e = 8 * (int64_t)blk + (col & 7);
-    return (col < ncols && blk >= 0 && e < nv) ? e : -1;
+  // Half i = one pool block of 8 columns.  Lane i keeps the number of its
+  // visible entries (cnt) and the block to read (row 0's block when it has
+  // none, so every load reads existing rows); every half reads them back as
+  // wave-uniform values.  32-bit: entries < 2^30.
+  const int nv_i = (int)nv;
+  const int rem = nv_i - 8 * my_blk;
+  const int my_cnt = my_blk < 0 ? 0 : (rem <= 0 ? 0 : (rem >= 8 ? 8 : rem));
+  const int my_blkc = my_cnt > 0 ? my_blk : 0;
+  struct Half { int cnt; const uint8_t* base; };
+  auto half_cnt = [&](int i) { return __builtin_amdgcn_readlane(my_cnt, i); };
+  auto half_info = [&](int i) {
+    Half hf;
+    hf.cnt = half_cnt(i);
+    hf.base = kbase + (int64_t)__builtin_amdgcn_readlane(my_blkc, i) * (8 * ID);
+    return hf;
   };
+  // lane's byte offsets inside a half: row lane / 8, whole-line chunk of half h
+  // (row 0 when that row is not a visible entry)
+  const int lrow_k = lane >> 3;
+  const uint32_t off_row[2] = {(uint32_t)(lrow_k * ID + 16 * stage_chunk(lane, 0)),
+                               (uint32_t)(lrow_k * ID + 16 * stage_chunk(lane, 1))};
+  const uint32_t off_zero[2] = {(uint32_t)(16 * stage_chunk(lane, 0)), (uint32_t)(16 * stage_chunk(lane, 1))};
   // half h of fragment f: one whole-line load of 8 rows (lane / 8 picks the row)
   auto load_group = [&](int grp, uint4 (&v)[SQ_UNROLL][2]) {
 #pragma unroll
@@ -77,8 +92,8 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
       const int f = grp * SQ_UNROLL + u;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int64_t e = half_entry(2 * f + h, c_wave + 16 * f + 8 * h + (lane >> 3));
-        v[u][h] = load16<false>(kbase + (e < 0 ? 0 : e) * ID + 16 * stage_chunk(lane, h));
+        const Half hf = half_info(2 * f + h);
+        v[u][h] = load16<false>(hf.base + (lrow_k < hf.cnt ? off_row[h] : off_zero[h]));
       }
     }
   };
@@ -87,6 +102,8 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       a.scores ? (void*)(a.scores + q * ncols) : (void*)a.k_fp8, (short)0, a.scores ? (int)(ncols * 4) : 0,
       0x00020000);
+  const int ncols_i = (int)ncols;                     // <= 8 x 65,536
+  const int cw = (int)c_wave;
   auto compute_group = [&](int grp, const uint4 (&v)[SQ_UNROLL][2]) {
 #pragma unroll
     for (int u = 0; u < SQ_UNROLL; ++u) {
@@ -97,13 +114,12 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
       __builtin_amdgcn_wave_barrier();   // stores before the transposed reads (LDS keeps wave order)
       const f32x4 acc = frag_mma(afrag, to_frag(read_staged(stage, lane)));
       const float sc = head_sum(acc, w4);
-      // lane's output column c_wave + 16 f + lane % 16 (lanes 0-15 own it)
-      const int64_t col = c_wave + 16 * f + (lane & 15);
-      // (both halves' block ids are read wave-uniformly, then chosen per lane)
-      const int64_t e0 = half_entry(2 * f, col), e1 = half_entry(2 * f + 1, col);
-      const bool valid = ((lane & 8) ? e1 : e0) >= 0;
-      const float v_out = valid ? sc : -__builtin_huge_valf();
-      const uint32_t vo = (lane < 16 && col < ncols) ? (uint32_t)col * 4u : OOB;
+      // lane's output column cw + 16 f + lane % 16 (lanes 0-15 own it): valid
+      // when its offset in the pool block is below the block's visible count
+      const int col = cw + 16 * f + (lane & 15);
+      const int cnt = (lane & 8) ? half_cnt(2 * f + 1) : half_cnt(2 * f);
+      const float v_out = (lane & 7) < cnt ? sc : -__builtin_huge_valf();
+      const uint32_t vo = (lane < 16 && col < ncols_i) ? (uint32_t)col * 4u : OOB;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v_out), srs, vo, 0, 0);
     }
   };
