@@ -69,15 +69,17 @@ struct RawKey {
 };
 
 // Entry id of this lane's slot in tile t (-1: padding / out of range; the
-// window slots need no id).
-__device__ __forceinline__ int32_t slot_id(const AttnArgs& a, int64_t qi, int t, int t_end, int j) {
+// window slots need no id).  idx_q is the query's row of the index array.
+__device__ __forceinline__ int32_t slot_id(const int32_t* idx_q, int k, int t, int t_end, int j) {
   const int slot = t * AT_TILE + j;
-  if (t >= t_end || slot >= a.k) return -1;
-  return a.idx[qi * a.k + slot];
+  if (t >= t_end || slot >= k) return -1;
+  return idx_q[slot];
 }
 
+// wbase is the ring row of position p - 127 (mod win_cap, win_cap >= 128),
+// so window slot wi sits at row wbase + wi, wrapped at most once.
 __device__ __forceinline__ RawKey load_key(const AttnArgs& a, int t, int t_end, int j, int g, int w,
-                                           int32_t id, int32_t p, const uint8_t* codes_seq,
+                                           int32_t id, int32_t p, int64_t wbase, const uint8_t* codes_seq,
                                            const uint8_t* scales_seq, const uint8_t* win_seq) {
   RawKey r;
   r.a = make_uint4(0u, 0u, 0u, 0u);
@@ -94,9 +96,10 @@ __device__ __forceinline__ RawKey load_key(const AttnArgs& a, int t, int t_end, 
     }
   } else {
     const int wi = slot - a.k;
-    const int64_t wp = (int64_t)p - (NWIN - 1) + wi;
-    if (wi < NWIN && wp >= 0) {
-      const uint4* src = reinterpret_cast<const uint4*>(win_seq + (wp % a.win_cap) * D + AT_QCH * w + 32 * g);
+    if (wi < NWIN && p - (NWIN - 1) + wi >= 0) {
+      int64_t row = wbase + wi;
+      row = row >= a.win_cap ? row - a.win_cap : row;
+      const uint4* src = reinterpret_cast<const uint4*>(win_seq + row * D + AT_QCH * w + 32 * g);
       r.a = src[0];
       r.b = src[1];
       r.kind = 2;
@@ -176,13 +179,16 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int i = 0; i < 8; ++i) qraw[i] = src[i];
   }
+  const int32_t* idx_q = a.idx + qi * a.k;
+  int64_t wbase = ((int64_t)p - (NWIN - 1)) % a.win_cap;
+  wbase = wbase < 0 ? wbase + a.win_cap : wbase;
   int32_t id_ahead[AT_DEPTH];
 #pragma unroll
-  for (int i = 0; i < AT_DEPTH; ++i) id_ahead[i] = slot_id(a, qi, tile(AT_DEPTH + i), t_end, j);
+  for (int i = 0; i < AT_DEPTH; ++i) id_ahead[i] = slot_id(idx_q, a.k, tile(AT_DEPTH + i), t_end, j);
   RawKey ring[AT_DEPTH];
 #pragma unroll
   for (int i = 0; i < AT_DEPTH; ++i)
-    ring[i] = load_key(a, tile(i), t_end, j, g, w, slot_id(a, qi, tile(i), t_end, j), p,
+    ring[i] = load_key(a, tile(i), t_end, j, g, w, slot_id(idx_q, a.k, tile(i), t_end, j), p, wbase,
                        codes_seq, scales_seq, win_seq);
   f16x8 qf[4];
 #pragma unroll
@@ -202,11 +208,11 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
     const RawKey cur = ring[0];
 #pragma unroll
     for (int i = 0; i + 1 < AT_DEPTH; ++i) ring[i] = ring[i + 1];
-    ring[AT_DEPTH - 1] = load_key(a, tile(it + AT_DEPTH), t_end, j, g, w, id_ahead[0], p, codes_seq,
+    ring[AT_DEPTH - 1] = load_key(a, tile(it + AT_DEPTH), t_end, j, g, w, id_ahead[0], p, wbase, codes_seq,
                                   scales_seq, win_seq);
 #pragma unroll
     for (int i = 0; i + 1 < AT_DEPTH; ++i) id_ahead[i] = id_ahead[i + 1];
-    id_ahead[AT_DEPTH - 1] = slot_id(a, qi, tile(it + 2 * AT_DEPTH), t_end, j);
+    id_ahead[AT_DEPTH - 1] = slot_id(idx_q, a.k, tile(it + 2 * AT_DEPTH), t_end, j);
 
     // ---- 2. partial S^T over this wave's channels; slices to LDS row j ------
     __builtin_amdgcn_wave_barrier();   // the previous tile's LDS reads come first
