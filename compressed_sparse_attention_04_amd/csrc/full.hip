@@ -123,54 +123,67 @@ __global__ __launch_bounds__(FS_THREADS) void full_select_kernel(FullSelArgs a) 
     if (nv == 0) {   // nothing visible: every rescored slot is empty (and no row may be read)
       for (int i = tid; i < 16 * n_frag; i += FS_THREADS) sc[i] = -__builtin_huge_valf();
     } else {
-      // unconditional loads, an empty slot reading entry 0 (nv >= 1 here): its
-      // score is replaced by -inf below, and a column of an MFMA fragment
-      // affects only its own output column, so its bytes do not matter
-      auto load_frag = [&](int f, uint4& v0, uint4& v1) {
-        uint4 v[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int bi = 2 * f + h;
-          const int32_t blk = (f < n_frag && bi < K) ? top[bi] : -1;
-          const int64_t e = 8 * (int64_t)blk + (lane >> 3);
-          v[h] = load16<false>(kbase + ((blk >= 0 && e < nv) ? e : 0) * ID + 16 * stage_chunk(lane, h));
-        }
-        v0 = v[0];
-        v1 = v[1];
-      };
-      // groups of FS_GROUP fragments per wave, the next group's loads in flight
+      // Wave wv takes fragments f = wv + 16 i, i < n_mine, each two of the
+      // chosen blocks (halves).  Lane L < 2 n_mine keeps half L's block: its
+      // number of visible entries (cnt) and the block to read (row 0's block
+      // when it has none, so every load reads existing rows); every half
+      // reads them back as wave-uniform values.  Loads are unconditional and
+      // the groups of FS_GROUP fragments alternate between two register sets,
+      // so no register with a load in flight is copied.  32-bit: entries < 2^30.
       constexpr int FS_GROUP = 4;
-      const int n_mine = (n_frag - wv + FS_WAVES - 1) / FS_WAVES;
-      uint4 cur[FS_GROUP][2], nxt[FS_GROUP][2];
-#pragma unroll
-      for (int u = 0; u < FS_GROUP; ++u) load_frag(wv + FS_WAVES * u, cur[u][0], cur[u][1]);
-      for (int g0 = 0; g0 < n_mine; g0 += FS_GROUP) {
-        if (g0 + FS_GROUP < n_mine) {
-#pragma unroll
-          for (int u = 0; u < FS_GROUP; ++u)
-            load_frag(wv + FS_WAVES * (g0 + FS_GROUP + u), nxt[u][0], nxt[u][1]);
-        }
+      const int n_mine = (n_frag - wv + FS_WAVES - 1) / FS_WAVES;   // <= 32 (K <= 1,024)
+      int my_cnt = 0, my_blkc = 0;
+      {
+        const int f = wv + FS_WAVES * (lane >> 1), bi = 2 * f + (lane & 1);
+        const int32_t blk = ((lane >> 1) < n_mine && bi < K) ? top[bi] : -1;
+        const int rem = (int)nv - 8 * blk;
+        my_cnt = blk < 0 ? 0 : (rem <= 0 ? 0 : (rem >= 8 ? 8 : rem));
+        my_blkc = my_cnt > 0 ? blk : 0;
+      }
+      const int lrow_k = lane >> 3;
+      const uint32_t off_row[2] = {(uint32_t)(lrow_k * ID + 16 * stage_chunk(lane, 0)),
+                                   (uint32_t)(lrow_k * ID + 16 * stage_chunk(lane, 1))};
+      const uint32_t off_zero[2] = {(uint32_t)(16 * stage_chunk(lane, 0)), (uint32_t)(16 * stage_chunk(lane, 1))};
+      auto load_group = [&](int grp, uint4 (&v)[FS_GROUP][2]) {
 #pragma unroll
         for (int u = 0; u < FS_GROUP; ++u) {
-          const int f = wv + FS_WAVES * (g0 + u);
-          if (g0 + u >= n_mine) break;
+          const int i = grp * FS_GROUP + u;   // may pass n_mine: reads row 0, never used
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int hl = (2 * i + h) & 63;
+            const int cnt = __builtin_amdgcn_readlane(my_cnt, hl);
+            const uint8_t* base = kbase + (int64_t)__builtin_amdgcn_readlane(my_blkc, hl) * (8 * ID);
+            v[u][h] = load16<false>(base + (lrow_k < cnt ? off_row[h] : off_zero[h]));
+          }
+        }
+      };
+      auto compute_group = [&](int grp, const uint4 (&v)[FS_GROUP][2]) {
+#pragma unroll
+        for (int u = 0; u < FS_GROUP; ++u) {
+          const int i = grp * FS_GROUP + u;
+          if (i >= n_mine) break;   // wave-uniform
+          const int f = wv + FS_WAVES * i;
           __builtin_amdgcn_wave_barrier();
-          stage[lane] = cur[u][0];
-          stage[64 + lane] = cur[u][1];
+          stage[lane] = v[u][0];
+          stage[64 + lane] = v[u][1];
           __builtin_amdgcn_wave_barrier();
           const f32x4 acc = frag_mma(afrag, to_frag(read_staged(stage, lane)));
           const float sco = head_sum(acc, w4);
-          // lane n < 16 holds column n: entry 8 top[2 f + n / 8] + n % 8
-          const int bi = 2 * f + ((lane & 15) >> 3);
-          const int32_t blk = bi < K ? top[bi] : -1;
-          const int64_t e = 8 * (int64_t)blk + (lane & 7);
-          if (lane < 16) sc[16 * f + lane] = (blk >= 0 && e < nv) ? sco : -__builtin_huge_valf();
+          // lane n < 16 holds column n: entry n % 8 of half n / 8
+          const int c0 = __builtin_amdgcn_readlane(my_cnt, (2 * i) & 63);
+          const int c1 = __builtin_amdgcn_readlane(my_cnt, (2 * i + 1) & 63);
+          const int cnt = (lane & 8) ? c1 : c0;
+          if (lane < 16) sc[16 * f + lane] = (lane & 7) < cnt ? sco : -__builtin_huge_valf();
         }
-#pragma unroll
-        for (int u = 0; u < FS_GROUP; ++u) {
-          cur[u][0] = nxt[u][0];
-          cur[u][1] = nxt[u][1];
-        }
+      };
+      const int n_groups = (n_mine + FS_GROUP - 1) / FS_GROUP;
+      uint4 ra[FS_GROUP][2], rb[FS_GROUP][2];
+      load_group(0, ra);
+      for (int grp = 0; grp < n_groups; grp += 2) {
+        if (grp + 1 < n_groups) load_group(grp + 1, rb);
+        compute_group(grp, ra);
+        if (grp + 2 < n_groups) load_group(grp + 2, ra);
+        if (grp + 1 < n_groups) compute_group(grp + 1, rb);
       }
     }
   }
