@@ -145,6 +145,35 @@ def test_index_score_dense(n_seq, q_per_seq, n_entries, pos_base):
     assert worst <= 2e-6, worst
 
 
+def test_index_score_dense_scan_several_chunks_per_block():
+    """Decode-shaped scoring (fewer than 32 queries per sequence) where each
+    block streams several 1,024-column chunks (1,120 queries, 3 chunks, the
+    last one ragged), the launch shape of long-context decode."""
+    rng = np.random.default_rng(77)
+    n_seq, q_per_seq, n_entries = 70, 16, 2600
+    Q = n_seq * q_per_seq
+    q8, k8, w, _ = _scores_case(rng, n_seq, q_per_seq, n_entries, n_entries + 3, 0)
+    pos = rng.integers(4 * 2000, 4 * n_entries + 40, Q).astype(np.int32)   # partial and full visibility
+    scores, bm = ops.csa_index_score(t_(q8), t_(w), t_(pos), t_(k8), n_seq, q_per_seq, n_entries,
+                                     want_block_max=True)
+    torch.cuda.synchronize()
+    sc, bmg = np_(scores), np_(bm)
+    qv = formats.e4m3_decode(q8).astype(np.float64)
+    kv = formats.e4m3_decode(k8).astype(np.float64)
+    for s in range(n_seq):
+        rows = slice(s * q_per_seq, (s + 1) * q_per_seq)
+        dots = np.einsum("qhd,nd->qhn", qv[rows], kv[s, :n_entries])          # exact for E4M3 operands
+        ref = np.einsum("qh,qhn->qn", w[rows].astype(np.float64), np.maximum(dots, 0.0))
+        nv = np.minimum((pos[rows].astype(np.int64) + 1) // 4, n_entries)
+        vis = np.arange(n_entries)[None, :] < nv[:, None]
+        got = sc[rows]
+        assert np.all(np.abs(got - ref)[vis] <= 2e-6 * np.maximum(1.0, np.abs(ref[vis])))
+        assert np.all(np.isneginf(got[~vis]))
+        pad = np.full((q_per_seq, bmg.shape[1] * 8), -np.inf, np.float32)
+        pad[:, :n_entries] = got
+        assert np.array_equal(bmg[rows], pad.reshape(q_per_seq, -1, 8).max(axis=2))
+
+
 @pytest.mark.parametrize("n_seq,q_per_seq", [(2, 40), (3, 100)])
 def test_index_score_ragged_tiles_stay_in_bounds(n_seq, q_per_seq):
     """Prefill tiles hold 64 queries; a sequence whose query count is not a
