@@ -133,6 +133,12 @@ __device__ __forceinline__ f16x8 key_slice(const RawKey& r, int s) {
 // and O is rarely rescaled.
 constexpr float AT_RESCALE = 8.0f;
 
+// 2^x on the transcendental unit alone (v_exp_f32, ~1 ulp): the loop's
+// arguments are <= AT_RESCALE or -inf (-> 0), and a weight that underflows to
+// 0 is below anything the fp32 sums could hold, so the denormal range
+// handling of exp2f is not needed there.
+__device__ __forceinline__ float exp2_loop(float x) { return __builtin_amdgcn_exp2f(x); }
+
 template <int KG>
 struct AttnLds {
   union {
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
     const bool first = (m_run == -__builtin_huge_valf());
     const bool move = !first && (mx > m_run + AT_RESCALE);
     if (__ballot(move)) {
-      const float alpha = move ? exp2f(m_run - mx) : 1.0f;
+      const float alpha = move ? exp2_loop(m_run - mx) : 1.0f;
       l_run *= alpha;
       float al[4];
 #pragma unroll
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
     float pr[4], psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      pr[r] = exp2f(x[r] - base);
+      pr[r] = exp2_loop(x[r] - base);
       psum += pr[r];
     }
     psum = sum_xor32(sum_xor16(psum));
