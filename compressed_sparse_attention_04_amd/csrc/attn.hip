@@ -196,12 +196,15 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
   for (int i = 0; i < AT_DEPTH; ++i)
     ring[i] = load_key(a, tile(i), t_end, j, g, w, slot_id(idx_q, a.k, tile(i), t_end, j), p, wbase,
                        codes_seq, scales_seq, win_seq);
+  // Q carries the logit scale (sm_scale * log2 e), so S is already in the
+  // log2 domain of the softmax
   f16x8 qf[4];
+  const float cq = a.c_log2;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const float4 x = qraw[2 * s], y = qraw[2 * s + 1];
-    qf[s] = f16x8{(_Float16)x.x, (_Float16)x.y, (_Float16)x.z, (_Float16)x.w,
-                  (_Float16)y.x, (_Float16)y.y, (_Float16)y.z, (_Float16)y.w};
+    qf[s] = f16x8{(_Float16)(x.x * cq), (_Float16)(x.y * cq), (_Float16)(x.z * cq), (_Float16)(x.w * cq),
+                  (_Float16)(y.x * cq), (_Float16)(y.y * cq), (_Float16)(y.z * cq), (_Float16)(y.w * cq)};
   }
 
   f32x4 acc_o[8];
@@ -241,14 +244,12 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
 
     // ---- 3. online softmax (lane: keys 4g+r, head j), lazy rescaling --------
     const uint32_t vmask = (uint32_t)(__ballot(cur.kind != 0) & 0xFFFFull);
-    float x[4];
-    float mx = -__builtin_huge_valf();
+    float x[4] = {S[0], S[1], S[2], S[3]};
+    if (vmask != 0xFFFFu) {   // wave-uniform: only tiles with an absent key mask
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool ok = (vmask >> (4 * g + r)) & 1u;
-      x[r] = ok ? S[r] * a.c_log2 : -__builtin_huge_valf();
-      mx = fmaxf(mx, x[r]);
+      for (int r = 0; r < 4; ++r) x[r] = ((vmask >> (4 * g + r)) & 1u) ? x[r] : -__builtin_huge_valf();
     }
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = max_xor32(max_xor16(mx));
     const bool first = (m_run == -__builtin_huge_valf());
     const bool move = !first && (mx > m_run + AT_RESCALE);
