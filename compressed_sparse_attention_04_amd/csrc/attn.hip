@@ -273,8 +273,7 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
       pr[r] = exp2_loop(x[r] - base);
       psum += pr[r];
     }
-    psum = sum_xor32(sum_xor16(psum));
-    l_run += psum;
+    l_run += psum;   // this lane's keys only; the four lanes of head j are summed after the loop
     const f16x4 pa = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
 
     // ---- 4. P V: gather keys 4g .. 4g+3 of channels 8j .. 8j+7 from LDS ---------
@@ -299,6 +298,8 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
       acc_o[2 * i + 1] = mfma_f16_16x16x16(pa, bhi, acc_o[2 * i + 1]);
     }
   }
+
+  l_run = sum_xor32(sum_xor16(l_run));   // head j's sum over all keys of this group
 
   // ---- merge the key groups: O, max and sum per head over the groups --------
   // lane holds O[head 4g + r][channel 128 w + 8 j + n]; m_run, l_run are head j's
