@@ -123,6 +123,17 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v_out), srs, vo, 0, 0);
     }
   };
+  if (nv == 0) {
+    // nothing visible: every column is -inf, and no key row may be read (the
+    // key array can be empty)
+#pragma unroll
+    for (int f = 0; f < NFRAG; ++f) {
+      const int col = cw + 16 * f + (lane & 15);
+      const uint32_t vo = (lane < 16 && col < ncols_i) ? (uint32_t)col * 4u : OOB;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-__builtin_huge_valf()), srs, vo, 0, 0);
+    }
+    return;
+  }
   uint4 ra[SQ_UNROLL][2], rb[SQ_UNROLL][2];
   load_group(0, ra);
 #pragma unroll
