@@ -67,9 +67,13 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
   // visible entries (cnt) and the block to read (row 0's block when it has
   // none, so every load reads existing rows); every half reads them back as
   // wave-uniform values.  32-bit: entries < 2^30.
+  // (a block id outside the visible entries, or a bogus one from the caller,
+  // has no visible entry; the test comes before the multiply, so 8 * id
+  // stays below 2^30)
   const int nv_i = (int)nv;
-  const int rem = nv_i - 8 * my_blk;
-  const int my_cnt = my_blk < 0 ? 0 : (rem <= 0 ? 0 : (rem >= 8 ? 8 : rem));
+  const bool in_range = my_blk >= 0 && my_blk <= (nv_i >> 3);
+  const int rem = in_range ? nv_i - 8 * my_blk : 0;
+  const int my_cnt = rem <= 0 ? 0 : (rem >= 8 ? 8 : rem);
   const int my_blkc = my_cnt > 0 ? my_blk : 0;
   struct Half { int cnt; const uint8_t* base; };
   auto half_cnt = [&](int i) { return __builtin_amdgcn_readlane(my_cnt, i); };
