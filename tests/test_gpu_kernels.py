@@ -401,6 +401,29 @@ def test_window_rebuild_then_append_matches_rebuild_later():
     assert torch.equal(a, b)
 
 
+def test_index_score_pooled_ids_beyond_entries():
+    """Pool ids whose entries lie at or past n_entries score -inf (a partly
+    valid last block keeps its valid entries), including ids so large that
+    8 * id does not fit 32 bits; valid blocks match the oracle."""
+    rng = np.random.default_rng(21)
+    n_seq, n_entries = 2, 1001                     # block 125 holds entry 1000 only
+    q8, k8, w, pos = _scores_case(rng, n_seq, 1, n_entries, n_entries + 3, 4 * 1100)
+    pool = np.array([[0, 5, 125, 126, 4000, (1 << 30) - 1, -1, -1],
+                     [3, 7, 125, (1 << 28) + 1, 2 ** 31 - 1, -1, -1, -1]], np.int32)
+    sc, _ = ops.csa_index_score(t_(q8), t_(w), t_(pos), t_(k8), n_seq, 1, n_entries, pool_blocks=t_(pool))
+    torch.cuda.synchronize()
+    got = np_(sc)
+    for s in range(n_seq):
+        ref = oracle.index_scores(q8[s], w[s], k8[s, :n_entries])
+        for c in range(8 * pool.shape[1]):
+            b = int(pool[s, c // 8])
+            e = 8 * b + c % 8
+            if b < 0 or e >= n_entries:
+                assert np.isneginf(got[s, c]), (s, c, b)
+            else:
+                assert abs(got[s, c] - ref[e]) <= 2e-6 * max(1.0, abs(ref[e])), (s, c, b)
+
+
 def test_index_score_pooled_nothing_visible():
     """Pooled scoring with no visible entry (no entries at all, or a query
     before the first complete entry): every column is -inf."""
