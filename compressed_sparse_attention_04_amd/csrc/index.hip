@@ -75,12 +75,15 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
   const int rem = in_range ? nv_i - 8 * my_blk : 0;
   const int my_cnt = rem <= 0 ? 0 : (rem >= 8 ? 8 : rem);
   const int my_blkc = my_cnt > 0 ? my_blk : 0;
+  // one word per half (block id < 2^27 above the count), one readlane each
+  const int my_pack = (my_blkc << 4) | my_cnt;
   struct Half { int cnt; const uint8_t* base; };
   auto half_cnt = [&](int i) { return __builtin_amdgcn_readlane(my_cnt, i); };
   auto half_info = [&](int i) {
+    const int pk = __builtin_amdgcn_readlane(my_pack, i);
     Half hf;
-    hf.cnt = half_cnt(i);
-    hf.base = kbase + (int64_t)__builtin_amdgcn_readlane(my_blkc, i) * (8 * ID);
+    hf.cnt = pk & 15;
+    hf.base = kbase + (int64_t)(pk >> 4) * (8 * ID);
     return hf;
   };
   // lane's byte offsets inside a half: row lane / 8, whole-line chunk of half h
