@@ -68,6 +68,16 @@ struct RawKey {
   int32_t kind;
 };
 
+// Tile kinds, wave-uniform: all slots selected entries, all window slots, or
+// both (only when k is not a multiple of the tile, in the one tile holding
+// slot k).  Padding slots are kind 0 and fit every tile kind.
+constexpr int TK_ENTRY = 0, TK_WINDOW = 1, TK_MIXED = 2;
+// Kind of tile t (t * AT_TILE is the same in every lane).
+__device__ __forceinline__ int tile_kind(int t, int k) {
+  const int slot0 = t * AT_TILE;
+  return slot0 + AT_TILE <= k ? TK_ENTRY : slot0 >= k ? TK_WINDOW : TK_MIXED;
+}
+
 // Entry id of this lane's slot in tile t (-1: padding / out of range; the
 // window slots need no id).  idx_q is the query's row of the index array.
 __device__ __forceinline__ int32_t slot_id(const int32_t* idx_q, int k, int t, int t_end, int j) {
@@ -78,6 +88,9 @@ __device__ __forceinline__ int32_t slot_id(const int32_t* idx_q, int k, int t, i
 
 // wbase is the ring row of position p - 127 (mod win_cap, win_cap >= 128),
 // so window slot wi sits at row wbase + wi, wrapped at most once.
+// TK (see below) is the kind of tile t, the same for every lane: an entry
+// tile loads no window bytes and a window tile no entry bytes.
+template <int TK>
 __device__ __forceinline__ RawKey load_key(const AttnArgs& a, int t, int t_end, int j, int g, int w,
                                            int32_t id, int32_t p, int64_t wbase, const uint8_t* codes_seq,
                                            const uint8_t* scales_seq, const uint8_t* win_seq) {
@@ -88,7 +101,8 @@ __device__ __forceinline__ RawKey load_key(const AttnArgs& a, int t, int t_end, 
   r.kind = 0;
   if (t >= t_end) return r;
   const int slot = t * AT_TILE + j;
-  if (slot < a.k) {
+  const bool entry_slot = (TK == TK_ENTRY) ? true : (TK == TK_WINDOW) ? false : slot < a.k;
+  if (entry_slot) {
     if (id >= 0 && id < a.kv_rows) {
       r.a = *reinterpret_cast<const uint4*>(codes_seq + (int64_t)id * CODE_BYTES + 64 * w + 16 * g);
       r.sc = *reinterpret_cast<const uint16_t*>(scales_seq + (int64_t)id * SCALE_BYTES + 8 * w + 2 * g);
@@ -109,15 +123,17 @@ __device__ __forceinline__ RawKey load_key(const AttnArgs& a, int t, int t_end, 
 }
 
 // Channels 8 s .. 8 s + 7 of the lane's 32 as fp16 (exact), k-step s < 4.
-// Entry: code dword s (two channels per byte) times the scale of group s / 2;
-// window: E4M3 bytes 8 s .. 8 s + 7.
-__device__ __forceinline__ f16x8 key_slice(const RawKey& r, int s) {
+// Window token: E4M3 bytes 8 s .. 8 s + 7.  Entry: code dword s (two
+// channels per byte) times the scale of group s / 2.  A key of kind 0 has
+// all bytes zero and gives +0 either way.
+__device__ __forceinline__ f16x8 window_slice(const RawKey& r, int s) {
   const uint32_t wd[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
-  if (r.kind == 2) {
-    const f16x2 a = fp8x2_to_f16<0>(wd[2 * s]), b = fp8x2_to_f16<1>(wd[2 * s]);
-    const f16x2 c = fp8x2_to_f16<0>(wd[2 * s + 1]), d = fp8x2_to_f16<1>(wd[2 * s + 1]);
-    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-  }
+  const f16x2 a = fp8x2_to_f16<0>(wd[2 * s]), b = fp8x2_to_f16<1>(wd[2 * s]);
+  const f16x2 c = fp8x2_to_f16<0>(wd[2 * s + 1]), d = fp8x2_to_f16<1>(wd[2 * s + 1]);
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+__device__ __forceinline__ f16x8 entry_slice(const RawKey& r, int s) {
+  const uint32_t wd[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
   const f16x2 sc2 = fp8x2_to_f16<0>(r.sc);
   const _Float16 scale = (s < 2) ? sc2[0] : sc2[1];
   const f16x2 sp = f16x2{scale, scale};
@@ -125,6 +141,12 @@ __device__ __forceinline__ f16x8 key_slice(const RawKey& r, int s) {
   const f16x2 a = fp4x2_to_f16<0>(cw) * sp, b = fp4x2_to_f16<1>(cw) * sp;
   const f16x2 c = fp4x2_to_f16<2>(cw) * sp, d = fp4x2_to_f16<3>(cw) * sp;
   return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+template <int TK>
+__device__ __forceinline__ f16x8 key_slice(const RawKey& r, int s) {
+  if constexpr (TK == TK_ENTRY) return entry_slice(r, s);
+  else if constexpr (TK == TK_WINDOW) return window_slice(r, s);
+  else return r.kind == 2 ? window_slice(r, s) : entry_slice(r, s);
 }
 
 // Rescale threshold of the online softmax (log2 units): the running reference
@@ -158,7 +180,10 @@ template <int KG>
 __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu(4))) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnLds<KG> lds;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = (tid >> 6) & (AT_WAVES - 1), kg = tid >> 8;
+  const int lane = tid & 63, w = (tid >> 6) & (AT_WAVES - 1);
+  // the key group is wave-uniform: taken from lane 0, so the tile index and
+  // every branch on it are scalar
+  const int kg = __builtin_amdgcn_readfirstlane(tid >> 8);
   const int j = lane & 15;      // key slot (loads, S rows), head (Q, softmax), channel group (P V)
   const int g = lane >> 4;      // 32-channel group (loads), key group of 4 (S, P)
   const int64_t qi = blockIdx.y;
@@ -192,10 +217,15 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
   for (int i = 0; i < AT_DEPTH; ++i) id_ahead[i] = slot_id(idx_q, a.k, tile(AT_DEPTH + i), t_end, j);
   RawKey ring[AT_DEPTH];
+  // loads of tile t, dispatched on its kind (a scalar branch)
+  auto issue = [&](int t, int32_t id) -> RawKey {
+    const int tk = tile_kind(t, a.k);
+    if (tk == TK_ENTRY) return load_key<TK_ENTRY>(a, t, t_end, j, g, w, id, p, wbase, codes_seq, scales_seq, win_seq);
+    if (tk == TK_WINDOW) return load_key<TK_WINDOW>(a, t, t_end, j, g, w, id, p, wbase, codes_seq, scales_seq, win_seq);
+    return load_key<TK_MIXED>(a, t, t_end, j, g, w, id, p, wbase, codes_seq, scales_seq, win_seq);
+  };
 #pragma unroll
-  for (int i = 0; i < AT_DEPTH; ++i)
-    ring[i] = load_key(a, tile(i), t_end, j, g, w, slot_id(idx_q, a.k, tile(i), t_end, j), p, wbase,
-                       codes_seq, scales_seq, win_seq);
+  for (int i = 0; i < AT_DEPTH; ++i) ring[i] = issue(tile(i), slot_id(idx_q, a.k, tile(i), t_end, j));
   // Q carries the logit scale (sm_scale * log2 e), so S is already in the
   // log2 domain of the softmax
   f16x8 qf[4];
@@ -217,8 +247,7 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
     const RawKey cur = ring[0];
 #pragma unroll
     for (int i = 0; i + 1 < AT_DEPTH; ++i) ring[i] = ring[i + 1];
-    ring[AT_DEPTH - 1] = load_key(a, tile(it + AT_DEPTH), t_end, j, g, w, id_ahead[0], p, wbase, codes_seq,
-                                  scales_seq, win_seq);
+    ring[AT_DEPTH - 1] = issue(tile(it + AT_DEPTH), id_ahead[0]);
 #pragma unroll
     for (int i = 0; i + 1 < AT_DEPTH; ++i) id_ahead[i] = id_ahead[i + 1];
     id_ahead[AT_DEPTH - 1] = slot_id(idx_q, a.k, tile(it + 2 * AT_DEPTH), t_end, j);
@@ -226,12 +255,19 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
     // ---- 2. partial S^T over this wave's channels; slices to LDS row j ------
     __builtin_amdgcn_wave_barrier();   // the previous tile's LDS reads come first
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    auto qk = [&](auto tk) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const f16x8 av = key_slice(cur, s);
-      *reinterpret_cast<f16x8*>(krow + j * AT_KPITCH + 64 * g + 16 * s) = av;
-      sacc = mfma_f16_16x16x32(av, qf[s], sacc);
-    }
+      for (int s = 0; s < 4; ++s) {
+        const f16x8 av = key_slice<decltype(tk)::value>(cur, s);
+        *reinterpret_cast<f16x8*>(krow + j * AT_KPITCH + 64 * g + 16 * s) = av;
+        sacc = mfma_f16_16x16x32(av, qf[s], sacc);
+      }
+    };
+    // one conversion per tile kind
+    const int tk = tile_kind(tile(it), a.k);
+    if (tk == TK_ENTRY) qk(std::integral_constant<int, TK_ENTRY>{});
+    else if (tk == TK_WINDOW) qk(std::integral_constant<int, TK_WINDOW>{});
+    else qk(std::integral_constant<int, TK_MIXED>{});
     const int par = it & 1;
     lds.loop.s[par][kg][w][lane] = sacc;
     __syncthreads();
