@@ -22,7 +22,7 @@
 //      lane can gather 4 keys of one channel for the B operand of P V
 //      (8 x v_mfma 16x16x16).  Output channel of N-tile n in lane column c is
 //      128 w + 8 c + n, so every lane reads 16 contiguous bytes per key.
-// Key bytes are loaded AT_DEPTH tiles ahead of use and slot ids 2 AT_DEPTH
+// Key bytes are loaded at_depth tiles ahead of use and slot ids 2 at_depth
 // tiles ahead.  The key groups of a block merge their (O, max, sum) through
 // LDS at the end, so a split writes one partial however many groups it has;
 // with several splits per query the partials are combined by
@@ -37,7 +37,11 @@ constexpr int AT_WAVES = 4;                      // waves of one key group
 constexpr int AT_THREADS = 64 * AT_WAVES;
 constexpr int AT_QCH = D / AT_WAVES;             // channels per wave
 constexpr int AT_KPITCH = AT_QCH * 2 + 16;       // bytes per LDS key row of one wave (fp16 + pad)
-constexpr int AT_DEPTH = 2;                      // tiles of key bytes in flight
+// Tiles of key bytes in flight: two with several key groups per block (few
+// blocks, so the loads' latency shows), one with a single group (four
+// waves per SIMD, whose interleaving covers the latency of one tile ahead;
+// one register set fewer to rotate).
+template <int KG> constexpr int at_depth() { return KG == 1 ? 1 : 2; }
 
 struct AttnArgs {
   const float* q;
@@ -184,6 +188,7 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
   // the key group is wave-uniform: taken from lane 0, so the tile index and
   // every branch on it are scalar
   const int kg = __builtin_amdgcn_readfirstlane(tid >> 8);
+  constexpr int AT_DEPTH = at_depth<KG>();
   const int j = lane & 15;      // key slot (loads, S rows), head (Q, softmax), channel group (P V)
   const int g = lane >> 4;      // 32-channel group (loads), key group of 4 (S, P)
   const int64_t qi = blockIdx.y;
