@@ -169,11 +169,13 @@ __global__ __launch_bounds__(FS_THREADS) void full_select_kernel(FullSelArgs a) 
           __builtin_amdgcn_wave_barrier();
           const f32x4 acc = frag_mma(afrag, to_frag(read_staged(stage, lane)));
           const float sco = head_sum(acc, w4);
-          // lane n < 16 holds column n: entry n % 8 of half n / 8
-          const int c0 = __builtin_amdgcn_readlane(my_cnt, (2 * i) & 63);
-          const int c1 = __builtin_amdgcn_readlane(my_cnt, (2 * i + 1) & 63);
-          const int cnt = (lane & 8) ? c1 : c0;
-          if (lane < 16) sc[16 * f + lane] = (lane & 7) < cnt ? sco : -__builtin_huge_valf();
+          // lane n < 16 holds column n: entry n % 8 of half n / 8, valid when
+          // n % 8 is below that half's visible count (<= 8): bit n of a
+          // wave-uniform mask built on the scalar unit
+          const uint32_t c0 = __builtin_amdgcn_readlane(my_cnt, (2 * i) & 63);
+          const uint32_t c1 = __builtin_amdgcn_readlane(my_cnt, (2 * i + 1) & 63);
+          const uint32_t m16 = ((1u << c0) - 1u) | (((1u << c1) - 1u) << 8);
+          if (lane < 16) sc[16 * f + lane] = __builtin_amdgcn_inverse_ballot_w64((uint64_t)m16) ? sco : -__builtin_huge_valf();
         }
       };
       const int n_groups = (n_mine + FS_GROUP - 1) / FS_GROUP;

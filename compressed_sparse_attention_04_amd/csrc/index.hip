@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
   // one word per half (block id < 2^27 above the count), one readlane each
   const int my_pack = (my_blkc << 4) | my_cnt;
   struct Half { int cnt; const uint8_t* base; };
-  auto half_cnt = [&](int i) { return __builtin_amdgcn_readlane(my_cnt, i); };
+  auto half_cnt = [&](int i) { return __builtin_amdgcn_readlane(my_pack, i) & 15; };
   auto half_info = [&](int i) {
     const int pk = __builtin_amdgcn_readlane(my_pack, i);
     Half hf;
@@ -111,6 +111,12 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
       0x00020000);
   const int ncols_i = (int)ncols;                     // <= 8 x 65,536
   const int cw = (int)c_wave;
+  // Lanes 0-15 own output column cw + 16 f + lane of fragment f: byte offset
+  // vo0 + 64 f.  A column at or past ncols is past the view's records and its
+  // store is dropped (the range check covers the instruction's immediate
+  // offset, where the constant 64 f goes); the other lanes' offset stays past
+  // the records for every f.
+  const uint32_t vo0 = lane < 16 ? (uint32_t)(cw + lane) * 4u : OOB;
   auto compute_group = [&](int grp, const uint4 (&v)[SQ_UNROLL][2]) {
 #pragma unroll
     for (int u = 0; u < SQ_UNROLL; ++u) {
@@ -121,13 +127,12 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
       __builtin_amdgcn_wave_barrier();   // stores before the transposed reads (LDS keeps wave order)
       const f32x4 acc = frag_mma(afrag, to_frag(read_staged(stage, lane)));
       const float sc = head_sum(acc, w4);
-      // lane's output column cw + 16 f + lane % 16 (lanes 0-15 own it): valid
-      // when its offset in the pool block is below the block's visible count
-      const int col = cw + 16 * f + (lane & 15);
-      const int cnt = (lane & 8) ? half_cnt(2 * f + 1) : half_cnt(2 * f);
-      const float v_out = (lane & 7) < cnt ? sc : -__builtin_huge_valf();
-      const uint32_t vo = (lane < 16 && col < ncols_i) ? (uint32_t)col * 4u : OOB;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v_out), srs, vo, 0, 0);
+      // valid when the column's offset in its pool block (lane % 8) is below
+      // that block's visible count: bit lane of a wave-uniform mask built
+      // from the two halves' counts (<= 8) on the scalar unit
+      const uint32_t m16 = ((1u << half_cnt(2 * f)) - 1u) | (((1u << half_cnt(2 * f + 1)) - 1u) << 8);
+      const float v_out = __builtin_amdgcn_inverse_ballot_w64((uint64_t)m16) ? sc : -__builtin_huge_valf();
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v_out), srs, vo0 + 64u * (uint32_t)f, 0, 0);
     }
   };
   if (nv == 0) {
