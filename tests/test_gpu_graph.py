@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import workloads as W
-from compressed_sparse_attention_04_amd.step import from_workload
+from compressed_sparse_attention_04_amd.step import from_schedule, from_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -68,5 +68,41 @@ def test_graph_replay_matches_eager(cfg):
         assert torch.equal(ref[2], got[2]) and torch.equal(ref[3], got[3]), (cfg.name, rep, "new entries")
         assert torch.equal(ref[4], got[4]), (cfg.name, rep, "window rings")
         _ = torch.randn(1 << 20, device="cuda").sum().item()     # eager work between replays
+    del g
+    torch.cuda.synchronize()
+
+
+def test_graph_replay_schedule_matches_eager():
+    """The 38-layer schedule (four groups, each with its own global KV and
+    windows) captured as one graph: every replay from the pre-step state
+    matches the eager step bit for bit."""
+    cfgs = W.v41_schedule("decode", n_seq=2, ctx_tokens=4 * 1500, cid=420)
+    wls = [W.make_workload(c, device="cuda") for c in cfgs]
+    sch = from_schedule(wls)
+    sch.setup()
+    for st in sch.groups:
+        rows = slice(st.prior, st.prior + st.new)
+        st.codes[:, rows].zero_()
+        st.scales[:, rows].zero_()
+    torch.cuda.synchronize()
+    pres = [(st.codes.clone(), st.scales.clone(), st.win_all.clone()) for st in sch.groups]
+    sch.step()
+    torch.cuda.synchronize()
+    refs = [snapshot(st) for st in sch.groups]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sch.step()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for st, pre in zip(sch.groups, pres):
+            restore(st, pre)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for gi, (st, ref) in enumerate(zip(sch.groups, refs)):
+            got = snapshot(st)
+            assert all(torch.equal(a, b) for a, b in zip(ref[0], got[0])), (gi, rep, "attention output")
+            assert all(torch.equal(a, b) for a, b in zip(ref[1], got[1])), (gi, rep, "indices")
+            assert torch.equal(ref[4], got[4]), (gi, rep, "window rings")
     del g
     torch.cuda.synchronize()
