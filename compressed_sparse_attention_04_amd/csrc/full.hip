@@ -12,7 +12,9 @@
 // with the scan's own arithmetic (the same fragments and fp32 sums, so the
 // same bits) and selects among them.
 //
-// One 1024-thread block per query:
+// One block per query (1,024 threads, or 512 for many queries with top_k <=
+// 512: about 68 KB of LDS, so two blocks share a compute unit and overlap
+// each other's barriers and memory waits):
 //   A. pool = the NB best blocks (ascending ids, -1 padded); when the pool is
 //      larger than top_k, the top_k best blocks are selected from the pool's
 //      own block maxima;
@@ -31,7 +33,6 @@ using namespace sel;
 using namespace idxf;
 
 constexpr int FS_THREADS = 1024;
-constexpr int FS_WAVES = FS_THREADS / 64;
 constexpr int FS_KMAX = 1024;     // top_k handled here (8 top_k entries are rescored)
 
 struct FullSelArgs {
@@ -49,13 +50,20 @@ struct FullSelArgs {
   int64_t k_rows, n_entries;
 };
 
-template <int PER, int PER2>   // block maxima per thread; rescored entries per thread
-__global__ __launch_bounds__(FS_THREADS) void full_select_kernel(FullSelArgs a) {
+// NT threads; block maxima per thread; rescored entries per thread; top_k
+// bound (8 KMAX rescored scores in LDS).  The pool (phase A) and the key
+// staging (phase B) are never live together and share their LDS.
+template <int NT, int PER, int PER2, int KMAX>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void full_select_kernel(FullSelArgs a) {
+  constexpr int FS_WAVES = NT / 64;
   __shared__ SelShared s;
-  __shared__ int32_t pool[SEL_POOL_MAX];
-  __shared__ int32_t top[FS_KMAX];
-  __shared__ float sc[8 * FS_KMAX];
-  __shared__ uint4 stage_all[FS_WAVES][128];
+  __shared__ union {
+    int32_t pool[SEL_POOL_MAX];
+    uint4 stage_all[FS_WAVES][128];
+  } ps;
+  __shared__ int32_t top[KMAX];
+  __shared__ float sc[8 * KMAX];
+  int32_t* pool = ps.pool;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t q = blockIdx.y;
   const int NB = a.NB, K = a.K;
@@ -67,11 +75,11 @@ __global__ __launch_bounds__(FS_THREADS) void full_select_kernel(FullSelArgs a) 
     {
       uint32_t key[PER];
       load_keys<PER>(row, pw, (int)a.nblk, key);
-      const uint32_t n_pool = block_select<FS_THREADS, PER>(s, key, (uint32_t)NB, [&](int p, uint32_t, uint32_t slot) {
+      const uint32_t n_pool = block_select<NT, PER>(s, key, (uint32_t)NB, [&](int p, uint32_t, uint32_t slot) {
         pool[slot] = p;
         if (a.pool_out) a.pool_out[q * NB + slot] = p;
       });
-      for (int j = (int)n_pool + tid; j < NB; j += FS_THREADS) {
+      for (int j = (int)n_pool + tid; j < NB; j += NT) {
         pool[j] = -1;
         if (a.pool_out) a.pool_out[q * NB + j] = -1;
       }
@@ -80,7 +88,7 @@ __global__ __launch_bounds__(FS_THREADS) void full_select_kernel(FullSelArgs a) 
       // the top_k blocks are among the pool: select them from the pool's own
       // block maxima (pool order is id order, so ties still go to lower ids)
       __syncthreads();   // pool is complete
-      constexpr int PP = SEL_POOL_MAX / FS_THREADS;
+      constexpr int PP = SEL_POOL_MAX / NT;
       const int pp = 64 * PP * wv + lane;
       uint32_t key[PP];
       {
@@ -96,13 +104,13 @@ __global__ __launch_bounds__(FS_THREADS) void full_select_kernel(FullSelArgs a) 
 #pragma unroll
         for (int u = 0; u < PP; ++u) key[u] = b[u] >= 0 ? select_key(v[u]) : 0u;
       }
-      const uint32_t n_top = block_select<FS_THREADS, PP>(s, key, (uint32_t)K, [&](int i, uint32_t, uint32_t slot) {
+      const uint32_t n_top = block_select<NT, PP>(s, key, (uint32_t)K, [&](int i, uint32_t, uint32_t slot) {
         top[slot] = pool[i];
       });
-      for (int j = (int)n_top + tid; j < K; j += FS_THREADS) top[j] = -1;
+      for (int j = (int)n_top + tid; j < K; j += NT) top[j] = -1;
     } else {
       __syncthreads();   // pool is complete
-      for (int j = tid; j < K; j += FS_THREADS) top[j] = pool[j];
+      for (int j = tid; j < K; j += NT) top[j] = pool[j];
     }
   }
   __syncthreads();
@@ -118,10 +126,10 @@ __global__ __launch_bounds__(FS_THREADS) void full_select_kernel(FullSelArgs a) 
 #pragma unroll
     for (int r = 0; r < 4; ++r) w4[r] = (lane < 32) ? a.w[q * IH + 4 * (lane >> 4) + r] : 0.f;
     const uint8_t* kbase = a.k_fp8 + seq * a.k_rows * ID;
-    uint4* stage = stage_all[wv];
+    uint4* stage = ps.stage_all[wv];
     const int n_frag = (K + 1) / 2;   // two blocks per 16-entry fragment; wave wv takes f = wv + 16 i
     if (nv == 0) {   // nothing visible: every rescored slot is empty (and no row may be read)
-      for (int i = tid; i < 16 * n_frag; i += FS_THREADS) sc[i] = -__builtin_huge_valf();
+      for (int i = tid; i < 16 * n_frag; i += NT) sc[i] = -__builtin_huge_valf();
     } else {
       // Wave wv takes fragments f = wv + 16 i, i < n_mine, each two of the
       // chosen blocks (halves).  Lane L < 2 n_mine keeps half L's block: its
@@ -200,10 +208,10 @@ __global__ __launch_bounds__(FS_THREADS) void full_select_kernel(FullSelArgs a) 
     for (int u = 0; u < PER2; ++u) key[u] = select_key(sc[pw + 64 * u < n ? pw + 64 * u : 0]);
 #pragma unroll
     for (int u = 0; u < PER2; ++u) key[u] = pw + 64 * u < n ? key[u] : 0u;
-    const uint32_t n_sel = block_select<FS_THREADS, PER2>(s, key, (uint32_t)K, [&](int p, uint32_t, uint32_t slot) {
+    const uint32_t n_sel = block_select<NT, PER2>(s, key, (uint32_t)K, [&](int p, uint32_t, uint32_t slot) {
       a.idx[q * K + slot] = 8 * top[p >> 3] + (p & 7);
     });
-    for (int j = (int)n_sel + tid; j < K; j += FS_THREADS) a.idx[q * K + j] = -1;
+    for (int j = (int)n_sel + tid; j < K; j += NT) a.idx[q * K + j] = -1;
   }
 }
 
@@ -217,12 +225,19 @@ hipError_t launch_full_select(const float* block_max, int64_t nblk, int64_t Q, i
                               hipStream_t st) {
   if (Q == 0) return hipSuccess;
   FullSelArgs a{block_max, nblk, nb, pool, k, idx, q_fp8, w, q_pos, q_per_seq, k_fp8, k_rows, n_entries};
-  const dim3 grid(1, (unsigned)Q), blk(FS_THREADS);
+  const dim3 grid(1, (unsigned)Q);
+  // many queries: 512-thread blocks, two per compute unit (top_k <= 512,
+  // nblk <= 16,384); a few queries: 1,024 threads, the shortest block
+  if (Q >= 512 && k <= 512 && nblk <= 512 * 32) {
+    hipLaunchKernelGGL((full_select_kernel<512, 32, 8, 512>), grid, dim3(512), 0, st, a);
+    return hipGetLastError();
+  }
+  const dim3 blk(FS_THREADS);
   const bool big1 = nblk > FS_THREADS * 16, big2 = 8 * (int64_t)k > FS_THREADS * 4;
-  if (!big1 && !big2) hipLaunchKernelGGL((full_select_kernel<16, 4>), grid, blk, 0, st, a);
-  else if (!big1) hipLaunchKernelGGL((full_select_kernel<16, 8>), grid, blk, 0, st, a);
-  else if (!big2) hipLaunchKernelGGL((full_select_kernel<32, 4>), grid, blk, 0, st, a);
-  else hipLaunchKernelGGL((full_select_kernel<32, 8>), grid, blk, 0, st, a);
+  if (!big1 && !big2) hipLaunchKernelGGL((full_select_kernel<FS_THREADS, 16, 4, FS_KMAX>), grid, blk, 0, st, a);
+  else if (!big1) hipLaunchKernelGGL((full_select_kernel<FS_THREADS, 16, 8, FS_KMAX>), grid, blk, 0, st, a);
+  else if (!big2) hipLaunchKernelGGL((full_select_kernel<FS_THREADS, 32, 4, FS_KMAX>), grid, blk, 0, st, a);
+  else hipLaunchKernelGGL((full_select_kernel<FS_THREADS, 32, 8, FS_KMAX>), grid, blk, 0, st, a);
   return hipGetLastError();
 }
 

@@ -55,6 +55,20 @@ def test_small_steps_all_queries(cfg):
     assert compared >= n_out // 2, (compared, skips, n_out)
 
 
+def test_prefill_512_queries_pool_sampled():
+    """512 queries (from this many on, the Full-layer selection runs in
+    512-thread blocks, two per compute unit) over 20,000 entries: the pool
+    selects 2,048 of 2,500 blocks and a Reindex layer rescores inside it;
+    every fourth query and the last are checked."""
+    cfg = W.small_config("prefill", n_seq=1, ctx_tokens=4 * 20000, chunk=512, layers=("F", "I"),
+                         build_pool=True, synthetic_cache=True, cid=108)
+    assert cfg.n_queries == 512
+    wl, st = run_step(cfg)
+    qs = list(range(0, cfg.n_queries, 4)) + [cfg.n_queries - 1]
+    swaps, compared, skips = check_queries(wl, st, qs)
+    assert swaps <= max(1, len(qs) // 50) and compared >= len(qs), (swaps, compared, skips)
+
+
 def test_window_and_new_entries_bit_exact():
     """The step's window rows and compressed entries versus the oracle's, at the
     decode workload with 1,024 entries (the 4K-context decode)."""
