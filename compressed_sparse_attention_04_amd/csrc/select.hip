@@ -148,11 +148,12 @@ namespace {
 // Block shapes: 1024 threads (four waves per SIMD hide the latency of each
 // step) with 16 keys each for rows up to 16K keys, 32 up to 32K.  Many rows
 // (prefill chunks) are throughput-bound instead: single selections then use
-// 256 threads with 64 keys each, which fit four blocks per CU and spend a
-// quarter of the per-row wave time on the block-wide steps (the two-phase
-// pool kernel at that shape holds too many registers for it to pay).
+// 512 threads with 32 keys each (about 80 registers, so three blocks, 24
+// waves, share a compute unit; 256 threads with 64 keys need ~150 registers
+// and spill scalar registers heavily, three blocks of 4 waves, and took 1.5x
+// as long).
 constexpr int SEL_NT = 1024, SEL_PER_S = 16, SEL_PER_L = 32;
-constexpr int SEL_NT_T = 256, SEL_PER_T = 64;
+constexpr int SEL_NT_T = 512, SEL_PER_T = 32;
 constexpr int64_t SEL_MANY_ROWS = 1024;
 static_assert(SEL_NT * SEL_PER_L == SEL_CHUNK_MAX, "block shape");
 

@@ -280,6 +280,37 @@ def test_topk_exact(Q, ncols, k, dist):
         assert np.array_equal(got[q], _oracle_topk_fp32(sc[q], k)), q
 
 
+@pytest.mark.parametrize("Q,ncols,k,dist,pooled", [(1024, 16384, 512, "ties", False), (1100, 9000, 512, "few", False),
+                                                   (1024, 16384, 512, "ties", True)])
+def test_topk_many_rows(Q, ncols, k, dist, pooled):
+    """1,024 rows and more take the block shape for many rows (several
+    blocks per compute unit); sampled rows are checked exactly."""
+    rng = np.random.default_rng(Q + ncols + pooled)
+    sc = _score_rows(rng, dist, Q, ncols)
+    sc[:, ::11] = -np.inf
+    sc[5, :] = -np.inf                       # a row with nothing valid
+    sc[6, : ncols - 100] = -np.inf           # fewer valid keys than k
+    blocks = None
+    if pooled:
+        nb = ncols // 8
+        blocks = np.stack([np.sort(rng.choice(3 * nb, nb, replace=False)) for _ in range(Q)]).astype(np.int32)
+        blocks[7, -9:] = -1
+        sc[7, -72:] = -np.inf                # absent blocks score -inf, as the pooled scoring writes them
+        idx = ops.csa_topk(t_(sc), k=k, col_blocks=t_(blocks))
+    else:
+        idx = ops.csa_topk(t_(sc), k=k)
+    torch.cuda.synchronize()
+    got = np_(idx)
+    rows = sorted(set([0, 1, 5, 6, 7, Q // 2, Q - 1] + list(rng.choice(Q, 9, replace=False))))
+    for q in rows:
+        if pooled:
+            ids = (8 * blocks[q][:, None] + np.arange(8)[None]).reshape(-1)
+            want = _oracle_topk_fp32(sc[q], k, ids=ids)
+        else:
+            want = _oracle_topk_fp32(sc[q], k)
+        assert np.array_equal(got[q], want), q
+
+
 @pytest.mark.parametrize("nb,k", [(300, 100), (5000, 512)])     # 5000 blocks: several chunks
 def test_topk_pooled_mapping(nb, k):
     rng = np.random.default_rng(9 + nb)
