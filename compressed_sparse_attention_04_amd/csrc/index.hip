@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
 // and its score is replaced by -inf (an MFMA column only reaches its own
 // output column), so the compiler can count the loads in flight instead of
 // waiting for all of them.
-constexpr int SC_BLOCKS = 2048;   // two rounds of four 4-wave blocks per compute unit
+constexpr int SC_BLOCKS = 2048;   // ~four rounds of two 4-wave blocks per CU (240 registers); 512 and 4,096 measured slower
 
 // SC_GROUP: 8 fragments when a block streams several chunks (4 measured 2%
 // slower there: fewer bytes in flight per wave), 4 when it has one chunk
