@@ -263,7 +263,7 @@ csa_status csa_topk(const float* scores, int64_t Q, int64_t ncols, const int32_t
   CHECK(Q >= 0, CSA_ERR_INVALID_ARG, "%s: Q < 0", fn);
   if (Q == 0) return CSA_OK;
   CHECK(ncols >= 1 && ncols < ((int64_t)1 << 31), CSA_ERR_UNSUPPORTED, "%s: ncols out of range", fn);
-  CHECK(k >= 1 && k <= 4096, CSA_ERR_UNSUPPORTED, "%s: k must be in [1, 4096]", fn);
+  CHECK(k >= 1 && k <= CSA_MAX_K, CSA_ERR_UNSUPPORTED, "%s: k must be in [1, 16384]", fn);
   CHECK(col_blocks == nullptr || ncols % 8 == 0, CSA_ERR_INVALID_ARG,
         "%s: pooled columns must be a multiple of 8", fn);
   CHECK_PTR(scores); CHECK_PTR(idx);
@@ -313,9 +313,10 @@ static csa_status check_attn(const char* fn, const float* q, const int32_t* q_po
                              int64_t kv_rows, const int32_t* idx, int32_t k, const uint8_t* win,
                              int64_t win_cap, float sm_scale, float* out, void* ws, size_t ws_bytes) {
   CHECK(n_seq >= 0 && q_per_seq >= 0, CSA_ERR_INVALID_ARG, "%s: negative size", fn);
-  CHECK(k >= 1 && k <= 4096, CSA_ERR_UNSUPPORTED, "%s: k must be in [1, 4096]", fn);
-  CHECK(kv_rows >= 0 && kv_rows < ((int64_t)1 << 31), CSA_ERR_UNSUPPORTED, "%s: kv_rows out of range", fn);
-  CHECK(win_cap >= NWIN, CSA_ERR_UNSUPPORTED, "%s: win_cap must be >= 128", fn);
+  CHECK(k >= 1 && k <= CSA_MAX_K, CSA_ERR_UNSUPPORTED, "%s: k must be in [1, 16384]", fn);
+  CHECK(kv_rows >= 0 && kv_rows < ((int64_t)1 << 23), CSA_ERR_UNSUPPORTED, "%s: kv_rows must be in [0, 2^23)", fn);
+  CHECK(win_cap >= NWIN && win_cap < ((int64_t)1 << 22), CSA_ERR_UNSUPPORTED, "%s: win_cap must be in [128, 2^22)",
+        fn);
   CHECK(std::isfinite(sm_scale), CSA_ERR_INVALID_ARG, "%s: sm_scale must be finite", fn);
   CHECK_PTR(q); CHECK_PTR(q_pos); CHECK_PTR(codes); CHECK_PTR(scales); CHECK_PTR(idx);
   CHECK_PTR(win); CHECK_PTR(out);
@@ -351,7 +352,7 @@ size_t csa_layer_workspace_size(int32_t mode, const csa_layer_args* a) {
 static csa_status check_layer(const char* fn, int32_t mode, const csa_layer_args* a, LayerPlan* plan) {
   CHECK(a != nullptr, CSA_ERR_INVALID_ARG, "%s: args is NULL", fn);
   CHECK(a->n_seq >= 0 && a->q_per_seq >= 0, CSA_ERR_INVALID_ARG, "%s: negative size", fn);
-  CHECK(a->top_k >= 1 && a->top_k <= 4096, CSA_ERR_UNSUPPORTED, "%s: top_k must be in [1, 4096]", fn);
+  CHECK(a->top_k >= 1 && a->top_k <= CSA_MAX_K, CSA_ERR_UNSUPPORTED, "%s: top_k must be in [1, 16384]", fn);
   CHECK(a->n_entries >= 0 && a->n_entries <= a->kv_rows, CSA_ERR_INVALID_ARG,
         "%s: n_entries must be <= kv_rows", fn);
   CHECK_PTR(a->idx); CHECK_PTR(a->out);

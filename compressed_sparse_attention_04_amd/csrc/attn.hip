@@ -1,32 +1,49 @@
 // Sparse multi-query attention over the selected MXFP4 entries plus the
 // FP8 sliding window.
 //
-// P3 §02: the selected Top-K entries are used for attention; one shared latent
-// serves all query heads (fewer KV heads).  P3 §03: the FP4 cache is
-// dequantized before attention (no FP4 matmul), the SWA window stays FP8 and
-// covers n_win = 128 tokens.
+// "DeepSeek-V4.1 架构解析" §02 (CSA2): the selected Top-K entries are the
+// keys of the attention, and one shared latent serves every query head (the
+// number of KV heads is compressed).  §03 (精度与状态重建): the FP4 cache is
+// dequantized before the attention (FP4 is a storage format, not a matmul
+// format), and the sliding-window KV stays in FP8 over the last n_win = 128
+// tokens.
 //
-// Work item = (query, split of its key slots); one block of KG key groups of
-// four waves per work item, wave w of a group owning channels 128 w .. 128 w
-// + 127, and group kg taking the split's tiles kg, kg + KG, ...  Key slots
-// 0..k-1 are the selected entries, slots k..k+127 the window tokens
-// p-127..p.  Per 16-slot tile:
-//   1. lane (j, g) of wave w loads channels 128 w + 32 g .. + 31 of key j
+// Key slots 0..k-1 of a query are its selected entries, slots k..k+127 the
+// window tokens p-127..p.  A key group is four waves; wave w owns channels
+// 128 w .. 128 w + 127.  Per 16-slot tile:
+//   1. lane (j, g) of wave w holds channels 128 w + 32 g .. + 31 of slot j
 //      (16 FP4 code bytes + 2 E4M3 scale bytes, or 32 E4M3 window bytes) and
-//      dequantizes them to fp16 in registers (exact);
-//   2. partial S^T = K Q^T over the wave's channels on the fp16 matrix cores
-//      (4 x v_mfma 16x16x32), summed over the four waves through LDS in a
-//      fixed order, so every wave holds the same S;
-//   3. online softmax in float32 (log2 domain), computed alike by each wave;
-//   4. the fp16 key slices go through the wave's own LDS rows so that each
-//      lane can gather 4 keys of one channel for the B operand of P V
-//      (8 x v_mfma 16x16x16).  Output channel of N-tile n in lane column c is
-//      128 w + 8 c + n, so every lane reads 16 contiguous bytes per key.
-// Key bytes are loaded at_depth tiles ahead of use and slot ids 2 at_depth
-// tiles ahead.  The key groups of a block merge their (O, max, sum) through
-// LDS at the end, so a split writes one partial however many groups it has;
-// with several splits per query the partials are combined by
-// attn_combine_kernel.
+//      widens them to fp16 in registers (exact: E2M1 x E4M3 needs 5
+//      significant bits);
+//   2. partial S^T = K Q^T over the wave's channels on the fp16 matrix cores.
+//      Q is carried as two fp16 halves, hi = fp16(q) and lo = fp16(q - hi),
+//      each contracted with the same exact keys (16x16x32, float32
+//      accumulation), so S carries q to about 2^-22 instead of fp16's 2^-11;
+//      the four waves' partials are summed through LDS in a fixed order, so
+//      every wave holds the same S;
+//   3. online softmax in float32 (log2 domain; every wave computes the same);
+//   4. P V on the matrix cores with P split the same way: P_hi V + P_lo V
+//      (16x16x16, exact products, float32 accumulation), so the weights
+//      enter at ~2^-22 relative; the denominator sums the same split
+//      weights.  The
+//      fp16 key slices go through the wave's own LDS rows so that each lane
+//      gathers 4 keys of one channel (output channel of N-tile n in lane
+//      column c is 128 w + 8 c + n: 16 contiguous bytes per key).
+// Key bytes are read through buffer views of the query's rows: an absent
+// key (a -1 id, an id past the cache, a window position before 0, padding)
+// reads past the view and gets zeros, so no load sits under a branch.
+//
+// Two launch shapes:
+//   * split (decode batches): a query's tiles are cut into splits of KG x T
+//     tiles; a block holds KG key groups, and every group issues the loads of
+//     all its T tiles before the first one is used, so the dependent gather
+//     (slot id, then the entry bytes) is paid once per block rather than
+//     once per tile.  Splits write (O, max, sum) partials that
+//     attn_combine_kernel merges.
+//   * stream (prefill chunks, and decode with very large k): one block per
+//     query (or a few splits), tiles streamed with one (one group) or two
+//     (two groups) tiles of key bytes in flight.
+// The key groups of a block merge their (O, max, sum) through LDS at the end.
 #include "common.h"
 #include "kernels.h"
 
@@ -37,11 +54,9 @@ constexpr int AT_WAVES = 4;                      // waves of one key group
 constexpr int AT_THREADS = 64 * AT_WAVES;
 constexpr int AT_QCH = D / AT_WAVES;             // channels per wave
 constexpr int AT_KPITCH = AT_QCH * 2 + 16;       // bytes per LDS key row of one wave (fp16 + pad)
-// Tiles of key bytes in flight: two with several key groups per block (few
-// blocks, so the loads' latency shows), one with a single group (four
-// waves per SIMD, whose interleaving covers the latency of one tile ahead;
-// one register set fewer to rotate).
-template <int KG> constexpr int at_depth() { return KG == 1 ? 1 : 2; }
+// Buffer offset past every view: the views hold fewer than 2^31 bytes
+// (kv_rows <= 2^23 entries of 256 bytes, win_cap < 2^22 rows of 512 bytes).
+constexpr uint32_t AT_OOB = 0x80000000u;
 
 struct AttnArgs {
   const float* q;
@@ -76,54 +91,96 @@ struct RawKey {
 // both (only when k is not a multiple of the tile, in the one tile holding
 // slot k).  Padding slots are kind 0 and fit every tile kind.
 constexpr int TK_ENTRY = 0, TK_WINDOW = 1, TK_MIXED = 2;
-// Kind of tile t (t * AT_TILE is the same in every lane).
 __device__ __forceinline__ int tile_kind(int t, int k) {
   const int slot0 = t * AT_TILE;
   return slot0 + AT_TILE <= k ? TK_ENTRY : slot0 >= k ? TK_WINDOW : TK_MIXED;
 }
 
-// Entry id of this lane's slot in tile t (-1: padding / out of range; the
-// window slots need no id).  idx_q is the query's row of the index array.
-__device__ __forceinline__ int32_t slot_id(const int32_t* idx_q, int k, int t, int t_end, int j) {
-  const int slot = t * AT_TILE + j;
-  if (t >= t_end || slot >= k) return -1;
-  return idx_q[slot];
+// Buffer views of one query's rows and its window geometry.
+struct QueryView {
+  __amdgpu_buffer_rsrc_t codes, scales, win, idx;
+  int32_t p;         // query position
+  int32_t wbase;     // ring row of position p - 127 (mod win_cap)
+  int32_t win_cap;
+};
+
+__device__ __forceinline__ QueryView query_view(const AttnArgs& a, int64_t qi) {
+  const int64_t seq = qi / a.q_per_seq;
+  QueryView v;
+  v.codes = __builtin_amdgcn_make_buffer_rsrc((void*)(a.codes + seq * a.kv_rows * CODE_BYTES), (short)0,
+                                              (int)(a.kv_rows * CODE_BYTES), 0x00020000);
+  v.scales = __builtin_amdgcn_make_buffer_rsrc((void*)(a.scales + seq * a.kv_rows * SCALE_BYTES), (short)0,
+                                               (int)(a.kv_rows * SCALE_BYTES), 0x00020000);
+  v.win = __builtin_amdgcn_make_buffer_rsrc((void*)(a.win + seq * a.win_cap * D), (short)0, (int)(a.win_cap * D),
+                                            0x00020000);
+  v.idx = __builtin_amdgcn_make_buffer_rsrc((void*)(a.idx + qi * a.k), (short)0, a.k * 4, 0x00020000);
+  v.p = a.q_pos[qi];
+  v.win_cap = (int32_t)a.win_cap;
+  int32_t wb = (int32_t)(((int64_t)v.p - (NWIN - 1)) % a.win_cap);
+  v.wbase = wb < 0 ? wb + v.win_cap : wb;
+  return v;
 }
 
-// wbase is the ring row of position p - 127 (mod win_cap, win_cap >= 128),
-// so window slot wi sits at row wbase + wi, wrapped at most once.
-// TK (see below) is the kind of tile t, the same for every lane: an entry
-// tile loads no window bytes and a window tile no entry bytes.
+// Entry id of this lane's slot j in tile t (-1: not an entry slot or past
+// the tiles in use).  The load is unconditional (a slot past k reads past the
+// index view and gets 0, which the slot test then discards).
+__device__ __forceinline__ int32_t slot_id(const QueryView& v, int k, int t, bool live, int j) {
+  const int slot = t * AT_TILE + j;
+  const uint32_t off = (live && slot < k) ? (uint32_t)slot * 4u : AT_OOB;
+  const int32_t id = __builtin_amdgcn_raw_buffer_load_b32(v.idx, off, 0, 0);
+  return (live && slot < k) ? id : -1;
+}
+
+__device__ __forceinline__ uint4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
+}
+
+// The lane's bytes of tile t (TK = the tile's kind, the same in every lane).
+// Every load is issued unconditionally; an absent key reads past its view.
 template <int TK>
-__device__ __forceinline__ RawKey load_key(const AttnArgs& a, int t, int t_end, int j, int g, int w,
-                                           int32_t id, int32_t p, int64_t wbase, const uint8_t* codes_seq,
-                                           const uint8_t* scales_seq, const uint8_t* win_seq) {
+__device__ __forceinline__ RawKey load_tile(const QueryView& v, const AttnArgs& a, int t, bool live, int j, int g,
+                                            int w, int32_t id) {
   RawKey r;
   r.a = make_uint4(0u, 0u, 0u, 0u);
   r.b = make_uint4(0u, 0u, 0u, 0u);
   r.sc = 0u;
   r.kind = 0;
-  if (t >= t_end) return r;
   const int slot = t * AT_TILE + j;
-  const bool entry_slot = (TK == TK_ENTRY) ? true : (TK == TK_WINDOW) ? false : slot < a.k;
-  if (entry_slot) {
-    if (id >= 0 && id < a.kv_rows) {
-      r.a = *reinterpret_cast<const uint4*>(codes_seq + (int64_t)id * CODE_BYTES + 64 * w + 16 * g);
-      r.sc = *reinterpret_cast<const uint16_t*>(scales_seq + (int64_t)id * SCALE_BYTES + 8 * w + 2 * g);
-      r.kind = 1;
-    }
-  } else {
+  if constexpr (TK != TK_WINDOW) {
+    const bool ok = live && (TK == TK_ENTRY || slot < a.k) && id >= 0 && id < a.kv_rows;
+    const uint32_t oc = ok ? (uint32_t)id * CODE_BYTES + 64u * w + 16u * g : AT_OOB;
+    const uint32_t os = ok ? (uint32_t)id * SCALE_BYTES + 8u * w + 2u * g : AT_OOB;
+    r.a = load_b128(v.codes, oc);
+    r.sc = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(v.scales, os, 0, 0);
+    r.kind = ok ? 1 : 0;
+  }
+  if constexpr (TK != TK_ENTRY) {
     const int wi = slot - a.k;
-    if (wi < NWIN && p - (NWIN - 1) + wi >= 0) {
-      int64_t row = wbase + wi;
-      row = row >= a.win_cap ? row - a.win_cap : row;
-      const uint4* src = reinterpret_cast<const uint4*>(win_seq + row * D + AT_QCH * w + 32 * g);
-      r.a = src[0];
-      r.b = src[1];
-      r.kind = 2;
+    const bool ok = live && wi >= 0 && wi < NWIN && v.p - (NWIN - 1) + wi >= 0;
+    int row = v.wbase + wi;
+    row = row >= v.win_cap ? row - v.win_cap : row;
+    const uint32_t ow = ok ? (uint32_t)row * D + AT_QCH * w + 32u * g : AT_OOB;
+    const uint4 wa = load_b128(v.win, ow), wb = load_b128(v.win, ow + 16u);
+    if constexpr (TK == TK_WINDOW) {
+      r.a = wa;
+      r.b = wb;
+      r.kind = ok ? 2 : 0;
+    } else {
+      r.a = ok ? wa : r.a;
+      r.b = wb;                         // zero unless ok
+      r.kind = ok ? 2 : r.kind;
     }
   }
   return r;
+}
+
+__device__ __forceinline__ RawKey load_tile_any(const QueryView& v, const AttnArgs& a, int t, bool live, int j,
+                                                int g, int w, int32_t id) {
+  const int tk = tile_kind(t, a.k);   // wave-uniform: a scalar branch
+  if (tk == TK_ENTRY) return load_tile<TK_ENTRY>(v, a, t, live, j, g, w, id);
+  if (tk == TK_WINDOW) return load_tile<TK_WINDOW>(v, a, t, live, j, g, w, id);
+  return load_tile<TK_MIXED>(v, a, t, live, j, g, w, id);
 }
 
 // Channels 8 s .. 8 s + 7 of the lane's 32 as fp16 (exact), k-step s < 4.
@@ -155,8 +212,7 @@ __device__ __forceinline__ f16x8 key_slice(const RawKey& r, int s) {
 
 // Rescale threshold of the online softmax (log2 units): the running reference
 // max of a head moves only when a new logit exceeds it by more than this, so
-// unnormalized weights stay <= 2^8 (exact range for fp16 P and fp32 sums)
-// and O is rarely rescaled.
+// unnormalized weights stay <= 2^8 and O is rarely rescaled.
 constexpr float AT_RESCALE = 8.0f;
 
 // 2^x on the transcendental unit alone (v_exp_f32, ~1 ulp): the loop's
@@ -179,177 +235,158 @@ struct AttnLds {
   };
 };
 
-// Four waves per SIMD: registers capped at 128 per lane.
-template <int KG>
-__global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu(4))) void attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) AttnLds<KG> lds;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = (tid >> 6) & (AT_WAVES - 1);
-  // the key group is wave-uniform: taken from lane 0, so the tile index and
-  // every branch on it are scalar
-  const int kg = __builtin_amdgcn_readfirstlane(tid >> 8);
-  constexpr int AT_DEPTH = at_depth<KG>();
-  const int j = lane & 15;      // key slot (loads, S rows), head (Q, softmax), channel group (P V)
-  const int g = lane >> 4;      // 32-channel group (loads), key group of 4 (S, P)
-  const int64_t qi = blockIdx.y;
-  const int split = blockIdx.x;
-  const int64_t seq = qi / a.q_per_seq;
-  const int32_t p = a.q_pos[qi];
-  const int n_slots = a.k + NWIN;
-  const int n_tiles = (n_slots + AT_TILE - 1) / AT_TILE;
-  const int t_begin = split * a.tiles_per_split;
-  int t_end = t_begin + a.tiles_per_split;
-  t_end = t_end < n_tiles ? t_end : n_tiles;
-  // group kg takes tiles t_begin + kg + KG i; every group runs n_iter rounds
-  // (a round past t_end is all padding), so the block barriers line up
-  const int n_iter = (t_end - t_begin + KG - 1) / KG;
-  const uint8_t* codes_seq = a.codes + seq * a.kv_rows * CODE_BYTES;
-  const uint8_t* scales_seq = a.scales + seq * a.kv_rows * SCALE_BYTES;
-  const uint8_t* win_seq = a.win + seq * a.win_cap * D;
-  auto tile = [&](int i) { return t_begin + kg + KG * i; };
+// Running state of one wave: O of heads 4 g + r (rows) x channels
+// 128 w + 8 j + n (acc_o[n][r]); max and sum of head j.
+struct AttnState {
+  f32x4 acc_o[8];
+  float m_run, l_run;
+};
 
-  // Q: head j, channels 128 w + 32 g .. + 31 (issued first: nothing depends on it)
-  float4 qraw[8];
-  {
-    const float4* src = reinterpret_cast<const float4*>(a.q + (qi * HEADS + j) * D + AT_QCH * w + 32 * g);
+__device__ __forceinline__ void state_init(AttnState& st) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qraw[i] = src[i];
-  }
-  const int32_t* idx_q = a.idx + qi * a.k;
-  int64_t wbase = ((int64_t)p - (NWIN - 1)) % a.win_cap;
-  wbase = wbase < 0 ? wbase + a.win_cap : wbase;
-  int32_t id_ahead[AT_DEPTH];
+  for (int n = 0; n < 8; ++n) st.acc_o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -__builtin_huge_valf();
+  st.l_run = 0.f;
+}
+
+// Q of head j, channels 128 w + 32 g .. + 31, scaled by the logit factor
+// (sm_scale log2 e, so S is in the log2 domain of the softmax) and split into
+// fp16 hi / lo halves per k-step.
+__device__ __forceinline__ void load_q(const AttnArgs& a, int64_t qi, int j, int g, int w, float4 (&qraw)[8]) {
+  const float4* src = reinterpret_cast<const float4*>(a.q + (qi * HEADS + j) * D + AT_QCH * w + 32 * g);
 #pragma unroll
-  for (int i = 0; i < AT_DEPTH; ++i) id_ahead[i] = slot_id(idx_q, a.k, tile(AT_DEPTH + i), t_end, j);
-  RawKey ring[AT_DEPTH];
-  // loads of tile t, dispatched on its kind (a scalar branch)
-  auto issue = [&](int t, int32_t id) -> RawKey {
-    const int tk = tile_kind(t, a.k);
-    if (tk == TK_ENTRY) return load_key<TK_ENTRY>(a, t, t_end, j, g, w, id, p, wbase, codes_seq, scales_seq, win_seq);
-    if (tk == TK_WINDOW) return load_key<TK_WINDOW>(a, t, t_end, j, g, w, id, p, wbase, codes_seq, scales_seq, win_seq);
-    return load_key<TK_MIXED>(a, t, t_end, j, g, w, id, p, wbase, codes_seq, scales_seq, win_seq);
-  };
-#pragma unroll
-  for (int i = 0; i < AT_DEPTH; ++i) ring[i] = issue(tile(i), slot_id(idx_q, a.k, tile(i), t_end, j));
-  // Q carries the logit scale (sm_scale * log2 e), so S is already in the
-  // log2 domain of the softmax
-  f16x8 qf[4];
-  const float cq = a.c_log2;
+  for (int i = 0; i < 8; ++i) qraw[i] = src[i];
+}
+__device__ __forceinline__ void split_q(const float4 (&qraw)[8], float cq, f16x8 (&qh)[4], f16x8 (&ql)[4]) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const float4 x = qraw[2 * s], y = qraw[2 * s + 1];
-    qf[s] = f16x8{(_Float16)(x.x * cq), (_Float16)(x.y * cq), (_Float16)(x.z * cq), (_Float16)(x.w * cq),
-                  (_Float16)(y.x * cq), (_Float16)(y.y * cq), (_Float16)(y.z * cq), (_Float16)(y.w * cq)};
-  }
-
-  f32x4 acc_o[8];
+    const float v[8] = {x.x * cq, x.y * cq, x.z * cq, x.w * cq, y.x * cq, y.y * cq, y.z * cq, y.w * cq};
 #pragma unroll
-  for (int n = 0; n < 8; ++n) acc_o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_huge_valf(), l_run = 0.f;
-  uint8_t* krow = lds.loop.k[AT_WAVES * kg + w];
-
-  for (int it = 0; it < n_iter; ++it) {
-    const RawKey cur = ring[0];
-#pragma unroll
-    for (int i = 0; i + 1 < AT_DEPTH; ++i) ring[i] = ring[i + 1];
-    ring[AT_DEPTH - 1] = issue(tile(it + AT_DEPTH), id_ahead[0]);
-#pragma unroll
-    for (int i = 0; i + 1 < AT_DEPTH; ++i) id_ahead[i] = id_ahead[i + 1];
-    id_ahead[AT_DEPTH - 1] = slot_id(idx_q, a.k, tile(it + 2 * AT_DEPTH), t_end, j);
-
-    // ---- 2. partial S^T over this wave's channels; slices to LDS row j ------
-    __builtin_amdgcn_wave_barrier();   // the previous tile's LDS reads come first
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-    auto qk = [&](auto tk) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const f16x8 av = key_slice<decltype(tk)::value>(cur, s);
-        *reinterpret_cast<f16x8*>(krow + j * AT_KPITCH + 64 * g + 16 * s) = av;
-        sacc = mfma_f16_16x16x32(av, qf[s], sacc);
-      }
-    };
-    // one conversion per tile kind
-    const int tk = tile_kind(tile(it), a.k);
-    if (tk == TK_ENTRY) qk(std::integral_constant<int, TK_ENTRY>{});
-    else if (tk == TK_WINDOW) qk(std::integral_constant<int, TK_WINDOW>{});
-    else qk(std::integral_constant<int, TK_MIXED>{});
-    const int par = it & 1;
-    lds.loop.s[par][kg][w][lane] = sacc;
-    __syncthreads();
-    f32x4 S = lds.loop.s[par][kg][0][lane];
-#pragma unroll
-    for (int v = 1; v < AT_WAVES; ++v) {
-      const f32x4 o = lds.loop.s[par][kg][v][lane];
-      S[0] += o[0]; S[1] += o[1]; S[2] += o[2]; S[3] += o[3];
-    }
-
-    // ---- 3. online softmax (lane: keys 4g+r, head j), lazy rescaling --------
-    const uint32_t vmask = (uint32_t)(__ballot(cur.kind != 0) & 0xFFFFull);
-    float x[4] = {S[0], S[1], S[2], S[3]};
-    if (vmask != 0xFFFFu) {   // wave-uniform: only tiles with an absent key mask
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = ((vmask >> (4 * g + r)) & 1u) ? x[r] : -__builtin_huge_valf();
-    }
-    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mx = max_xor32(max_xor16(mx));
-    const bool first = (m_run == -__builtin_huge_valf());
-    const bool move = !first && (mx > m_run + AT_RESCALE);
-    if (__ballot(move)) {
-      const float alpha = move ? exp2_loop(m_run - mx) : 1.0f;
-      l_run *= alpha;
-      float al[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * g + r);
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        acc_o[n][0] *= al[0]; acc_o[n][1] *= al[1];
-        acc_o[n][2] *= al[2]; acc_o[n][3] *= al[3];
-      }
-    }
-    if (first || move) m_run = mx;
-    const float base = (m_run == -__builtin_huge_valf()) ? 0.f : m_run;
-    float pr[4], psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pr[r] = exp2_loop(x[r] - base);
-      psum += pr[r];
-    }
-    l_run += psum;   // this lane's keys only; the four lanes of head j are summed after the loop
-    const f16x4 pa = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
-
-    // ---- 4. P V: gather keys 4g .. 4g+3 of channels 8j .. 8j+7 from LDS ---------
-    uint4 v[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      v[kk] = *reinterpret_cast<const uint4*>(krow + (4 * g + kk) * AT_KPITCH + 16 * j);
-    const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
-    const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
-    const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
-    const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // channel pair (2i, 2i+1) of the 8: N-tiles 2i and 2i+1
-      const f16x2 a0 = bits_f16x2(__builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u));
-      const f16x2 a1 = bits_f16x2(__builtin_amdgcn_perm(w3[i], w2[i], 0x05040100u));
-      const f16x2 b0 = bits_f16x2(__builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u));
-      const f16x2 b1 = bits_f16x2(__builtin_amdgcn_perm(w3[i], w2[i], 0x07060302u));
-      const f16x4 blo = {a0[0], a0[1], a1[0], a1[1]};
-      const f16x4 bhi = {b0[0], b0[1], b1[0], b1[1]};
-      acc_o[2 * i] = mfma_f16_16x16x16(pa, blo, acc_o[2 * i]);
-      acc_o[2 * i + 1] = mfma_f16_16x16x16(pa, bhi, acc_o[2 * i + 1]);
+    for (int e = 0; e < 8; ++e) {
+      const _Float16 h = (_Float16)v[e];
+      qh[s][e] = h;
+      ql[s][e] = (_Float16)(v[e] - (float)h);
     }
   }
+}
 
-  l_run = sum_xor32(sum_xor16(l_run));   // head j's sum over all keys of this group
+// Step 2 of one tile for this wave (TK = the tile's kind): the key slices to
+// the wave's LDS rows and the wave's partial S^T = K (Q_hi + Q_lo)^T.
+template <int TK>
+__device__ __forceinline__ f32x4 tile_qk(const RawKey& cur, const f16x8 (&qh)[4], const f16x8 (&ql)[4],
+                                         uint8_t* krow, int j, int g) {
+  __builtin_amdgcn_wave_barrier();   // the previous tile's LDS reads come first
+  f32x4 sh = {0.f, 0.f, 0.f, 0.f}, sl = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const f16x8 av = key_slice<TK>(cur, s);
+    *reinterpret_cast<f16x8*>(krow + j * AT_KPITCH + 64 * g + 16 * s) = av;
+    sh = mfma_f16_16x16x32(av, qh[s], sh);
+    sl = mfma_f16_16x16x32(av, ql[s], sl);
+  }
+  return f32x4{sh[0] + sl[0], sh[1] + sl[1], sh[2] + sl[2], sh[3] + sl[3]};
+}
 
-  // ---- merge the key groups: O, max and sum per head over the groups --------
+// Steps 2-4 of one tile for this wave.  krow: the wave's LDS key rows; sbuf:
+// the group's partial-S exchange buffer for this tile's parity.  Every wave
+// of the block calls this the same number of times (it holds a barrier).
+// Only the key conversion depends on the tile kind (a scalar branch).
+__device__ __forceinline__ void attn_tile(int tk, AttnState& st, const RawKey& cur, const f16x8 (&qh)[4],
+                                          const f16x8 (&ql)[4], uint8_t* krow, f32x4 (*sbuf)[64], int w,
+                                          int lane, int j, int g) {
+  f32x4 part;
+  if (tk == TK_ENTRY) part = tile_qk<TK_ENTRY>(cur, qh, ql, krow, j, g);
+  else if (tk == TK_WINDOW) part = tile_qk<TK_WINDOW>(cur, qh, ql, krow, j, g);
+  else part = tile_qk<TK_MIXED>(cur, qh, ql, krow, j, g);
+  sbuf[w][lane] = part;
+  __syncthreads();
+  f32x4 S = sbuf[0][lane];
+#pragma unroll
+  for (int v = 1; v < AT_WAVES; ++v) {
+    const f32x4 o = sbuf[v][lane];
+    S[0] += o[0]; S[1] += o[1]; S[2] += o[2]; S[3] += o[3];
+  }
+
+  // ---- 3. online softmax (lane: keys 4g+r, head j), lazy rescaling --------
+  const uint32_t vmask = (uint32_t)(__ballot(cur.kind != 0) & 0xFFFFull);
+  float x[4] = {S[0], S[1], S[2], S[3]};
+  if (vmask != 0xFFFFu) {   // wave-uniform: only tiles with an absent key mask
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = ((vmask >> (4 * g + r)) & 1u) ? x[r] : -__builtin_huge_valf();
+  }
+  float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  mx = max_xor32(max_xor16(mx));
+  const bool first = (st.m_run == -__builtin_huge_valf());
+  const bool move = !first && (mx > st.m_run + AT_RESCALE);
+  if (__ballot(move)) {
+    const float alpha = move ? exp2_loop(st.m_run - mx) : 1.0f;
+    st.l_run *= alpha;
+    float al[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * g + r);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      st.acc_o[n][0] *= al[0]; st.acc_o[n][1] *= al[1];
+      st.acc_o[n][2] *= al[2]; st.acc_o[n][3] *= al[3];
+    }
+  }
+  if (first || move) st.m_run = mx;
+  const float base = (st.m_run == -__builtin_huge_valf()) ? 0.f : st.m_run;
+  // A operands of P V: P_hi and P_lo of keys 4g..4g+3 (head j); the sum
+  // takes the same two halves
+  f16x4 ph, pl;
+  float psum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float pr = exp2_loop(x[r] - base);
+    const _Float16 h = (_Float16)pr;
+    const _Float16 l = (_Float16)(pr - (float)h);
+    ph[r] = h;
+    pl[r] = l;
+    psum += (float)h + (float)l;
+  }
+  st.l_run += psum;   // this lane's keys only; the four lanes of head j are summed at the end
+
+  // ---- 4. P V: keys 4g .. 4g+3 of channels 8j .. 8j+7 from LDS -------------
+  uint4 v[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) v[kk] = *reinterpret_cast<const uint4*>(krow + (4 * g + kk) * AT_KPITCH + 16 * j);
+  const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+  const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
+  const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
+  const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // channel pair (2i, 2i+1) of the 8: N-tiles 2i and 2i+1, each against the
+    // hi and then the lo weights
+    const f16x2 a0 = bits_f16x2(__builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u));
+    const f16x2 a1 = bits_f16x2(__builtin_amdgcn_perm(w3[i], w2[i], 0x05040100u));
+    const f16x2 b0 = bits_f16x2(__builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u));
+    const f16x2 b1 = bits_f16x2(__builtin_amdgcn_perm(w3[i], w2[i], 0x07060302u));
+    const f16x4 blo = {a0[0], a0[1], a1[0], a1[1]};
+    const f16x4 bhi = {b0[0], b0[1], b1[0], b1[1]};
+    st.acc_o[2 * i] = mfma_f16_16x16x16(ph, blo, st.acc_o[2 * i]);
+    st.acc_o[2 * i + 1] = mfma_f16_16x16x16(ph, bhi, st.acc_o[2 * i + 1]);
+    st.acc_o[2 * i] = mfma_f16_16x16x16(pl, blo, st.acc_o[2 * i]);
+    st.acc_o[2 * i + 1] = mfma_f16_16x16x16(pl, bhi, st.acc_o[2 * i + 1]);
+  }
+}
+
+// Merge the KG groups' states (group 0 keeps the result; the others return
+// false) and write the block's result: the output when the query has one
+// split, else the split's partial (O unnormalized, max, sum).
+template <int KG>
+__device__ __forceinline__ void attn_finish(AttnLds<KG>& lds, AttnState& st, const AttnArgs& a, int64_t qi,
+                                            int split, int kg, int w, int lane, int j, int g) {
+  st.l_run = sum_xor32(sum_xor16(st.l_run));   // head j's sum over all keys of this group
   // lane holds O[head 4g + r][channel 128 w + 8 j + n]; m_run, l_run are head j's
   float lsum[4];   // sum of head 4 g + r over the groups
   if constexpr (KG > 1) {
     __syncthreads();                                   // loop LDS is free
     if (w == 0 && lane < 16) {
-      lds.red.ml[kg][0][j] = m_run;
-      lds.red.ml[kg][1][j] = l_run;
+      lds.red.ml[kg][0][j] = st.m_run;
+      lds.red.ml[kg][1][j] = st.l_run;
     }
     __syncthreads();
     float mine[4];
@@ -369,7 +406,6 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
       }
       lsum[r] = L;
     }
-    // head j's merged max and sum (what a partial carries)
     {
       float M = lds.red.ml[0][0][j];
 #pragma unroll
@@ -380,19 +416,19 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
         const float mv = lds.red.ml[v][0][j];
         L = fmaf((mv == -__builtin_huge_valf()) ? 0.f : exp2f(mv - M), lds.red.ml[v][1][j], L);
       }
-      m_run = M;
-      l_run = L;
+      st.m_run = M;
+      st.l_run = L;
     }
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-      acc_o[n][0] *= mine[0]; acc_o[n][1] *= mine[1];
-      acc_o[n][2] *= mine[2]; acc_o[n][3] *= mine[3];
+      st.acc_o[n][0] *= mine[0]; st.acc_o[n][1] *= mine[1];
+      st.acc_o[n][2] *= mine[2]; st.acc_o[n][3] *= mine[3];
     }
     if (kg > 0) {
 #pragma unroll
       for (int n = 0; n < 8; ++n)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) lds.red.o[kg - 1][w][4 * n + r][lane] = acc_o[n][r];
+        for (int r = 0; r < 4; ++r) lds.red.o[kg - 1][w][4 * n + r][lane] = st.acc_o[n][r];
     }
     __syncthreads();
     if (kg > 0) return;
@@ -401,13 +437,12 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
       for (int n = 0; n < 8; ++n)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc_o[n][r] += lds.red.o[v][w][4 * n + r][lane];
+        for (int r = 0; r < 4; ++r) st.acc_o[n][r] += lds.red.o[v][w][4 * n + r][lane];
   } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) lsum[r] = __shfl(l_run, 4 * g + r);
+    for (int r = 0; r < 4; ++r) lsum[r] = __shfl(st.l_run, 4 * g + r);
   }
 
-  // ---- epilogue (group 0) ---------------------------------------------------
   if (a.n_splits == 1) {
     float inv[4];
 #pragma unroll
@@ -415,22 +450,130 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float4* dst = reinterpret_cast<float4*>(a.out + (qi * HEADS + 4 * g + r) * D + AT_QCH * w + 8 * j);
-      dst[0] = make_float4(acc_o[0][r] * inv[r], acc_o[1][r] * inv[r], acc_o[2][r] * inv[r], acc_o[3][r] * inv[r]);
-      dst[1] = make_float4(acc_o[4][r] * inv[r], acc_o[5][r] * inv[r], acc_o[6][r] * inv[r], acc_o[7][r] * inv[r]);
+      const f32x4* o = st.acc_o;
+      dst[0] = make_float4(o[0][r] * inv[r], o[1][r] * inv[r], o[2][r] * inv[r], o[3][r] * inv[r]);
+      dst[1] = make_float4(o[4][r] * inv[r], o[5][r] * inv[r], o[6][r] * inv[r], o[7][r] * inv[r]);
     }
   } else {
     const int64_t ps = qi * a.n_splits + split;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float4* dst = reinterpret_cast<float4*>(a.part_o + (ps * HEADS + 4 * g + r) * D + AT_QCH * w + 8 * j);
-      dst[0] = make_float4(acc_o[0][r], acc_o[1][r], acc_o[2][r], acc_o[3][r]);
-      dst[1] = make_float4(acc_o[4][r], acc_o[5][r], acc_o[6][r], acc_o[7][r]);
+      const f32x4* o = st.acc_o;
+      dst[0] = make_float4(o[0][r], o[1][r], o[2][r], o[3][r]);
+      dst[1] = make_float4(o[4][r], o[5][r], o[6][r], o[7][r]);
     }
     if (w == 0 && lane < 16) {
-      a.part_ml[(ps * 2 + 0) * HEADS + j] = m_run;
-      a.part_ml[(ps * 2 + 1) * HEADS + j] = l_run;
+      a.part_ml[(ps * 2 + 0) * HEADS + j] = st.m_run;
+      a.part_ml[(ps * 2 + 1) * HEADS + j] = st.l_run;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Split kernel: block (split, query) holds KG key groups; group kg takes the
+// split's tiles t_begin + kg + KG i, i < T, and issues the loads of all of
+// them (slot ids, then key bytes) before its first tile.
+template <int KG, int T>
+__global__ __launch_bounds__(AT_THREADS * KG) void attn_split_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) AttnLds<KG> lds;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = (tid >> 6) & (AT_WAVES - 1);
+  const int kg = __builtin_amdgcn_readfirstlane(tid >> 8);   // wave-uniform
+  const int j = lane & 15, g = lane >> 4;
+  const int64_t qi = blockIdx.y;
+  const int split = blockIdx.x;
+  const int n_tiles = (a.k + NWIN + AT_TILE - 1) / AT_TILE;
+  const int t_begin = split * a.tiles_per_split;
+  int t_end = t_begin + a.tiles_per_split;
+  t_end = t_end < n_tiles ? t_end : n_tiles;
+  const int n_iter = (t_end - t_begin + KG - 1) / KG;   // <= T; the same in every group
+
+  float4 qraw[8];
+  load_q(a, qi, j, g, w, qraw);
+  const QueryView v = query_view(a, qi);
+  int32_t id[T];
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    const int t = t_begin + kg + KG * i;
+    id[i] = slot_id(v, a.k, t, t < t_end, j);
+  }
+  RawKey rk[T];
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    const int t = t_begin + kg + KG * i;
+    rk[i] = load_tile_any(v, a, t, t < t_end, j, g, w, id[i]);
+  }
+  f16x8 qh[4], ql[4];
+  split_q(qraw, a.c_log2, qh, ql);
+
+  AttnState st;
+  state_init(st);
+  uint8_t* krow = lds.loop.k[AT_WAVES * kg + w];
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    if (i >= n_iter) break;   // block-uniform
+    const int t = t_begin + kg + KG * i;
+    attn_tile(tile_kind(t, a.k), st, rk[i], qh, ql, krow, lds.loop.s[i & 1][kg], w, lane, j, g);
+  }
+  attn_finish<KG>(lds, st, a, qi, split, kg, w, lane, j, g);
+}
+
+// ---------------------------------------------------------------------------
+// Stream kernel: block (split, query) of KG key groups walks the split's
+// tiles t_begin + kg + KG i; key bytes DEPTH tiles ahead, slot ids 2 DEPTH
+// ahead.  One group: four waves per SIMD (registers capped at 128, no
+// spills); two groups (two tiles in flight): three waves per SIMD.
+template <int KG> constexpr int stream_depth() { return KG == 1 ? 1 : 2; }
+
+template <int KG>
+__global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu(KG == 1 ? 4 : 3))) void attn_stream_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) AttnLds<KG> lds;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = (tid >> 6) & (AT_WAVES - 1);
+  const int kg = __builtin_amdgcn_readfirstlane(tid >> 8);
+  constexpr int DEPTH = stream_depth<KG>();
+  const int j = lane & 15, g = lane >> 4;
+  const int64_t qi = blockIdx.y;
+  const int split = blockIdx.x;
+  const int n_tiles = (a.k + NWIN + AT_TILE - 1) / AT_TILE;
+  const int t_begin = split * a.tiles_per_split;
+  int t_end = t_begin + a.tiles_per_split;
+  t_end = t_end < n_tiles ? t_end : n_tiles;
+  // group kg takes tiles t_begin + kg + KG i; every group runs n_iter rounds
+  // (a round past t_end is all padding), so the block barriers line up
+  const int n_iter = (t_end - t_begin + KG - 1) / KG;
+  auto tile = [&](int i) { return t_begin + kg + KG * i; };
+
+  float4 qraw[8];
+  load_q(a, qi, j, g, w, qraw);
+  const QueryView v = query_view(a, qi);
+  int32_t id_ahead[DEPTH];
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i) id_ahead[i] = slot_id(v, a.k, tile(DEPTH + i), tile(DEPTH + i) < t_end, j);
+  RawKey ring[DEPTH];
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i)
+    ring[i] = load_tile_any(v, a, tile(i), tile(i) < t_end, j, g, w, slot_id(v, a.k, tile(i), tile(i) < t_end, j));
+  f16x8 qh[4], ql[4];
+  split_q(qraw, a.c_log2, qh, ql);
+
+  AttnState st;
+  state_init(st);
+  uint8_t* krow = lds.loop.k[AT_WAVES * kg + w];
+  for (int it = 0; it < n_iter; ++it) {
+    const RawKey cur = ring[0];
+#pragma unroll
+    for (int i = 0; i + 1 < DEPTH; ++i) ring[i] = ring[i + 1];
+    const int tn = tile(it + DEPTH);
+    ring[DEPTH - 1] = load_tile_any(v, a, tn, tn < t_end, j, g, w, id_ahead[0]);
+#pragma unroll
+    for (int i = 0; i + 1 < DEPTH; ++i) id_ahead[i] = id_ahead[i + 1];
+    const int ti = tile(it + 2 * DEPTH);
+    id_ahead[DEPTH - 1] = slot_id(v, a.k, ti, ti < t_end, j);
+    attn_tile(tile_kind(tile(it), a.k), st, cur, qh, ql, krow, lds.loop.s[it & 1][kg], w, lane, j, g);
+  }
+  attn_finish<KG>(lds, st, a, qi, split, kg, w, lane, j, g);
 }
 
 // out[q, h, :] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.  One block of
@@ -475,30 +618,56 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
 }
 
 namespace {
+
+// Launch plan.  kind 0: split kernel (KG groups x T tiles per block, all
+// loaded up front); kind 1: stream kernel.
 struct AttnPlan {
-  int kg, n_splits, tiles_per_split;
+  int kind, kg, t, n_splits, tiles_per_split;
 };
 
-// Below 512 queries (decode batches) a query's slots go to 4 splits of two
-// key groups each: the first tile's dependent gather (slot id, then the
-// entry bytes) dominates a block's time, so each group takes several tiles,
-// and four partials per query keep the combine small.  From 512 queries on,
-// one group and one split per query (no partials).
+#ifndef CSA_ATTN_SPLIT_KG
+#define CSA_ATTN_SPLIT_KG 2
+#endif
+#ifndef CSA_ATTN_SPLIT_T
+#define CSA_ATTN_SPLIT_T 2
+#endif
+constexpr int SPLIT_KG = CSA_ATTN_SPLIT_KG;     // key groups per split block
+constexpr int SPLIT_T = CSA_ATTN_SPLIT_T;       // tiles per group, loaded up front
+
+// Below 512 queries (decode batches) a query's tiles go to splits of
+// SPLIT_KG x SPLIT_T tiles when that needs at most AT_MAX_SPLITS splits (k up
+// to ~1K); each group then holds every key it uses in registers before
+// computing, and there are enough blocks to cover the compute units.  Longer
+// selections stream in 4 splits of two groups.  From 512 queries on
+// (prefill) one group streams every tile of its query (no partials).
 AttnPlan attn_plan(int64_t Q, int32_t k) {
   const int n_tiles = (k + NWIN + AT_TILE - 1) / AT_TILE;
+  AttnPlan pl;
+  if (Q < 512) {
+    const int per = SPLIT_KG * SPLIT_T;
+    const int s = (n_tiles + per - 1) / per;
+    if (s <= AT_MAX_SPLITS) {
+      pl.kind = 0;
+      pl.kg = SPLIT_KG;
+      pl.t = SPLIT_T;
+      pl.tiles_per_split = per;
+      pl.n_splits = s;
+      return pl;
+    }
+  }
   int kg = 1, want = 1;
   if (Q < 512) {
     kg = 2;
     want = 4;
   }
-  // at least KG tiles (one per group) per split
   int max_split = n_tiles / kg;
   max_split = max_split < 1 ? 1 : max_split;
   max_split = max_split < AT_MAX_SPLITS ? max_split : AT_MAX_SPLITS;
   int s = want < max_split ? want : max_split;
   s = s < 1 ? 1 : s;
-  AttnPlan pl;
+  pl.kind = 1;
   pl.kg = kg;
+  pl.t = 0;
   pl.tiles_per_split = (n_tiles + s - 1) / s;
   pl.n_splits = (n_tiles + pl.tiles_per_split - 1) / pl.tiles_per_split;
   return pl;
@@ -534,8 +703,12 @@ hipError_t launch_sparse_attn(const float* q, const int32_t* q_pos, int64_t n_se
     a.part_ml = a.part_o + (size_t)Q * a.n_splits * HEADS * D;
   }
   const dim3 grid(a.n_splits, (unsigned)Q);
-  if (pl.kg == 2) hipLaunchKernelGGL(attn_kernel<2>, grid, dim3(AT_THREADS * 2), 0, st, a);
-  else hipLaunchKernelGGL(attn_kernel<1>, grid, dim3(AT_THREADS), 0, st, a);
+  if (pl.kind == 0)
+    hipLaunchKernelGGL((attn_split_kernel<SPLIT_KG, SPLIT_T>), grid, dim3(AT_THREADS * SPLIT_KG), 0, st, a);
+  else if (pl.kg == 2)
+    hipLaunchKernelGGL(attn_stream_kernel<2>, grid, dim3(AT_THREADS * 2), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_stream_kernel<1>, grid, dim3(AT_THREADS), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(HEADS, (unsigned)Q), dim3(128), 0, st, a.part_o, a.part_ml,

@@ -56,6 +56,7 @@ extern "C" {
 #define CSA_TOP_K 512
 #define CSA_POOL_BLOCKS 2048
 #define CSA_N_WIN 128
+#define CSA_MAX_K 16384      /* largest k / top_k the selection and attention take */
 
 typedef int32_t csa_status;
 enum {
@@ -248,7 +249,8 @@ csa_status csa_index_score(const uint8_t* q_fp8, const float* w, const int32_t* 
  *   col_blocks (may be NULL) int32 [Q, ncols / 8]: when given, column c maps
  *   to id 8 * col_blocks[q, c / 8] + c % 8 (pooled scores; the block ids must
  *   be ascending so that id order equals column order).
- *   1 <= k <= 4096; ncols >= 1.
+ *   1 <= k <= 16384 (CSA_MAX_K); ncols >= 1.  A k at or above the number of
+ *   valid columns selects every valid column (the dense case).
  *   Workspace: csa_topk_workspace_size(Q, ncols, k).
  */
 size_t csa_topk_workspace_size(int64_t Q, int64_t ncols, int32_t k);
@@ -284,9 +286,12 @@ csa_status csa_block_pool(const float* values, int32_t is_block_max, int64_t Q, 
  *     - the window tokens max(0, p - 127) .. p, read from
  *       win uint8 [n_seq, win_cap, 512] row p % win_cap (E4M3, no scale),
  *   with one softmax of logits sm_scale * q . key.  out float32 [Q, 16, 512].
- *   Arithmetic: keys and values are exact in fp16; q is rounded to fp16;
+ *   Arithmetic: keys and values are exact in fp16; q and the softmax weights
+ *   are each carried as two fp16 halves (hi + lo, ~2^-22 relative) on the
  *   fp16 matrix cores with float32 accumulation; float32 softmax.
- *   1 <= k <= 4096.  Workspace: csa_sparse_attn_workspace_size(Q, k).
+ *   1 <= k <= 16384 (CSA_MAX_K); kv_rows < 2^23 (8,388,608 entries, a
+ *   33.5M-token context); 128 <= win_cap < 2^22 (CSA_ERR_UNSUPPORTED otherwise).
+ *   Workspace: csa_sparse_attn_workspace_size(Q, k).
  */
 size_t csa_sparse_attn_workspace_size(int64_t Q, int32_t k);
 csa_status csa_sparse_attn(const float* q, const int32_t* q_pos, int64_t n_seq, int64_t q_per_seq,
@@ -327,7 +332,8 @@ typedef struct csa_layer_args {
   const uint8_t* q_idx;    /* [Q, 8, 128] (Full, Reindex) */
   const float* w_idx;      /* [Q, 8] (Full, Reindex) */
   float sm_scale;
-  int32_t top_k;           /* k (512 for the method) */
+  int32_t top_k;           /* k (512 for the method), 1 .. 16384, and at most
+                              n_pool_blocks with build_pool */
   int32_t build_pool;      /* Full: also build the pool */
   int32_t n_pool_blocks;   /* 2048 for the method */
   int32_t* pool_blocks;    /* [Q, n_pool_blocks]: out (Full + build_pool), in (Reindex) */

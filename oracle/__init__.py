@@ -42,7 +42,7 @@ from .formats import (
 )
 from .mxfp4 import quantize, dequantize, GROUP
 from .compressor import compress, rope_rotate, compress_rope_fp32
-from .indexer import visible_entries, index_scores, pooled_entries
+from .indexer import visible_entries, index_scores, index_scores_many, pooled_entries
 from .select import topk, block_pool
 from .attention import window_positions, sparse_attention
 from .layer import LayerState, layer_full, layer_reindex, layer_reuse, window_encode, window_rebuild
@@ -51,7 +51,7 @@ __all__ = [
     "E2M1_VALUES", "e4m3_decode", "e4m3_encode", "e2m1_decode", "e2m1_encode",
     "quantize", "dequantize", "GROUP",
     "compress", "rope_rotate", "compress_rope_fp32",
-    "visible_entries", "index_scores", "pooled_entries",
+    "visible_entries", "index_scores", "index_scores_many", "pooled_entries",
     "topk", "block_pool",
     "window_positions", "sparse_attention",
     "LayerState", "layer_full", "layer_reindex", "layer_reuse", "window_encode", "window_rebuild",

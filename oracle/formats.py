@@ -18,19 +18,29 @@ import numpy as np
 # ---------------------------------------------------------------- E4M3 (FN) --
 
 
-def e4m3_decode(b):
-    """Decode E4M3FN bytes to float64.
+def _e4m3_value(b):
+    """Value of E4M3FN bytes (int array), by the format's definition.
 
     Layout: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits.
     Exponent 0 is subnormal: m/8 * 2**-6.  Byte 0x7F / 0xFF is NaN.
     """
-    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    b = np.asarray(b).astype(np.int64)
     s = (b >> 7) & 1
     e = (b >> 3) & 0xF
     m = b & 0x7
     mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
     mag = np.where((e == 15) & (m == 7), np.nan, mag)
     return np.where(s == 1, -mag, mag)
+
+
+# The definition applied once to each of the 256 bytes; decoding a large
+# array is then one table lookup per byte.
+_E4M3_TABLE = _e4m3_value(np.arange(256))
+
+
+def e4m3_decode(b):
+    """Decode E4M3FN bytes to float64 (see _e4m3_value for the layout)."""
+    return _E4M3_TABLE[np.asarray(b, dtype=np.uint8)]
 
 
 # All non-negative finite E4M3FN magnitudes, indexed by their byte (0x00..0x7E).

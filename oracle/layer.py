@@ -61,31 +61,39 @@ def window_rebuild(x_last, p_last, win_cap):
 
 
 def layer_full(codes, scales, k_fp8, q_fp8, w, q_attn, q_pos, win_fp8, sm_scale,
-               build_pool=False, k=TOP_K, n_blocks=POOL_BLOCKS, n_entries=None):
-    """Full mode for one query: score all visible entries, Top-K, attention."""
+               build_pool=False, k=TOP_K, n_blocks=POOL_BLOCKS, n_entries=None,
+               k_values=None, scores=None, attend=True):
+    """Full mode for one query: score all visible entries, Top-K, attention.
+
+    k_values: optional float64 decoded keys (rows of k_fp8); scores: optional
+    scores of the visible entries computed beforehand (index_scores_many);
+    attend=False skips the attention (out is None).
+    """
     nv = visible_entries(q_pos, n_entries if n_entries is not None else len(k_fp8))
-    scores = index_scores(q_fp8, w, np.asarray(k_fp8)[:nv])
+    if scores is None:
+        scores = index_scores(q_fp8, w, np.asarray(k_fp8)[:nv],
+                              k_values=None if k_values is None else np.asarray(k_values)[:nv])
     idx = topk(scores, k)
     pool = block_pool(scores, n_blocks, BLOCK) if build_pool else None
-    out = sparse_attention(q_attn, codes, scales, idx, win_fp8, sm_scale)
+    out = sparse_attention(q_attn, codes, scales, idx, win_fp8, sm_scale) if attend else None
     return LayerState(idx=idx, out=out, pool=pool, scores=scores)
 
 
 def layer_reindex(codes, scales, k_fp8, pool, q_fp8, w, q_attn, q_pos, win_fp8,
-                  sm_scale, k=TOP_K, n_entries=None):
+                  sm_scale, k=TOP_K, n_entries=None, k_values=None, attend=True):
     """Reindex mode: rescore with this layer's query, inside the pool if given."""
     nv = visible_entries(q_pos, n_entries if n_entries is not None else len(k_fp8))
     if pool is None:
         ids = np.arange(nv)
     else:
         ids = pooled_entries(pool, nv, BLOCK)
-    scores = index_scores(q_fp8, w, k_fp8, entries=ids)
+    scores = index_scores(q_fp8, w, k_fp8, entries=ids, k_values=k_values)
     idx = topk(scores, k, ids=ids)
-    out = sparse_attention(q_attn, codes, scales, idx, win_fp8, sm_scale)
+    out = sparse_attention(q_attn, codes, scales, idx, win_fp8, sm_scale) if attend else None
     return LayerState(idx=idx, out=out, pool=pool, scores=scores)
 
 
-def layer_reuse(codes, scales, idx, q_attn, win_fp8, sm_scale):
+def layer_reuse(codes, scales, idx, q_attn, win_fp8, sm_scale, attend=True):
     """Reuse mode: attention with the most recent Top-K indices."""
-    out = sparse_attention(q_attn, codes, scales, idx, win_fp8, sm_scale)
+    out = sparse_attention(q_attn, codes, scales, idx, win_fp8, sm_scale) if attend else None
     return LayerState(idx=np.asarray(idx), out=out)

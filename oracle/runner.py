@@ -7,8 +7,10 @@ oracle functions of this package on them; nothing here touches the GPU path.
 
 import numpy as np
 
-from .attention import window_positions
+from .attention import sparse_attention, window_positions
 from .compressor import compress, rope_rotate
+from .formats import e4m3_decode
+from .indexer import index_scores_many, visible_entries
 from .layer import layer_full, layer_reindex, layer_reuse, window_encode
 from .mxfp4 import quantize
 
@@ -68,30 +70,75 @@ class OracleStep:
         pos = window_positions(p)
         return window_encode(x[pos - first])
 
-    def query(self, qi):
-        """Per-layer oracle results for query qi: list of LayerState."""
+    def keys(self, s):
+        """Sequence s's indexer keys decoded to float64 (the latest sequence
+        asked for is kept)."""
+        if getattr(self, "_keys_s", None) != s:
+            self._keys = e4m3_decode(self.cache(s)[2])
+            self._keys_s = s
+        return self._keys
+
+    def precompute_full_scores(self, queries, batch=64):
+        """Full-layer scores of many queries of one chunk at once (prefill
+        queries of a sequence share its keys): fills a cache that query()
+        uses.  The scores equal index_scores' up to the order of the final
+        8-term weighted sum."""
+        cfg, t = self.cfg, self.wl.tensors
+        self._scores = getattr(self, "_scores", {})
+        fl = [li for li, m in enumerate(cfg.layers) if m == "F"]
+        by_seq = {}
+        for qi in queries:
+            by_seq.setdefault(qi // cfg.chunk, []).append(qi)
+        for s, qs in by_seq.items():
+            kv = self.keys(s)
+            for li in fl:
+                q8, w = _np(t["q_fp8"][li]), _np(t["w_idx"][li])
+                for b in range(0, len(qs), batch):
+                    qb = np.array(qs[b:b + batch])
+                    nvs = [visible_entries(int(t["q_pos"][qi]), cfg.entries_total) for qi in qb]
+                    sc = index_scores_many(q8[qb], w[qb], kv[:max(nvs)])
+                    for i, qi in enumerate(qb):
+                        self._scores[(int(qi), li)] = sc[i, :nvs[i]]
+
+    def query(self, qi, attend=True):
+        """Per-layer oracle results for query qi: list of LayerState
+        (attend=False: selection only, every out is None)."""
         cfg, t = self.cfg, self.wl.tensors
         s = qi // cfg.chunk
         p = int(t["q_pos"][qi])
         codes, scales, k_fp8, _ = self.cache(s)
+        kv = self.keys(s)
         per_layer = "x_win" in t
-        win = None if per_layer else self.window(s, p)
+        win = None if (per_layer or not attend) else self.window(s, p)
         n_entries = cfg.entries_total
+        cached = getattr(self, "_scores", {})
         res, idx, pool = [], None, None
         for li, mode in enumerate(cfg.layers):
-            if per_layer:
+            if per_layer and attend:
                 win = self.window(s, p, li)
-            qa = _np(t["q_attn"][li][qi])
+            qa = _np(t["q_attn"][li][qi]) if attend else None
             if mode == "F":
                 st = layer_full(codes, scales, k_fp8, _np(t["q_fp8"][li][qi]),
-                                       _np(t["w_idx"][li][qi]), qa, p, win, SM,
-                                       build_pool=cfg.build_pool, n_entries=n_entries)
+                                _np(t["w_idx"][li][qi]), qa, p, win, SM,
+                                build_pool=cfg.build_pool, n_entries=n_entries, k_values=kv,
+                                scores=cached.get((qi, li)), attend=attend)
                 pool = st.pool
             elif mode == "I":
                 st = layer_reindex(codes, scales, k_fp8, pool, _np(t["q_fp8"][li][qi]),
-                                          _np(t["w_idx"][li][qi]), qa, p, win, SM, n_entries=n_entries)
+                                   _np(t["w_idx"][li][qi]), qa, p, win, SM, n_entries=n_entries,
+                                   k_values=kv, attend=attend)
             else:
-                st = layer_reuse(codes, scales, idx, qa, win, SM)
+                st = layer_reuse(codes, scales, idx, qa, win, SM, attend=attend)
             idx = st.idx
             res.append(st)
         return res
+
+    def attention(self, qi, li, idx, codes, scales):
+        """Layer li's attention output for query qi over the given selected
+        ids and cache bytes (codes / scales of the query's sequence), with
+        the oracle's own window bytes."""
+        t = self.wl.tensors
+        s = qi // self.cfg.chunk
+        p = int(t["q_pos"][qi])
+        win = self.window(s, p, li if "x_win" in t else 0)
+        return sparse_attention(_np(t["q_attn"][li][qi]), codes, scales, idx, win, SM)

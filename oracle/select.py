@@ -37,7 +37,9 @@ def block_max(scores, block=8):
     """Max over aligned blocks of ``block`` consecutive entries (last may be partial)."""
     scores = np.asarray(scores, dtype=np.float64)
     nb = (len(scores) + block - 1) // block
-    return np.array([scores[b * block:(b + 1) * block].max() for b in range(nb)])
+    padded = np.full(nb * block, -np.inf)      # the missing tail of a partial block adds nothing
+    padded[:len(scores)] = scores
+    return padded.reshape(nb, block).max(axis=1)
 
 
 def block_pool(scores, n_blocks=2048, block=8):

@@ -80,7 +80,7 @@ def test_compress_validation(lib):
 
 def test_topk_and_pool_validation(lib):
     assert lib.csa_topk(P, 2, 100, None, 0, P, None, 0, None) == UNSUPPORTED
-    assert lib.csa_topk(P, 2, 100, None, 4097, P, None, 0, None) == UNSUPPORTED
+    assert lib.csa_topk(P, 2, 100, None, 16385, P, None, 0, None) == UNSUPPORTED   # k above CSA_MAX_K
     assert lib.csa_topk(P, 2, 100, P, 10, P, None, 0, None) == INVALID     # pooled, 100 % 8 != 0
     need = lib.csa_topk_workspace_size(2, 100000, 512)
     assert need > 0

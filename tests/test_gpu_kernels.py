@@ -468,3 +468,102 @@ def test_index_score_pooled_nothing_visible():
                                     pool_blocks=t_(pool))
         torch.cuda.synchronize()
         assert np.isneginf(np_(sc)).all()
+
+
+def _peaked_case(rng, n_seq, q_per_seq, rows, k):
+    """Selections holding two entries a, b with equal first halves (u) and
+    opposite second halves (+v, -v) at scale 1, among small entries and a
+    small window; half of the heads point at u (logit ~25-30) with a slight
+    lean to +v, so the softmax puts nearly all weight on a and b and their v
+    halves cancel in the output; the other heads are 8 x N(0,1), a peaked
+    softmax over keys of mixed sign."""
+    Q = n_seq * q_per_seq
+    codes = rng.integers(0, 256, (n_seq, rows, 256)).astype(np.uint8)
+    scales = rng.integers(0x20, 0x28, (n_seq, rows, 32)).astype(np.uint8)
+    ia, ib = 10, 20
+    mag = rng.integers(1, 8, (n_seq, 512)).astype(np.uint8)         # E2M1 magnitudes 0.5 .. 6
+    sgn = rng.integers(0, 2, (n_seq, 512)).astype(np.uint8) << 3
+    ca = mag | sgn
+    cb = ca.copy()
+    cb[:, 256:] ^= 8                                                 # opposite sign on the v half
+    codes[:, ia] = ca[:, 0::2] | (ca[:, 1::2] << 4)
+    codes[:, ib] = cb[:, 0::2] | (cb[:, 1::2] << 4)
+    scales[:, ia] = scales[:, ib] = 0x38                             # 1.0
+    win = formats.e4m3_encode(0.1 * rng.standard_normal((n_seq, 128 + q_per_seq, 512)))
+    idx = np.stack([np.sort(np.concatenate([[ia, ib], rng.choice(np.arange(30, rows), k - 2, replace=False)]))
+                    for _ in range(Q)]).astype(np.int32)
+    q = (8.0 * rng.standard_normal((Q, 16, 512))).astype(np.float64)
+    for qi in range(Q):
+        s = qi // q_per_seq
+        a = mxfp4.dequantize(codes[s, ia], scales[s, ia])
+        u, v = a.copy(), a.copy()
+        u[256:] = 0.0
+        v[:256] = 0.0
+        for h in range(8):
+            gam = rng.uniform(25, 30) * np.sqrt(512) / (u @ u)
+            dl = rng.uniform(0.0, 1.0) * np.sqrt(512) / (v @ v)
+            q[qi, h] = gam * u + dl * v
+    pos = np.array([5000 + (i % q_per_seq) for i in range(Q)], np.int32)
+    return codes, scales, win, q.astype(np.float32), idx, pos
+
+
+# decode (split plan: few queries) and prefill (stream plan: 512+ queries)
+@pytest.mark.parametrize("n_seq,q_per_seq", [(4, 1), (1, 520)])
+def test_sparse_attn_peaked_cancelling_softmax(n_seq, q_per_seq):
+    rng = np.random.default_rng(31 + q_per_seq)
+    rows, k, win_cap = 1500, 512, 128 + q_per_seq
+    codes, scales, win, q, idx, pos = _peaked_case(rng, n_seq, q_per_seq, rows, k)
+    out = ops.csa_sparse_attn(t_(q), t_(pos), t_(codes), t_(scales), t_(idx), t_(win), n_seq, q_per_seq)
+    torch.cuda.synchronize()
+    qs = range(n_seq * q_per_seq) if q_per_seq == 1 else list(range(0, 520, 13)) + [519]
+    got = np_(out)
+    for qi in qs:
+        s = qi // q_per_seq
+        wp = oracle.window_positions(pos[qi])
+        ref = oracle.sparse_attention(q[qi], codes[s], scales[s], idx[qi], win[s, wp % win_cap], SM)
+        check_attn(got[qi], ref)
+        # the case is what it claims: the u heads put more than 99% of their
+        # softmax weight on a and b (whose v halves then largely cancel)
+        kv = mxfp4.dequantize(codes[s][[10, 20]], scales[s][[10, 20]])
+        allk = np.concatenate([mxfp4.dequantize(codes[s][idx[qi]], scales[s][idx[qi]]),
+                               formats.e4m3_decode(win[s, wp % win_cap])])
+        lg = (q[qi, :8].astype(np.float64) @ allk.T) * SM
+        lab = (q[qi, :8].astype(np.float64) @ kv.T) * SM
+        wab = np.exp(lab - lg.max(-1, keepdims=True)).sum(-1) / np.exp(lg - lg.max(-1, keepdims=True)).sum(-1)
+        assert wab.min() > 0.99, wab.min()
+
+
+@pytest.mark.parametrize("n_ent,top_k", [(3000, 4096), (16000, 16384)])
+def test_full_layer_k_at_least_visible_is_dense(n_ent, top_k):
+    """Check (b) through the library: a Full layer whose Top-K covers every
+    visible entry selects all of them (ascending, -1 padded) and its
+    attention is dense attention over the compressed cache plus the window."""
+    rng = np.random.default_rng(n_ent)
+    n_seq, win_cap = 2, 128
+    codes = rng.integers(0, 256, (n_seq, n_ent, 256)).astype(np.uint8)
+    scales = rng.integers(0x28, 0x31, (n_seq, n_ent, 32)).astype(np.uint8)
+    k8 = formats.e4m3_encode(rng.standard_normal((n_seq, n_ent, 128)))
+    q8 = formats.e4m3_encode(rng.standard_normal((n_seq, 8, 128)))
+    w = rng.random((n_seq, 8)).astype(np.float32)
+    q_attn = rng.standard_normal((n_seq, 16, 512)).astype(np.float32)
+    win = formats.e4m3_encode(rng.standard_normal((n_seq, win_cap, 512)))
+    pos = np.array([4 * n_ent - 1, 4 * n_ent - 1 - 403], np.int32)      # second: a partial block
+    idx = torch.empty((n_seq, top_k), dtype=torch.int32, device=DEV)
+    out = torch.empty((n_seq, 16, 512), dtype=torch.float32, device=DEV)
+    call = ops.LayerCall(ops.MODE_FULL, codes=t_(codes), scales=t_(scales), k_fp8=t_(k8), win=t_(win),
+                         q_pos=t_(pos), q_attn=t_(q_attn), idx=idx, out=out, n_seq=n_seq, q_per_seq=1,
+                         n_entries=n_ent, q_idx=t_(q8), w_idx=t_(w), top_k=top_k)
+    call()
+    torch.cuda.synchronize()
+    gi, go = np_(idx), np_(out)
+    for s in range(n_seq):
+        nv = oracle.visible_entries(pos[s], n_ent)
+        want = np.full(top_k, -1, np.int64)
+        want[:nv] = np.arange(nv)
+        assert np.array_equal(gi[s], want), s
+        wp = oracle.window_positions(pos[s])
+        dense = oracle.sparse_attention(q_attn[s], codes[s], scales[s], np.arange(nv), win[s, wp % win_cap], SM)
+        check_attn(go[s], dense)
+        ref = oracle.layer_full(codes[s], scales[s], k8[s], q8[s], w[s], q_attn[s], pos[s], win[s, wp % win_cap],
+                                SM, k=top_k, n_entries=n_ent)
+        assert np.array_equal(ref.idx, want)

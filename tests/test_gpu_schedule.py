@@ -35,9 +35,9 @@ def test_v41_schedule_small_all_queries():
     wls, sch = run_schedule(cfgs)
     assert sum(len(c.layers) for c in cfgs) == 38
     for wl, st in zip(wls, sch.groups):
-        swaps, compared, skips = check_queries(wl, st, range(wl.cfg.n_queries))
+        r = check_queries(wl, st, range(wl.cfg.n_queries))
         n_out = wl.cfg.n_queries * len(wl.cfg.layers)
-        assert swaps <= 1 and compared >= n_out // 2, (wl.cfg.name, swaps, compared, skips)
+        assert r["swaps"] <= 1 and r["compared"] == n_out, (wl.cfg.name, r)
     # every layer's own window ring, bit-exact
     for wl, st in zip(wls, sch.groups):
         ref = OracleStep(wl)
@@ -66,11 +66,16 @@ def test_v41_schedule_layers_differ():
 
 
 def test_v41_schedule_1m_decode_sampled():
+    """The 1M-context, batch-32 schedule: every query's pool and Top-K in each
+    group, attention on 16 sampled queries (every layer) per group."""
     name = "decode_b32_1m_v41_38layers"
     cfgs = W.v41_schedule(**W.SCHEDULES[name])
     wls, sch = run_schedule(cfgs)
-    for wl, st in zip(wls, sch.groups):
-        swaps, compared, skips = check_queries(wl, st, [0, 31])
-        assert swaps <= 1 and compared >= 1, (wl.cfg.name, swaps, compared, skips)
+    for g, (wl, st) in enumerate(zip(wls, sch.groups)):
+        qa = sorted(np.random.default_rng(g).choice(wl.cfg.n_queries, 16, replace=False).tolist())
+        r = check_queries(wl, st, range(wl.cfg.n_queries), attn_queries=qa)
+        print(f"[parity] {wl.cfg.name}: {r}", flush=True)
+        n_sel = wl.cfg.n_queries * sum(m in ("F", "I") for m in wl.cfg.layers)
+        assert r["swaps"] <= max(1, n_sel // 50) and r["compared"] == 16 * len(wl.cfg.layers), (wl.cfg.name, r)
     del sch, wls
     torch.cuda.empty_cache()

@@ -137,3 +137,56 @@ def test_reindex_with_full_query_reproduces_full_topk():
     re = layer_reindex(codes, scales, k_fp8, full.pool, q, w, qa, p, win, 512 ** -0.5, k=64)
     assert np.array_equal(full.idx, re.idx)
     np.testing.assert_array_equal(full.out, re.out)
+
+
+def test_pooled_entries_partial_last_block():
+    """Hand-enumerated candidates of a pool whose blocks end at, inside and
+    past the visible prefix: a prefill query that sees 43 entries sees
+    entries 40..42 of block 5 and nothing of blocks 6 and up; -1 slots are
+    empty (the pool holds 8-entry blocks; a query sees only entries whose
+    last token precedes it)."""
+    got = indexer.pooled_entries(np.array([0, 3, 5, 6, 11, -1, -1]), 43)
+    want = list(range(0, 8)) + list(range(24, 32)) + [40, 41, 42]
+    assert got.tolist() == want
+    assert indexer.pooled_entries(np.array([2, 9]), 20).tolist() == [16, 17, 18, 19]
+    assert indexer.pooled_entries(np.array([5]), 40).tolist() == []       # block 5 starts at the prefix end
+    assert indexer.pooled_entries(np.array([5]), 41).tolist() == [40]
+    assert indexer.pooled_entries(np.array([4]), 40).tolist() == list(range(32, 40))
+    assert indexer.pooled_entries(np.array([-1, -1]), 100).tolist() == []
+
+
+def test_reindex_never_scores_invisible_pool_entries():
+    """A prefill query whose visible prefix ends inside a pool block: the
+    Reindex candidates stop at the prefix, so with K above the candidate
+    count the selection is exactly the visible pool entries, and the scores
+    are those of the visible entries only."""
+    rng = np.random.default_rng(12)
+    n = 200
+    k_fp8 = e4m3_bytes(rng, (n, 128))
+    q = e4m3_bytes(rng, (8, 128))
+    w = rng.random(8).astype(np.float32)
+    codes = rng.integers(0, 256, (n, 256)).astype(np.uint8)
+    scales = rng.integers(0x28, 0x31, (n, 32)).astype(np.uint8)
+    qa = rng.standard_normal((16, 512)).astype(np.float32)
+    win = e4m3_bytes(rng, (128, 512))
+    p = 4 * 45 + 2                       # sees entries 0..44 (45 entries): block 5 holds 40..44
+    pool = np.array([1, 5, 7, 20, -1])   # block 7 and 20 lie past the prefix
+    re = layer_reindex(codes, scales, k_fp8, pool, q, w, qa, p, win, 512 ** -0.5, k=64)
+    want = list(range(8, 16)) + [40, 41, 42, 43, 44]
+    assert re.idx[:len(want)].tolist() == want and np.all(re.idx[len(want):] == -1)
+    assert len(re.scores) == len(want)
+    np.testing.assert_array_equal(re.scores, indexer.index_scores(q, w, k_fp8[want]))
+
+
+def test_index_scores_many_equals_one_query_at_a_time():
+    """The batched scoring of a chunk's queries (shared keys) gives each
+    query's index_scores up to the order of the final 8-term sum."""
+    rng = np.random.default_rng(13)
+    k_fp8 = e4m3_bytes(rng, (300, 128))
+    q = e4m3_bytes(rng, (5, 8, 128))
+    w = rng.random((5, 8)).astype(np.float32)
+    many = indexer.index_scores_many(q, w, torch_decode(k_fp8))
+    for i in range(5):
+        one = indexer.index_scores(q[i], w[i], k_fp8)
+        np.testing.assert_allclose(many[i], one, rtol=1e-15, atol=0)
+        np.testing.assert_array_equal(indexer.index_scores(q[i], w[i], k_fp8, k_values=torch_decode(k_fp8)), one)
