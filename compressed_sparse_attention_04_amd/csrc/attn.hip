@@ -31,7 +31,9 @@
 //      column c is 128 w + 8 c + n: 16 contiguous bytes per key).
 // Key bytes are read through buffer views of the query's rows: an absent
 // key (a -1 id, an id past the cache, a window position before 0, padding)
-// reads past the view and gets zeros, so no load sits under a branch.
+// reads past the view and gets zeros, so no load sits under a branch: every
+// slot issues its entry loads and its window loads, and the one that is not
+// its kind returns zeros.
 //
 // Two launch shapes:
 //   * split (decode batches): a query's tiles are cut into splits of KG x T
@@ -70,6 +72,7 @@ struct AttnArgs {
   const uint8_t* win;
   int64_t win_cap;
   float c_log2;          // sm_scale * log2(e)
+  int64_t n_queries;
   float* out;
   float* part_o;         // [Q, n_splits, 16, 512] (n_splits > 1)
   float* part_ml;        // [Q, n_splits, 2, 16]
@@ -121,14 +124,15 @@ __device__ __forceinline__ QueryView query_view(const AttnArgs& a, int64_t qi) {
   return v;
 }
 
-// Entry id of this lane's slot j in tile t (-1: not an entry slot or past
-// the tiles in use).  The load is unconditional (a slot past k reads past the
-// index view and gets 0, which the slot test then discards).
+// The index-array word of this lane's slot j in tile t, loaded
+// unconditionally: a slot that is not an entry slot (or a tile past the ones
+// in use) reads past the index view and gets 0, which load_slot's own slot
+// test discards.  (Applying that test here would put the result under a
+// branch and make the compiler wait for the load on the spot.)
 __device__ __forceinline__ int32_t slot_id(const QueryView& v, int k, int t, bool live, int j) {
   const int slot = t * AT_TILE + j;
   const uint32_t off = (live && slot < k) ? (uint32_t)slot * 4u : AT_OOB;
-  const int32_t id = __builtin_amdgcn_raw_buffer_load_b32(v.idx, off, 0, 0);
-  return (live && slot < k) ? id : -1;
+  return __builtin_amdgcn_raw_buffer_load_b32(v.idx, off, 0, 0);
 }
 
 __device__ __forceinline__ uint4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -136,51 +140,36 @@ __device__ __forceinline__ uint4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t of
   return make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
 }
 
-// The lane's bytes of tile t (TK = the tile's kind, the same in every lane).
-// Every load is issued unconditionally; an absent key reads past its view.
-template <int TK>
-__device__ __forceinline__ RawKey load_tile(const QueryView& v, const AttnArgs& a, int t, bool live, int j, int g,
-                                            int w, int32_t id) {
-  RawKey r;
-  r.a = make_uint4(0u, 0u, 0u, 0u);
-  r.b = make_uint4(0u, 0u, 0u, 0u);
-  r.sc = 0u;
-  r.kind = 0;
-  const int slot = t * AT_TILE + j;
-  if constexpr (TK != TK_WINDOW) {
-    const bool ok = live && (TK == TK_ENTRY || slot < a.k) && id >= 0 && id < a.kv_rows;
-    const uint32_t oc = ok ? (uint32_t)id * CODE_BYTES + 64u * w + 16u * g : AT_OOB;
-    const uint32_t os = ok ? (uint32_t)id * SCALE_BYTES + 8u * w + 2u * g : AT_OOB;
-    r.a = load_b128(v.codes, oc);
-    r.sc = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(v.scales, os, 0, 0);
-    r.kind = ok ? 1 : 0;
-  }
-  if constexpr (TK != TK_ENTRY) {
-    const int wi = slot - a.k;
-    const bool ok = live && wi >= 0 && wi < NWIN && v.p - (NWIN - 1) + wi >= 0;
-    int row = v.wbase + wi;
-    row = row >= v.win_cap ? row - v.win_cap : row;
-    const uint32_t ow = ok ? (uint32_t)row * D + AT_QCH * w + 32u * g : AT_OOB;
-    const uint4 wa = load_b128(v.win, ow), wb = load_b128(v.win, ow + 16u);
-    if constexpr (TK == TK_WINDOW) {
-      r.a = wa;
-      r.b = wb;
-      r.kind = ok ? 2 : 0;
-    } else {
-      r.a = ok ? wa : r.a;
-      r.b = wb;                         // zero unless ok
-      r.kind = ok ? 2 : r.kind;
-    }
-  }
-  return r;
+// The lane's bytes of slot j of tile t: the code and scale bytes of its
+// entry and the bytes of its window token.  All four loads are issued in
+// every lane (straight-line code: no register of a load in flight is copied
+// at a branch join, and the compiler counts the loads in flight instead of
+// waiting); a slot that is not an entry (or not a window token) reads past
+// that view and gets zeros, so OR-ing the code and window bytes keeps
+// whichever the slot is.
+__device__ __forceinline__ uint4 or4(uint4 x, uint4 y) {
+  return make_uint4(x.x | y.x, x.y | y.y, x.z | y.z, x.w | y.w);
 }
-
-__device__ __forceinline__ RawKey load_tile_any(const QueryView& v, const AttnArgs& a, int t, bool live, int j,
-                                                int g, int w, int32_t id) {
-  const int tk = tile_kind(t, a.k);   // wave-uniform: a scalar branch
-  if (tk == TK_ENTRY) return load_tile<TK_ENTRY>(v, a, t, live, j, g, w, id);
-  if (tk == TK_WINDOW) return load_tile<TK_WINDOW>(v, a, t, live, j, g, w, id);
-  return load_tile<TK_MIXED>(v, a, t, live, j, g, w, id);
+__device__ __forceinline__ RawKey load_slot(const QueryView& v, const AttnArgs& a, int t, bool live, int j, int g,
+                                            int w, int32_t id) {
+  const int slot = t * AT_TILE + j;
+  const bool ent = live && slot < a.k && id >= 0 && id < a.kv_rows;
+  const int wi = slot - a.k;
+  const bool win = live && wi >= 0 && wi < NWIN && v.p - (NWIN - 1) + wi >= 0;
+  int row = v.wbase + wi;
+  row = row >= v.win_cap ? row - v.win_cap : row;
+  const uint32_t oc = ent ? (uint32_t)id * CODE_BYTES + 64u * w + 16u * g : AT_OOB;
+  const uint32_t os = ent ? (uint32_t)id * SCALE_BYTES + 8u * w + 2u * g : AT_OOB;
+  const uint32_t ow = win ? (uint32_t)row * D + AT_QCH * w + 32u * g : AT_OOB;
+  const uint4 c = load_b128(v.codes, oc);
+  const uint32_t sc = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(v.scales, os, 0, 0);
+  const uint4 wa = load_b128(v.win, ow), wb = load_b128(v.win, ow + 16u);
+  RawKey r;
+  r.a = or4(c, wa);
+  r.b = wb;
+  r.sc = sc;
+  r.kind = ent ? 1 : (win ? 2 : 0);
+  return r;
 }
 
 // Channels 8 s .. 8 s + 7 of the lane's 32 as fp16 (exact), k-step s < 4.
@@ -376,8 +365,8 @@ __device__ __forceinline__ void attn_tile(int tk, AttnState& st, const RawKey& c
 // Merge the KG groups' states (group 0 keeps the result; the others return
 // false) and write the block's result: the output when the query has one
 // split, else the split's partial (O unnormalized, max, sum).
-template <int KG>
-__device__ __forceinline__ void attn_finish(AttnLds<KG>& lds, AttnState& st, const AttnArgs& a, int64_t qi,
+template <int KG, class Lds>
+__device__ __forceinline__ void attn_finish(Lds& lds, AttnState& st, const AttnArgs& a, int64_t qi,
                                             int split, int kg, int w, int lane, int j, int g) {
   st.l_run = sum_xor32(sum_xor16(st.l_run));   // head j's sum over all keys of this group
   // lane holds O[head 4g + r][channel 128 w + 8 j + n]; m_run, l_run are head j's
@@ -471,52 +460,218 @@ __device__ __forceinline__ void attn_finish(AttnLds<KG>& lds, AttnState& st, con
 }
 
 // ---------------------------------------------------------------------------
-// Split kernel: block (split, query) holds KG key groups; group kg takes the
-// split's tiles t_begin + kg + KG i, i < T, and issues the loads of all of
-// them (slot ids, then key bytes) before its first tile.
-template <int KG, int T>
-__global__ __launch_bounds__(AT_THREADS * KG) void attn_split_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) AttnLds<KG> lds;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = (tid >> 6) & (AT_WAVES - 1);
-  const int kg = __builtin_amdgcn_readfirstlane(tid >> 8);   // wave-uniform
-  const int j = lane & 15, g = lane >> 4;
-  const int64_t qi = blockIdx.y;
-  const int split = blockIdx.x;
-  const int n_tiles = (a.k + NWIN + AT_TILE - 1) / AT_TILE;
-  const int t_begin = split * a.tiles_per_split;
-  int t_end = t_begin + a.tiles_per_split;
-  t_end = t_end < n_tiles ? t_end : n_tiles;
-  const int n_iter = (t_end - t_begin + KG - 1) / KG;   // <= T; the same in every group
+// Split kernel: block (query, split) holds KG key groups; group kg takes the
+// split's tiles t_begin + kg + KG i, i < T.  A group issues the loads of all
+// its tiles first (slot ids, then key bytes), then runs them as one batch:
+// the partial S of every tile, one barrier for the four waves' partials, one
+// softmax over all the group's keys (its exact max first, so no rescaling),
+// then P V tile by tile (the key slices are widened again from the
+// registers into the wave's LDS rows, which only the P V transpose needs).
+// The dependent chain per block is one load round trip, one barrier and one
+// softmax, however many tiles the group holds.
+//
+// A block whose tiles are all selected entries (or all window tokens) loads
+// only that kind of bytes; a block holding both (or the mixed tile) loads
+// every slot's entry and window bytes (load_slot).
+constexpr int PATH_ENTRY = 0, PATH_WINDOW = 1, PATH_ANY = 2;
 
-  float4 qraw[8];
-  load_q(a, qi, j, g, w, qraw);
+template <int PATH>
+__device__ __forceinline__ RawKey load_slot_p(const QueryView& v, const AttnArgs& a, int t, bool live, int j, int g,
+                                              int w, int32_t id) {
+  if constexpr (PATH == PATH_ANY) {
+    return load_slot(v, a, t, live, j, g, w, id);
+  } else {
+    RawKey r;
+    r.a = make_uint4(0u, 0u, 0u, 0u);
+    r.b = make_uint4(0u, 0u, 0u, 0u);
+    r.sc = 0u;
+    const int slot = t * AT_TILE + j;
+    if constexpr (PATH == PATH_ENTRY) {
+      const bool ent = live && slot < a.k && id >= 0 && id < a.kv_rows;
+      const uint32_t oc = ent ? (uint32_t)id * CODE_BYTES + 64u * w + 16u * g : AT_OOB;
+      const uint32_t os = ent ? (uint32_t)id * SCALE_BYTES + 8u * w + 2u * g : AT_OOB;
+      r.a = load_b128(v.codes, oc);
+      r.sc = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(v.scales, os, 0, 0);
+      r.kind = ent ? 1 : 0;
+    } else {
+      const int wi = slot - a.k;
+      const bool win = live && wi >= 0 && wi < NWIN && v.p - (NWIN - 1) + wi >= 0;
+      int row = v.wbase + wi;
+      row = row >= v.win_cap ? row - v.win_cap : row;
+      const uint32_t ow = win ? (uint32_t)row * D + AT_QCH * w + 32u * g : AT_OOB;
+      r.a = load_b128(v.win, ow);
+      r.b = load_b128(v.win, ow + 16u);
+      r.kind = win ? 2 : 0;
+    }
+    return r;
+  }
+}
+
+// Key slice s of a slot for a block of the given PATH (t's kind decides
+// inside a PATH_ANY block; a scalar branch).
+template <int PATH>
+__device__ __forceinline__ f16x8 path_slice(int tk, const RawKey& r, int s) {
+  if constexpr (PATH == PATH_ENTRY) return entry_slice(r, s);
+  else if constexpr (PATH == PATH_WINDOW) return window_slice(r, s);
+  else {
+    if (tk == TK_ENTRY) return entry_slice(r, s);
+    if (tk == TK_WINDOW) return window_slice(r, s);
+    return r.kind == 2 ? window_slice(r, s) : entry_slice(r, s);
+  }
+}
+
+template <int KG, int T>
+struct SplitLds {
+  union {
+    struct {
+      uint8_t k[KG * AT_WAVES][AT_TILE * AT_KPITCH];   // one tile's fp16 key slices per wave (P V)
+      f32x4 s[T][KG][AT_WAVES][64];                      // partial S of every tile
+    } loop;
+    struct {
+      float o[KG > 1 ? KG - 1 : 1][AT_WAVES][32][64];     // scaled O of groups 1..KG-1
+      float ml[KG][2][HEADS];                            // (max, sum) per group and head
+    } red;
+  };
+};
+
+template <int KG, int T, int PATH>
+__device__ __forceinline__ void split_body(SplitLds<KG, T>& lds, const AttnArgs& a, int64_t qi, int split,
+                                           int t_begin, int t_end, int kg, int w, int lane, int j, int g) {
+  const int n_iter = (t_end - t_begin + KG - 1) / KG;   // <= T; the same in every group
+  // slot ids first, then Q: waiting for the ids (to address the keys) does
+  // not wait for Q
   const QueryView v = query_view(a, qi);
   int32_t id[T];
 #pragma unroll
   for (int i = 0; i < T; ++i) {
     const int t = t_begin + kg + KG * i;
-    id[i] = slot_id(v, a.k, t, t < t_end, j);
+    id[i] = PATH == PATH_WINDOW ? -1 : slot_id(v, a.k, t, t < t_end, j);
   }
+  float4 qraw[8];
+  load_q(a, qi, j, g, w, qraw);
   RawKey rk[T];
 #pragma unroll
   for (int i = 0; i < T; ++i) {
     const int t = t_begin + kg + KG * i;
-    rk[i] = load_tile_any(v, a, t, t < t_end, j, g, w, id[i]);
+    rk[i] = load_slot_p<PATH>(v, a, t, t < t_end, j, g, w, id[i]);
   }
   f16x8 qh[4], ql[4];
   split_q(qraw, a.c_log2, qh, ql);
 
-  AttnState st;
-  state_init(st);
-  uint8_t* krow = lds.loop.k[AT_WAVES * kg + w];
+  // ---- partial S of every tile (A operand straight from the registers) ----
 #pragma unroll
   for (int i = 0; i < T; ++i) {
     if (i >= n_iter) break;   // block-uniform
-    const int t = t_begin + kg + KG * i;
-    attn_tile(tile_kind(t, a.k), st, rk[i], qh, ql, krow, lds.loop.s[i & 1][kg], w, lane, j, g);
+    const int tk = tile_kind(t_begin + kg + KG * i, a.k);
+    f32x4 sh = {0.f, 0.f, 0.f, 0.f}, sl = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f16x8 av = path_slice<PATH>(tk, rk[i], s);
+      sh = mfma_f16_16x16x32(av, qh[s], sh);
+      sl = mfma_f16_16x16x32(av, ql[s], sl);
+    }
+    lds.loop.s[i][kg][w][lane] = f32x4{sh[0] + sl[0], sh[1] + sl[1], sh[2] + sl[2], sh[3] + sl[3]};
+  }
+  __syncthreads();
+
+  // ---- one softmax over the group's keys (lane: head j, keys 4g + r) ------
+  float x[T][4];
+  float mx = -__builtin_huge_valf();
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    if (i < n_iter) {
+      f32x4 S = lds.loop.s[i][kg][0][lane];
+#pragma unroll
+      for (int vv = 1; vv < AT_WAVES; ++vv) {
+        const f32x4 o = lds.loop.s[i][kg][vv][lane];
+        S[0] += o[0]; S[1] += o[1]; S[2] += o[2]; S[3] += o[3];
+      }
+      const uint32_t vmask = (uint32_t)(__ballot(rk[i].kind != 0) & 0xFFFFull);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[i][r] = ((vmask >> (4 * g + r)) & 1u) ? S[r] : -__builtin_huge_valf();
+        mx = fmaxf(mx, x[i][r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[i][r] = -__builtin_huge_valf();
+    }
+  }
+  mx = max_xor32(max_xor16(mx));   // head j's max over the group's keys
+  const float base = (mx == -__builtin_huge_valf()) ? 0.f : mx;
+  AttnState st;
+  state_init(st);
+  st.m_run = mx;
+  f16x4 ph[T], pl[T];
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float pr = exp2_loop(x[i][r] - base);   // <= 1; 0 for an absent key
+      const _Float16 h = (_Float16)pr;
+      const _Float16 l = (_Float16)(pr - (float)h);
+      ph[i][r] = h;
+      pl[i][r] = l;
+      st.l_run += (float)h + (float)l;
+    }
+  }
+
+  // ---- P V tile by tile -----------------------------------------------------
+  uint8_t* krow = lds.loop.k[AT_WAVES * kg + w];
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    if (i >= n_iter) break;
+    const int tk = tile_kind(t_begin + kg + KG * i, a.k);
+    __builtin_amdgcn_wave_barrier();   // the previous tile's LDS reads come first
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      *reinterpret_cast<f16x8*>(krow + j * AT_KPITCH + 64 * g + 16 * s) = path_slice<PATH>(tk, rk[i], s);
+    __builtin_amdgcn_wave_barrier();   // stores before the transposed reads (LDS keeps wave order)
+    uint4 vk[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) vk[kk] = *reinterpret_cast<const uint4*>(krow + (4 * g + kk) * AT_KPITCH + 16 * j);
+    const uint32_t w0[4] = {vk[0].x, vk[0].y, vk[0].z, vk[0].w};
+    const uint32_t w1[4] = {vk[1].x, vk[1].y, vk[1].z, vk[1].w};
+    const uint32_t w2[4] = {vk[2].x, vk[2].y, vk[2].z, vk[2].w};
+    const uint32_t w3[4] = {vk[3].x, vk[3].y, vk[3].z, vk[3].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f16x2 a0 = bits_f16x2(__builtin_amdgcn_perm(w1[c], w0[c], 0x05040100u));
+      const f16x2 a1 = bits_f16x2(__builtin_amdgcn_perm(w3[c], w2[c], 0x05040100u));
+      const f16x2 b0 = bits_f16x2(__builtin_amdgcn_perm(w1[c], w0[c], 0x07060302u));
+      const f16x2 b1 = bits_f16x2(__builtin_amdgcn_perm(w3[c], w2[c], 0x07060302u));
+      const f16x4 blo = {a0[0], a0[1], a1[0], a1[1]};
+      const f16x4 bhi = {b0[0], b0[1], b1[0], b1[1]};
+      st.acc_o[2 * c] = mfma_f16_16x16x16(ph[i], blo, st.acc_o[2 * c]);
+      st.acc_o[2 * c + 1] = mfma_f16_16x16x16(ph[i], bhi, st.acc_o[2 * c + 1]);
+      st.acc_o[2 * c] = mfma_f16_16x16x16(pl[i], blo, st.acc_o[2 * c]);
+      st.acc_o[2 * c + 1] = mfma_f16_16x16x16(pl[i], bhi, st.acc_o[2 * c + 1]);
+    }
   }
   attn_finish<KG>(lds, st, a, qi, split, kg, w, lane, j, g);
+}
+
+template <int KG, int T>
+__global__ __launch_bounds__(AT_THREADS * KG) void attn_split_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) SplitLds<KG, T> lds;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = (tid >> 6) & (AT_WAVES - 1);
+  const int kg = __builtin_amdgcn_readfirstlane(tid >> 8);   // wave-uniform
+  const int j = lane & 15, g = lane >> 4;
+  const int64_t qi = blockIdx.x;   // query in x: see attn_grid
+  const int split = blockIdx.y;
+  if (qi >= a.n_queries) return;  // grid padding (the whole block)
+  const int n_tiles = (a.k + NWIN + AT_TILE - 1) / AT_TILE;
+  const int t_begin = split * a.tiles_per_split;
+  int t_end = t_begin + a.tiles_per_split;
+  t_end = t_end < n_tiles ? t_end : n_tiles;
+  const int k0 = tile_kind(t_begin, a.k), k1 = tile_kind(t_end - 1, a.k);   // block-uniform
+  if (k0 == TK_ENTRY && k1 == TK_ENTRY)
+    split_body<KG, T, PATH_ENTRY>(lds, a, qi, split, t_begin, t_end, kg, w, lane, j, g);
+  else if (k0 == TK_WINDOW && k1 == TK_WINDOW)
+    split_body<KG, T, PATH_WINDOW>(lds, a, qi, split, t_begin, t_end, kg, w, lane, j, g);
+  else
+    split_body<KG, T, PATH_ANY>(lds, a, qi, split, t_begin, t_end, kg, w, lane, j, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -534,8 +689,9 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
   const int kg = __builtin_amdgcn_readfirstlane(tid >> 8);
   constexpr int DEPTH = stream_depth<KG>();
   const int j = lane & 15, g = lane >> 4;
-  const int64_t qi = blockIdx.y;
-  const int split = blockIdx.x;
+  const int64_t qi = blockIdx.x;   // query in x: see attn_grid
+  const int split = blockIdx.y;
+  if (qi >= a.n_queries) return;  // grid padding (the whole block)
   const int n_tiles = (a.k + NWIN + AT_TILE - 1) / AT_TILE;
   const int t_begin = split * a.tiles_per_split;
   int t_end = t_begin + a.tiles_per_split;
@@ -545,16 +701,17 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
   const int n_iter = (t_end - t_begin + KG - 1) / KG;
   auto tile = [&](int i) { return t_begin + kg + KG * i; };
 
-  float4 qraw[8];
-  load_q(a, qi, j, g, w, qraw);
   const QueryView v = query_view(a, qi);
-  int32_t id_ahead[DEPTH];
+  int32_t id0[DEPTH], id_ahead[DEPTH];
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i) id0[i] = slot_id(v, a.k, tile(i), tile(i) < t_end, j);
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i) id_ahead[i] = slot_id(v, a.k, tile(DEPTH + i), tile(DEPTH + i) < t_end, j);
+  float4 qraw[8];
+  load_q(a, qi, j, g, w, qraw);
   RawKey ring[DEPTH];
 #pragma unroll
-  for (int i = 0; i < DEPTH; ++i)
-    ring[i] = load_tile_any(v, a, tile(i), tile(i) < t_end, j, g, w, slot_id(v, a.k, tile(i), tile(i) < t_end, j));
+  for (int i = 0; i < DEPTH; ++i) ring[i] = load_slot(v, a, tile(i), tile(i) < t_end, j, g, w, id0[i]);
   f16x8 qh[4], ql[4];
   split_q(qraw, a.c_log2, qh, ql);
 
@@ -566,7 +723,7 @@ __global__ __launch_bounds__(AT_THREADS * KG) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int i = 0; i + 1 < DEPTH; ++i) ring[i] = ring[i + 1];
     const int tn = tile(it + DEPTH);
-    ring[DEPTH - 1] = load_tile_any(v, a, tn, tn < t_end, j, g, w, id_ahead[0]);
+    ring[DEPTH - 1] = load_slot(v, a, tn, tn < t_end, j, g, w, id_ahead[0]);
 #pragma unroll
     for (int i = 0; i + 1 < DEPTH; ++i) id_ahead[i] = id_ahead[i + 1];
     const int ti = tile(it + 2 * DEPTH);
@@ -583,9 +740,11 @@ constexpr int AT_MAX_SPLITS = 16;
 
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
-                                                           int n_splits, float* __restrict__ out) {
-  const int64_t qi = blockIdx.y;
-  const int h = blockIdx.x;
+                                                           int n_splits, int64_t n_queries,
+                                                           float* __restrict__ out) {
+  const int64_t qi = blockIdx.x;   // query in x: see attn_grid
+  const int h = blockIdx.y;
+  if (qi >= n_queries) return;
   float m[AT_MAX_SPLITS], l[AT_MAX_SPLITS];
   float4 o[AT_MAX_SPLITS];
 #pragma unroll
@@ -619,6 +778,19 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
 
 namespace {
 
+// XCD-aware grid: the hardware hands workgroups to the eight XCDs round
+// robin by linear workgroup id (x fastest), and each XCD has its own L2.
+// With the query in x and x padded to a multiple of 8, linear id
+// y * gridDim.x + x falls on XCD x % 8 for every y: all splits of a query
+// (and, in the combine, all its heads) run on one XCD, so the query's Q is
+// fetched from HBM once and re-read from that L2, the split partials are
+// read back by the combine from the same L2, and the selection kernels
+// (one block per query, x = query) left the query's ids in it too.
+dim3 attn_grid(int64_t Q, int y) {
+  const int64_t xq = (Q + 7) / 8 * 8;
+  return dim3((unsigned)xq, (unsigned)y);
+}
+
 // Launch plan.  kind 0: split kernel (KG groups x T tiles per block, all
 // loaded up front); kind 1: stream kernel.
 struct AttnPlan {
@@ -626,20 +798,28 @@ struct AttnPlan {
 };
 
 #ifndef CSA_ATTN_SPLIT_KG
-#define CSA_ATTN_SPLIT_KG 2
+#define CSA_ATTN_SPLIT_KG 1
 #endif
 #ifndef CSA_ATTN_SPLIT_T
-#define CSA_ATTN_SPLIT_T 2
+#define CSA_ATTN_SPLIT_T 8
 #endif
 constexpr int SPLIT_KG = CSA_ATTN_SPLIT_KG;     // key groups per split block
 constexpr int SPLIT_T = CSA_ATTN_SPLIT_T;       // tiles per group, loaded up front
 
 // Below 512 queries (decode batches) a query's tiles go to splits of
 // SPLIT_KG x SPLIT_T tiles when that needs at most AT_MAX_SPLITS splits (k up
-// to ~1K); each group then holds every key it uses in registers before
-// computing, and there are enough blocks to cover the compute units.  Longer
-// selections stream in 4 splits of two groups.  From 512 queries on
-// (prefill) one group streams every tile of its query (no partials).
+// to ~1.9K); each group holds every key it uses in registers before
+// computing.  Longer selections stream in 4 splits of two groups.  From 512
+// queries on (prefill) one group streams every tile of its query (no
+// partials).
+// Measured in the 1M / 128K decode steps (batch 32 / 64, k = 512, traced
+// inside the captured step): one group of 8 tiles per split (5 splits) ran
+// 12.4 / ~15 us per layer, the same as 10 splits of 4 tiles and as the
+// former streaming plan (4 splits of two groups, two tiles ahead: 12.2 /
+// 14.8 us, with plain fp16 Q and P); two groups of 4 or 5 tiles ran 15-16
+// us.  What sets the time is not the tile loop: a launch whose blocks exit
+// at once, plus the combine, already takes ~2/3 of it, and each split's Q
+// read and partial write add to it (twice the splits, ~+6 us).
 AttnPlan attn_plan(int64_t Q, int32_t k) {
   const int n_tiles = (k + NWIN + AT_TILE - 1) / AT_TILE;
   AttnPlan pl;
@@ -702,7 +882,8 @@ hipError_t launch_sparse_attn(const float* q, const int32_t* q_pos, int64_t n_se
     a.part_o = reinterpret_cast<float*>(ws);
     a.part_ml = a.part_o + (size_t)Q * a.n_splits * HEADS * D;
   }
-  const dim3 grid(a.n_splits, (unsigned)Q);
+  a.n_queries = Q;
+  const dim3 grid = attn_grid(Q, a.n_splits);
   if (pl.kind == 0)
     hipLaunchKernelGGL((attn_split_kernel<SPLIT_KG, SPLIT_T>), grid, dim3(AT_THREADS * SPLIT_KG), 0, st, a);
   else if (pl.kg == 2)
@@ -711,8 +892,8 @@ hipError_t launch_sparse_attn(const float* q, const int32_t* q_pos, int64_t n_se
     hipLaunchKernelGGL(attn_stream_kernel<1>, grid, dim3(AT_THREADS), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(HEADS, (unsigned)Q), dim3(128), 0, st, a.part_o, a.part_ml,
-                     a.n_splits, out);
+  hipLaunchKernelGGL(attn_combine_kernel, attn_grid(Q, HEADS), dim3(128), 0, st, a.part_o, a.part_ml, a.n_splits,
+                     Q, out);
   return hipGetLastError();
 }
 
