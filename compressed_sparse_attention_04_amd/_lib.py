@@ -61,6 +61,9 @@ SIGNATURES = {
     "csa_sparse_attn_workspace_size": (c_size, [c_i64, c_i32]),
     "csa_sparse_attn": (c_i32, [c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_void_p, c_i64, c_void_p,
                                 c_i32, c_void_p, c_i64, c_f32, c_void_p, c_void_p, c_size, c_void_p]),
+    "csa_noalloc_scratch_bytes": (c_size, []),
+    "csa_sparse_attn_noalloc": (c_i32, [c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_void_p, c_i64, c_void_p,
+                                        c_i32, c_void_p, c_i64, c_f32, c_void_p, c_void_p]),
     "csa_layer_workspace_size": (c_size, [c_i32, ctypes.POINTER(CsaLayerArgs)]),
     "csa_layer_full": (c_i32, [ctypes.POINTER(CsaLayerArgs), c_void_p]),
     "csa_layer_reindex": (c_i32, [ctypes.POINTER(CsaLayerArgs), c_void_p]),

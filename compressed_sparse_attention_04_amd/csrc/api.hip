@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -337,6 +338,70 @@ csa_status csa_sparse_attn(const float* q, const int32_t* q_pos, int64_t n_seq, 
   if (n_seq * q_per_seq == 0 && n_seq >= 0 && q_per_seq >= 0) return CSA_OK;
   csa_status st = check_attn(fn, q, q_pos, n_seq, q_per_seq, codes, scales, kv_rows, idx, k, win, win_cap,
                              sm_scale, out, ws, ws_bytes);
+  if (st != CSA_OK) return st;
+  return hip_status(launch_sparse_attn(q, q_pos, n_seq, q_per_seq, codes, scales, kv_rows, idx, k, win,
+                                       win_cap, sm_scale, out, ws, stream),
+                    fn);
+}
+
+// ----------------------------------------------- a7, allocation-free ----
+// The split partials of csa_sparse_attn_noalloc live in this file-scope
+// device array (one copy per GPU, held until the process ends).  Host code
+// must not pass the array's name to a kernel: its device address is looked
+// up once per device with hipGetSymbolAddress and kept in g_scratch.
+}  // extern "C"
+
+static __device__ __align__(256) uint8_t scratch[CSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];   // device address of `scratch` per device, set on first use
+
+// The current device's address of `scratch` (looked up with that device
+// current, on the first call that needs it).
+csa_status scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(CSA_ERR_UNSUPPORTED, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (p == nullptr) return fail(CSA_ERR_HIP, "%s: no device address for the scratch array", fn);
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return CSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t csa_noalloc_scratch_bytes(void) { return CSA_NOALLOC_SCRATCH_BYTES; }
+
+csa_status csa_sparse_attn_noalloc(const float* q, const int32_t* q_pos, int64_t n_seq, int64_t q_per_seq,
+                                   const uint8_t* codes, const uint8_t* scales, int64_t kv_rows,
+                                   const int32_t* idx, int32_t k, const uint8_t* win, int64_t win_cap,
+                                   float sm_scale, float* out, hipStream_t stream) {
+  const char* fn = "csa_sparse_attn_noalloc";
+  if (n_seq * q_per_seq == 0 && n_seq >= 0 && q_per_seq >= 0) return CSA_OK;
+  CHECK(n_seq >= 0 && q_per_seq >= 0, CSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  CHECK(k >= 1 && k <= CSA_MAX_K, CSA_ERR_UNSUPPORTED, "%s: k must be in [1, 16384]", fn);
+  const size_t need = attn_workspace_bytes(n_seq * q_per_seq, k);
+  CHECK(need <= CSA_NOALLOC_SCRATCH_BYTES, CSA_ERR_UNSUPPORTED,
+        "%s: %lld queries at k = %d need %zu bytes of scratch; the static scratch holds %zu "
+        "(use csa_sparse_attn with a workspace, or fewer queries per call)",
+        fn, (long long)(n_seq * q_per_seq), k, need, (size_t)CSA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need) {
+    const csa_status st = scratch_address(fn, &ws);
+    if (st != CSA_OK) return st;
+  }
+  csa_status st = check_attn(fn, q, q_pos, n_seq, q_per_seq, codes, scales, kv_rows, idx, k, win, win_cap,
+                             sm_scale, out, ws, need);
   if (st != CSA_OK) return st;
   return hip_status(launch_sparse_attn(q, q_pos, n_seq, q_per_seq, codes, scales, kv_rows, idx, k, win,
                                        win_cap, sm_scale, out, ws, stream),

@@ -322,6 +322,34 @@ def csa_sparse_attn(q, q_pos, codes, scales, idx, win, n_seq, q_per_seq, sm_scal
     return out
 
 
+def csa_sparse_attn_noalloc(q, q_pos, codes, scales, idx, win, n_seq, q_per_seq, out, sm_scale=None,
+                            stream=None):
+    """csa_sparse_attn without a workspace: the library's static device scratch
+    holds the split partials (no allocation by the library or here; ``out``
+    is the caller's).  Calls that overlap on one GPU race."""
+    dev = q.device
+    Q = n_seq * q_per_seq
+    _need(q, "q", torch.float32, dev, shape=(Q, HEADS, D))
+    _need(q_pos, "q_pos", torch.int32, dev, shape=(Q,))
+    _need(codes, "codes", torch.uint8, dev)
+    _need(scales, "scales", torch.uint8, dev)
+    if codes.dim() != 3 or codes.shape[0] != n_seq or codes.shape[2] != D // 2:
+        raise ValueError("codes must be [n_seq, rows, 256]")
+    if tuple(scales.shape) != (n_seq, codes.shape[1], D // 16):
+        raise ValueError("scales must be [n_seq, rows, 32]")
+    _need(idx, "idx", torch.int32, dev)
+    if idx.dim() != 2 or idx.shape[0] != Q:
+        raise ValueError("idx must be [Q, k]")
+    _need(win, "win", torch.uint8, dev)
+    if win.dim() != 3 or win.shape[0] != n_seq or win.shape[2] != D:
+        raise ValueError("win must be [n_seq, cap, 512]")
+    _need(out, "out", torch.float32, dev, shape=(Q, HEADS, D))
+    sm = sm_scale if sm_scale is not None else 1.0 / math.sqrt(D)
+    _call("csa_sparse_attn_noalloc", _p(q), _p(q_pos), n_seq, q_per_seq, _p(codes), _p(scales), codes.shape[1],
+          _p(idx), idx.shape[1], _p(win), win.shape[1], ctypes.c_float(sm), _p(out), _stream(stream))
+    return out
+
+
 # ------------------------------------------------------------- a6 + a8 ----
 
 class LayerCall:

@@ -300,6 +300,30 @@ csa_status csa_sparse_attn(const float* q, const int32_t* q_pos, int64_t n_seq, 
                            float sm_scale, float* out, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 
+/* --------------------------------------------------- a7, no allocation ----
+ * csa_sparse_attn_noalloc: csa_sparse_attn for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the same arguments and result, without a
+ * workspace.  The split partials go to a static device scratch of
+ * CSA_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on every GPU it
+ * runs on until the process ends; this call allocates and frees nothing.
+ *   The call runs on the current device; csa_sparse_attn_workspace_size(Q, k)
+ *   must not exceed the scratch (about 199 decode queries at k = 512;
+ *   prefill plans of 512+ queries need none), else CSA_ERR_UNSUPPORTED and
+ *   nothing is enqueued.  The scratch holds no state between calls (every
+ *   partial is written before it is read).  All calls on one GPU share the
+ *   one scratch: calls that overlap in time on that GPU (on different
+ *   streams, or from different threads) race and must be ordered by the
+ *   caller.
+ * csa_noalloc_scratch_bytes: CSA_NOALLOC_SCRATCH_BYTES.
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+size_t csa_noalloc_scratch_bytes(void);
+csa_status csa_sparse_attn_noalloc(const float* q, const int32_t* q_pos, int64_t n_seq, int64_t q_per_seq,
+                                   const uint8_t* codes, const uint8_t* scales, int64_t kv_rows,
+                                   const int32_t* idx, int32_t k, const uint8_t* win, int64_t win_cap,
+                                   float sm_scale, float* out, hipStream_t stream);
+
 /* ------------------------------------------------------------ a6 + a8 ----
  * Layer entry points (P3 §02 layer modes).
  *   Full:    score every visible entry with (q_idx, w_idx) -> Top-k idx;

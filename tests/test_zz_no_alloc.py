@@ -1,0 +1,67 @@
+"""The allocation-free attention entry point (csa_sparse_attn_noalloc),
+called through the C ABI, against csa_sparse_attn with a workspace: the same
+kernels, so the outputs are compared bit for bit, on consecutive calls of
+decreasing size (the static scratch keeps the previous call's contents), on
+a prefill-sized call that needs no scratch, and on a request larger than the
+scratch (rejected, nothing written)."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats
+from compressed_sparse_attention_04_amd import ops, _lib
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _case(seed, n_seq, q_per_seq, rows, k, win_cap):
+    rng = np.random.default_rng(seed)
+    Q = n_seq * q_per_seq
+    codes = torch.from_numpy(rng.integers(0, 256, (n_seq, rows, 256)).astype(np.uint8)).to(DEV)
+    scales = torch.from_numpy(rng.integers(0x28, 0x31, (n_seq, rows, 32)).astype(np.uint8)).to(DEV)
+    win = torch.from_numpy(formats.e4m3_encode(rng.standard_normal((n_seq, win_cap, 512)))).to(DEV)
+    q = torch.from_numpy(rng.standard_normal((Q, 16, 512)).astype(np.float32)).to(DEV)
+    idx = np.stack([np.sort(rng.choice(rows, k, replace=False)) for _ in range(Q)]).astype(np.int32)
+    idx[rng.random(idx.shape) < 0.03] = -1
+    idx = torch.from_numpy(idx).to(DEV)
+    pos = torch.from_numpy(np.array([4 * rows - 1 - (i % q_per_seq) for i in range(Q)], np.int32)).to(DEV)
+    return q, pos, codes, scales, idx, win
+
+
+def _both(n_seq, q_per_seq, rows, k, win_cap, seed):
+    q, pos, codes, scales, idx, win = _case(seed, n_seq, q_per_seq, rows, k, win_cap)
+    ref = ops.csa_sparse_attn(q, pos, codes, scales, idx, win, n_seq, q_per_seq)
+    out = torch.full_like(ref, float("nan"))
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    ops.csa_sparse_attn_noalloc(q, pos, codes, scales, idx, win, n_seq, q_per_seq, out)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == before          # the call allocated nothing through torch
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), (n_seq, q_per_seq, k)
+    return out
+
+
+def test_noalloc_matches_workspace_entry_two_calls():
+    lib = _lib.load()
+    assert lib.csa_noalloc_scratch_bytes() == 32 << 20
+    _both(32, 1, 3000, 512, 128, 1)       # decode batch: five splits per query in the scratch
+    _both(5, 1, 900, 300, 128, 2)         # smaller: fewer partials, same scratch
+    _both(1, 600, 2000, 512, 728, 3)      # prefill plan: no partials at all
+    _both(32, 1, 3000, 512, 128, 4)       # the first size again
+
+
+def test_noalloc_rejects_more_than_the_scratch():
+    q, pos, codes, scales, idx, win = _case(5, 250, 1, 1000, 512, 128)
+    out = torch.full((250, 16, 512), 7.0, device=DEV)
+    lib = _lib.load()
+    need = lib.csa_sparse_attn_workspace_size(250, 512)
+    assert need > lib.csa_noalloc_scratch_bytes()
+    with pytest.raises(ops.CsaError) as e:
+        ops.csa_sparse_attn_noalloc(q, pos, codes, scales, idx, win, 250, 1, out)
+    assert e.value.status == 2 and "scratch" in e.value.message
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
