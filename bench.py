@@ -110,20 +110,42 @@ def capture(st, use_graph):
     return g.replay
 
 
-def time_step(runs, steps, warmup):
+FLUSH_BYTES = 512 << 20        # read between timed steps: more than the 256 MB MALL plus the L2s
+_flush_buf = None
+
+
+def flush_caches():
+    """Read a 512 MiB buffer (a plain cached read, so nothing dirty is left
+    behind): the next step starts with L2 and MALL holding none of its data."""
+    import torch
+    global _flush_buf
+    if _flush_buf is None:
+        _flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    return _flush_buf.sum()
+
+
+def time_step(runs, steps, warmup, flush=True):
+    """Time exactly `steps` steps, each between its own pair of HIP events on
+    the launch stream, after an untimed cache flush.  Returns a dict: median
+    (the reported ms_per_step), mean, p10, p90 and the per-step list (ms)."""
     import torch
     n = len(runs)
     for i in range(warmup):
+        if flush:
+            flush_caches()
         runs[i % n]()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i in range(steps):
+        if flush:
+            flush_caches()
+        ev[i][0].record()
         runs[i % n]()
-    t1.record()
+        ev[i][1].record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    q = lambda f: t[min(len(t) - 1, int(f * len(t)))]   # noqa: E731
+    return {"median": q(0.5), "mean": sum(t) / len(t), "p10": q(0.1), "p90": q(0.9), "n": len(t)}
 
 
 def time_kernel(fn, reps):
@@ -202,6 +224,41 @@ def counter_traffic(kernel_key, digest):
         return None
 
 
+def compress_call(st):
+    """The step's compression + MXFP4 store of its new entries (the same
+    launch the step makes), for timing it alone."""
+    from compressed_sparse_attention_04_amd import ops
+    tail = st.x_tail.shape[1]
+
+    def fn():
+        ops.csa_compress_quant(st.x_tail, st.w, st.rope_cs, st.codes, st.scales, n_seq=st.S, n_per_seq=st.new,
+                               x_seq_stride=tail * 512, x_offset=(tail - 4 * st.new) * 512, out_seq_stride=st.cap,
+                               out_offset=st.prior, rope_dim=st.rope_dim, eps=st.eps)
+    return fn
+
+
+def attention_call(st, li):
+    """Layer li's sparse attention launch of the step (its own inputs, ids
+    and output), for timing it alone."""
+    from compressed_sparse_attention_04_amd import ops
+    c = st.calls[li]
+    k = st.idxs[li].shape[1]
+    ws = ops._workspace(ops._lib.load().csa_sparse_attn_workspace_size(st.Q, k), st.codes.device)
+    q_attn = c.keep[5]
+
+    def fn():
+        ops.csa_sparse_attn(q_attn, c.keep[4], st.codes, st.scales, st.idxs[li], st.wins[li], st.S, st.q_per_seq,
+                            out=st.outs[li])
+    return fn, ws
+
+
+def attention_flops(cfg, k=512):
+    """Nominal attention flops of one layer: per query Q K^T and P V over its
+    k entries and its 128 window tokens (every query here sits past position
+    127), 16 heads x 512 channels, 2 flops per multiply-add."""
+    return 2 * 2 * 16 * 512 * cfg.n_queries * (k + 128)
+
+
 def measure_config(cid, steps, warmup, use_graph, kernel_reps):
     import torch
     import workloads as W
@@ -210,10 +267,25 @@ def measure_config(cid, steps, warmup, use_graph, kernel_reps):
     log(f"[bench] config {cid} {cfg.name}: building {n_inst} instance(s)")
     insts = build_steps(cfg, n_inst)
     runs = [capture(st, use_graph) for _, st in insts]
-    ms = time_step(runs, steps, warmup)
-    log(f"[bench] config {cid}: {ms:.3f} ms/step")
+    ts = time_step(runs, steps, warmup)
+    ms = ts["median"]
+    log(f"[bench] config {cid}: {ms:.3f} ms/step (median of {ts['n']}, p10 {ts['p10']:.3f}, p90 {ts['p90']:.3f})")
     wl, st = insts[0]
-    res = {"workload": cfg.name, "ms_per_step": ms, "algorithmic_bytes": algorithmic_bytes(cfg)}
+    res = {"workload": cfg.name, "ms_per_step": ms, "step_ms": {k: round(v, 4) for k, v in ts.items()},
+           "algorithmic_bytes": algorithmic_bytes(cfg)}
+    # compression of the step's new entries, timed alone (a decode step
+    # completes an entry every 4th token; the step above always compresses)
+    cms = time_kernel(compress_call(st), kernel_reps)
+    res["compress_ms"] = cms
+    if cfg.kind == "decode":
+        res["ms_per_step_amortized"] = ms - 0.75 * cms
+        res["tokens_per_s_amortized"] = cfg.n_seq / (res["ms_per_step_amortized"] * 1e-3)
+    # the first layer's attention alone (nominal flops)
+    afn, aws = attention_call(st, 0)
+    ams = time_kernel(afn, kernel_reps)
+    res["attention_ms"] = ams
+    res["attention_tflops"] = attention_flops(cfg) / (ams * 1e-3) / 1e12
+    del aws
     res["hbm_gbps"] = res["algorithmic_bytes"] / (ms * 1e-3) / 1e9
     if cfg.kind == "decode":
         res["tokens_per_s"] = cfg.n_seq / (ms * 1e-3)
@@ -247,7 +319,7 @@ def measure_schedule(name, steps, warmup, use_graph):
     sch.setup()
     torch.cuda.synchronize()
     run = capture(sch, use_graph)
-    ms = time_step([run], steps, warmup)
+    ms = time_step([run], steps, warmup)["median"]
     log(f"[bench] schedule {name}: {ms:.3f} ms/step")
     alg = sum(algorithmic_bytes(c) for c in cfgs)
     res = {"ms_per_step": round(ms, 4), "tokens_per_s": round(cfgs[0].n_seq / (ms * 1e-3), 1),
@@ -342,6 +414,17 @@ def probe_peaks():
     ms_r = time_kernel(read, 10)
     res = {"mfma_f16_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
            "read_gbs": round(buf.numel() / (ms_r * 1e-3) / 1e9, 1)}
+    # FP8: the 16x16x128 f8f6f4 instruction (65,536 flops) and the
+    # 16x16x32 fp8 one (16,384 flops), 32 chains per wave each
+    for variant, per in ((0, 2 * 16 * 16 * 128), (1, 2 * 16 * 16 * 32)):
+        it = iters if variant == 0 else 4 * iters
+
+        def f8():
+            rc = lib.csa_probe_mfma_f8(ops._p(out), blocks, it, variant, st)
+            if rc:
+                raise RuntimeError(lib.csa_last_error().decode())
+        ms8 = time_kernel(f8, 5)
+        res[f"mfma_f8_v{variant}_tflops"] = round(blocks * 4 * it * 32 * per / (ms8 * 1e-3) / 1e12, 1)
     del buf
     torch.cuda.empty_cache()
     return res
@@ -401,8 +484,16 @@ def cpu_baseline(cid, n_sample):
     for qi in range(sub_cfg.n_queries):
         ref.query(qi)
     dt = time.perf_counter() - t0
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": sub_cfg.n_queries / dt, "unit": "tokens/s", "cores": threads or os.cpu_count(),
-            "kind": "oracle",
+            "cpu_model": model, "kind": "oracle",
             "sample": f"{n_sample} of {cfg.n_seq} sequences of {cfg.name}, whole layer group "
                       f"(numpy float64 on the host), {dt:.1f} s"}
 
@@ -412,7 +503,7 @@ def cpu_baseline(cid, n_sample):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--no-secondary", action="store_true")
@@ -437,6 +528,7 @@ def main():
                               kernel_reps=max(5, args.steps))
     cfg = W.CONFIGS[args.config]
     digest = source_digest(["index.hip", "index_core.h", "common.h"])
+    pk = probe_peaks()
     if cfg.kind == "decode":
         key = "score_scan_" + cfg.name
         achieved = main_res["indexer_gbps"]
@@ -452,11 +544,8 @@ def main():
         # than this read-only scan, so the fraction can exceed 1
         roofline["stream_copy_gbs"] = round(cp, 1)
         roofline["frac_of_stream_copy"] = round(achieved / cp, 4)
-        pk = probe_peaks()
         roofline["read_probe_gbs"] = pk["read_gbs"]          # the scan's own loads, nothing else
         roofline["frac_of_read_probe"] = round(achieved / pk["read_gbs"], 4)
-        main_res["mfma_probe_tflops"] = pk["mfma_f16_tflops"]
-        value, unit = main_res["tokens_per_s"], "tokens/s"
     else:
         key = "score_tile_" + cfg.name
         achieved = main_res["indexer_tflops"]
@@ -466,8 +555,9 @@ def main():
                     "traffic": None if traffic is None else int(traffic),
                     "kernel": "score_tile_kernel (Full-layer dense indexer, fp16 MFMA)",
                     "flops_per_launch": indexer_flops(cfg),
-                    "avg_launch_ms": round(main_res["indexer_ms"], 4)}
-        value, unit = main_res["tokens_per_s"], "tokens/s"
+                    "avg_launch_ms": round(main_res["indexer_ms"], 4),
+                    "frac_of_f8_peak": round(achieved / F8_PEAK_TFLOPS, 4)}
+    value, unit = main_res["tokens_per_s"], "tokens/s"
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(main_res["ms_per_step"], 4),
@@ -476,31 +566,45 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.n_seq, "context_tokens": cfg.ctx_tokens,
                    "entries_per_seq": cfg.entries_total, "layers": "".join(cfg.layers),
                    "hierarchical_pool": cfg.build_pool},
+        "timing": "median of the timed steps; each step one graph replay between HIP events, after an "
+                  "untimed 512 MiB read that empties L2 and MALL",
+        "step_ms": main_res["step_ms"],
         "hbm_gbps": round(main_res["hbm_gbps"], 1),
         "hbm_frac": round(main_res["hbm_gbps"] / HBM_PEAK_GBS, 4),
         "roofline": roofline,
+        "probes": pk,
     }
+    for k in ("compress_ms", "ms_per_step_amortized", "tokens_per_s_amortized", "attention_ms",
+              "attention_tflops"):
+        if k in main_res:
+            out[k] = round(main_res[k], 4 if k.endswith("_ms") or k.startswith("ms_") else 1)
     if not args.no_secondary:
         sec = {}
-        for cid in (2, 4):
+        for cid in (0, 1, 2, 3, 4):
             if cid == args.config:
                 continue
-            r = measure_config(cid, max(3, args.steps // 2), max(1, args.warmup // 2), not args.no_graph,
-                               kernel_reps=max(3, args.steps // 2))
+            r = measure_config(cid, max(10, args.steps // 2), max(2, args.warmup // 2), not args.no_graph,
+                               kernel_reps=max(5, args.steps // 4))
+            c = W.CONFIGS[cid]
             e = {"ms_per_step": round(r["ms_per_step"], 4), "tokens_per_s": round(r["tokens_per_s"], 1),
-                 "hbm_gbps": round(r["hbm_gbps"], 1)}
+                 "hbm_gbps": round(r["hbm_gbps"], 1), "step_ms_p10_p90": [round(r["step_ms"]["p10"], 4),
+                                                                           round(r["step_ms"]["p90"], 4)],
+                 "compress_ms": round(r["compress_ms"], 4), "attention_ms": round(r["attention_ms"], 4),
+                 "attention_tflops": round(r["attention_tflops"], 1)}
+            if c.kind == "decode":
+                e["latency_us"] = round(1000 * r["ms_per_step"], 1)
+                e["ms_per_step_amortized"] = round(r["ms_per_step_amortized"], 4)
+                e["tokens_per_s_amortized"] = round(r["tokens_per_s_amortized"], 1)
             if "indexer_tflops" in r:
                 e["indexer_tflops"] = round(r["indexer_tflops"], 1)
                 e["indexer_frac_f16_peak"] = round(r["indexer_tflops"] / F16_PEAK_TFLOPS, 4)
-                if "mfma_probe_tflops" in main_res:
-                    e["mfma_f16_probe_tflops"] = main_res["mfma_probe_tflops"]
-                    e["indexer_frac_f16_probe"] = round(r["indexer_tflops"] / main_res["mfma_probe_tflops"], 4)
+                e["indexer_frac_f16_probe"] = round(r["indexer_tflops"] / pk["mfma_f16_tflops"], 4)
                 e["indexer_frac_f8_peak"] = round(r["indexer_tflops"] / F8_PEAK_TFLOPS, 4)
             else:
                 e["indexer_gbps"] = round(r["indexer_gbps"], 1)
             sec[r["workload"]] = e
         for name in W.SCHEDULES:
-            sec[name] = measure_schedule(name, max(3, args.steps // 2), max(1, args.warmup // 2),
+            sec[name] = measure_schedule(name, max(10, args.steps // 2), max(2, args.warmup // 2),
                                          not args.no_graph)
         sec["window_rebuild_b32_38layers"] = measure_window_rebuild()
         sec["kv_file_round_trip_1m_4seq"] = measure_kv_io()

@@ -9,7 +9,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcsa.so")
+# CSA_LIB_PATH selects another build of the same library (the sanitized
+# host build of the checked CPU tests); there is no fallback either way.
+LIB_PATH = os.environ.get("CSA_LIB_PATH") or os.path.join(_HERE, "libcsa.so")
 
 c_void_p = ctypes.c_void_p
 c_i64 = ctypes.c_int64
@@ -50,6 +52,7 @@ SIGNATURES = {
                             c_void_p]),
     "csa_kv_file_info": (c_i32, [ctypes.c_char_p, c_void_p, c_void_p]),
     "csa_probe_mfma_f16": (c_i32, [c_void_p, c_i32, c_i32, c_void_p]),
+    "csa_probe_mfma_f8": (c_i32, [c_void_p, c_i32, c_i32, c_i32, c_void_p]),
     "csa_probe_read": (c_i32, [c_void_p, c_i64, c_void_p, c_void_p]),
     "csa_index_score": (c_i32, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_i64, c_i64,
                                 c_void_p, c_i32, c_void_p, c_void_p, c_void_p]),

@@ -38,6 +38,22 @@ HIP_FLAGS = [
 ]
 
 
+# Host-side sanitizers for the checked build (the device code is unchanged):
+# every -fsanitize= right after -Xarch_host, so only the host pass gets it.
+SANITIZE_FLAGS = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+                  "-Xarch_host -fno-sanitize-recover=all -Xarch_host -fno-omit-frame-pointer").split()
+SAN_DIR = os.path.join(BUILD_DIR, "san")
+SAN_LIB_PATH = os.path.join(SAN_DIR, "libcsa_san.so")
+
+
+def sanitizer_runtime():
+    """The clang ASan runtime (its shared library also carries the UBSan
+    handlers), preloaded into a process that loads the checked build."""
+    import glob
+    libs = glob.glob(os.path.join(ROCM, "llvm", "lib", "clang", "*", "lib", "linux", "libclang_rt.asan-x86_64.so"))
+    return sorted(libs)[-1] if libs else None
+
+
 def torch_lib_dir():
     import importlib.util
     spec = importlib.util.find_spec("torch")
@@ -55,10 +71,17 @@ def _compile(src, obj, extra):
     return r.returncode, " ".join(cmd), err
 
 
-def build(verbose=False, extra_flags=None, jobs=None):
-    """Compile every csrc/*.hip and link libcsa.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    extra = list(extra_flags or [])
+def build(verbose=False, extra_flags=None, jobs=None, sanitize=False):
+    """Compile every csrc/*.hip and link libcsa.so; returns the library path.
+
+    sanitize=True builds the checked variant instead (host code under
+    AddressSanitizer and UBSan, objects in _build/san, library
+    _build/san/libcsa_san.so); load it with the runtime from
+    sanitizer_runtime() preloaded."""
+    obj_dir = SAN_DIR if sanitize else BUILD_DIR
+    lib_path = SAN_LIB_PATH if sanitize else LIB_PATH
+    os.makedirs(obj_dir, exist_ok=True)
+    extra = list(extra_flags or []) + (SANITIZE_FLAGS if sanitize else [])
     srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
     if not srcs:
         raise RuntimeError("no HIP sources found in " + CSRC)
@@ -67,7 +90,7 @@ def build(verbose=False, extra_flags=None, jobs=None):
     with cf.ThreadPoolExecutor(jobs) as ex:
         futs = {}
         for s in srcs:
-            obj = os.path.join(BUILD_DIR, s[:-4] + ".o")
+            obj = os.path.join(obj_dir, s[:-4] + ".o")
             objs.append(obj)
             futs[ex.submit(_compile, os.path.join(CSRC, s), obj, extra)] = s
         failed = []
@@ -82,22 +105,23 @@ def build(verbose=False, extra_flags=None, jobs=None):
     if failed:
         raise RuntimeError("HIP compile failed: " + ", ".join(sorted(failed)))
     tdir = torch_lib_dir()
-    link = [CLANG, "-shared", "-fPIC", "-o", LIB_PATH + ".tmp"] + objs
+    link = [CLANG, "-shared", "-fPIC", "-o", lib_path + ".tmp"] + objs
     if tdir:
         link += ["-L" + tdir, "-l:libamdhip64.so", "-Wl,-rpath," + tdir]
     else:
         link += ["-L" + os.path.join(ROCM, "lib"), "-lamdhip64",
                  "-Wl,-rpath," + os.path.join(ROCM, "lib")]
-    link += ["-Wl,--no-undefined", "-lstdc++"]
+    # the checked build leaves the sanitizer runtime's symbols to the preloaded runtime
+    link += ["-lstdc++"] if sanitize else ["-Wl,--no-undefined", "-lstdc++"]
     r = subprocess.run(link, capture_output=True, text=True)
     if verbose or r.returncode != 0:
         print(" ".join(link))
         print(r.stderr)
     if r.returncode != 0:
         raise RuntimeError("link failed")
-    os.replace(LIB_PATH + ".tmp", LIB_PATH)
-    return LIB_PATH
+    os.replace(lib_path + ".tmp", lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -187,17 +187,11 @@ __device__ __forceinline__ uint32_t select_key(float x) {
 }
 
 // MFMA wrappers (layouts verified: C lane l holds rows 4*(l/16)+r, column l%16).
-__device__ __forceinline__ f32x4 mfma_f8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
 __device__ __forceinline__ f32x4 mfma_f16_16x16x32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma_f16_16x16x16(f16x4 a, f16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 // fp64 16x16x4: A lane l = row l%16, k l/16 (same as fp32), but the result
 // lane l, register r holds row l/16 + 4r, column l%16 (verified on gfx950).

@@ -19,6 +19,7 @@
 // while one half is written to (or read from) the file, the other half's
 // device copy is in flight on the caller's stream.
 #include <cerrno>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
@@ -83,7 +84,13 @@ csa_status check_header(const char* fn, const KvHeader& h, int64_t file_bytes, c
                 h.scale_bytes, h.key_bytes, CODE_BYTES, SCALE_BYTES, ID);
   if (h.n_seq < 0 || h.n_entries < 0 || h.n_seq > ((int64_t)1 << 24) || h.n_entries > ((int64_t)1 << 32))
     return fail(CSA_ERR_IO, "%s: %s has sizes out of range", fn, path);
-  const int64_t payload = h.n_seq * h.n_entries * (CODE_BYTES + SCALE_BYTES + ID);
+  // the header's sizes are untrusted: the payload size must not overflow
+  // int64 (a wrapped product could match the file size)
+  int64_t rows = 0, payload = 0;
+  if (__builtin_mul_overflow(h.n_seq, h.n_entries, &rows) ||
+      __builtin_mul_overflow(rows, (int64_t)(CODE_BYTES + SCALE_BYTES + ID), &payload) ||
+      payload > INT64_MAX - (int64_t)KV_HEADER)
+    return fail(CSA_ERR_IO, "%s: %s has sizes whose payload overflows", fn, path);
   if (file_bytes != (int64_t)KV_HEADER + payload)
     return fail(CSA_ERR_IO, "%s: %s holds %lld bytes, its header needs %lld", fn, path, (long long)file_bytes,
                 (long long)(KV_HEADER + payload));

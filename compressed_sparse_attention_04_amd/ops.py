@@ -58,6 +58,18 @@ def _need(t, name, dtype, device=None, shape=None, contiguous=True):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _keep(stream, *tensors):
+    """Tensors this binding allocated for a call launched on ``stream`` (when
+    that is not the current stream) are recorded as used by that stream, so
+    the caching allocator, which tracks the current stream, does not hand
+    their memory to later work before the call's kernels have finished."""
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def _workspace(nbytes, device):
     if nbytes == 0:
         return None
@@ -83,6 +95,7 @@ def csa_quantize(e, codes=None, scales=None, stream=None):
     if codes.numel() != n * (D // 2) or scales.numel() != n * (D // 16):
         raise ValueError("codes / scales sizes do not match e")
     _call("csa_quantize", _p(e), n, _p(codes), _p(scales), _stream(stream))
+    _keep(stream, codes, scales)
     return codes, scales
 
 
@@ -95,6 +108,7 @@ def csa_dequantize(codes, scales, out=None, stream=None):
     out = out if out is not None else torch.empty((n, D), dtype=torch.float32, device=codes.device)
     _need(out, "out", torch.float32, codes.device)
     _call("csa_dequantize", _p(codes), _p(scales), n, _p(out), _stream(stream))
+    _keep(stream, out)
     return out
 
 
@@ -142,6 +156,7 @@ def csa_compress_quant(x, w, rope_cs, codes, scales, n_seq, n_per_seq, x_seq_str
           _p(rope_cs) if rope_dim else None, rope_dim, ctypes.c_float(eps),
           _ptr_off(codes, out_offset * (D // 2)), _ptr_off(scales, out_offset * (D // 16)), os_,
           _p(e_out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _keep(stream, ws)
 
 
 # ------------------------------------------------------------------ a9 ----
@@ -255,6 +270,7 @@ def csa_index_score(q_fp8, w, q_pos, k_fp8, n_seq, q_per_seq, n_entries, pool_bl
         bm = torch.empty((Q, (ncols + 7) // 8), dtype=torch.float32, device=dev)
     _call("csa_index_score", _p(q_fp8), _p(w), _p(q_pos), n_seq, q_per_seq, _p(k_fp8), k_fp8.shape[1],
           n_entries, _p(pool_blocks), nb, _p(scores), _p(bm), _stream(stream))
+    _keep(stream, scores, bm)
     return scores, bm
 
 
@@ -271,6 +287,7 @@ def csa_topk(scores, k=TOP_K, col_blocks=None, idx=None, stream=None):
     ws = _workspace(_lib.load().csa_topk_workspace_size(Q, ncols, k), dev)
     _call("csa_topk", _p(scores), Q, ncols, _p(col_blocks), k, _p(idx), _p(ws),
           0 if ws is None else ws.numel(), _stream(stream))
+    _keep(stream, ws, idx)
     return idx
 
 
@@ -286,6 +303,7 @@ def csa_block_pool(values, is_block_max=True, n_pool_blocks=POOL_BLOCKS, out=Non
                     dev)
     _call("csa_block_pool", _p(values), int(is_block_max), Q, ncols, n_pool_blocks, _p(out), _p(ws),
           0 if ws is None else ws.numel(), _stream(stream))
+    _keep(stream, ws, out)
     return out
 
 
@@ -319,6 +337,7 @@ def csa_sparse_attn(q, q_pos, codes, scales, idx, win, n_seq, q_per_seq, sm_scal
     _call("csa_sparse_attn", _p(q), _p(q_pos), n_seq, q_per_seq, _p(codes), _p(scales), codes.shape[1],
           _p(idx), k, _p(win), win.shape[1], ctypes.c_float(sm), _p(out), _p(ws),
           0 if ws is None else ws.numel(), _stream(stream))
+    _keep(stream, ws, out)
     return out
 
 
@@ -414,6 +433,7 @@ class LayerCall:
         name = {MODE_FULL: "csa_layer_full", MODE_REINDEX: "csa_layer_reindex",
                 MODE_REUSE: "csa_layer_reuse"}[self.mode]
         _call(name, ctypes.byref(self.args), _stream(stream))
+        _keep(stream, self.ws)
 
 
 def csa_layer_full(**kw):

@@ -206,10 +206,14 @@ csa_status csa_kv_file_info(const char* path, int64_t* n_seq, int64_t* n_entries
  * csa_probe_mfma_f16: `blocks` blocks of 256 threads, every wave running
  *   iters x 32 independent v_mfma_f32_16x16x32_f16 (16,384 multiply-adds
  *   each); out: one float (device), written only to keep the work live.
+ * csa_probe_mfma_f8: as csa_probe_mfma_f16 for the FP8 matrix instructions:
+ *   variant 0 = v_mfma_scale_f32_16x16x128_f8f6f4 on E4M3 operands (65,536
+ *   flops each), variant 1 = v_mfma_f32_16x16x32_fp8_fp8 (16,384 flops).
  * csa_probe_read: reads `bytes` (a multiple of 16, buf 16-byte aligned) with
  *   whole-line non-temporal 16-byte loads; out as above.
  */
 csa_status csa_probe_mfma_f16(float* out, int32_t blocks, int32_t iters, hipStream_t stream);
+csa_status csa_probe_mfma_f8(float* out, int32_t blocks, int32_t iters, int32_t variant, hipStream_t stream);
 csa_status csa_probe_read(const uint8_t* buf, int64_t bytes, float* out, hipStream_t stream);
 
 /* ---------------------------------------------------------------- a3 ----

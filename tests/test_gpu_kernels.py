@@ -567,3 +567,22 @@ def test_full_layer_k_at_least_visible_is_dense(n_ent, top_k):
         ref = oracle.layer_full(codes[s], scales[s], k8[s], q8[s], w[s], q_attn[s], pos[s], win[s, wp % win_cap],
                                 SM, k=top_k, n_entries=n_ent)
         assert np.array_equal(ref.idx, want)
+
+
+def test_side_stream_call_keeps_its_workspace():
+    """csa_sparse_attn launched on a side stream with a binding-allocated
+    workspace (decode plan: split partials): the current stream then
+    allocates and overwrites memory at once; the side stream's output still
+    matches the oracle (the workspace was recorded as in use there)."""
+    rng = np.random.default_rng(41)
+    rows, k, win_cap = 3000, 512, 128
+    codes, scales, win, q, idx, pos = _attn_case(rng, 16, 1, rows, k, win_cap, 9000)
+    tq, tpos, tc, ts, ti, tw = t_(q), t_(pos), t_(codes), t_(scales), t_(idx), t_(win)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())   # the inputs were written on the current stream
+    out = ops.csa_sparse_attn(tq, tpos, tc, ts, ti, tw, 16, 1, stream=side)
+    junk = [torch.full((1 << 22,), 1e30, device=DEV) for _ in range(8)]   # reuse freed blocks at once
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    check_attn(np_(out), _attn_ref(codes, scales, win, q, idx, pos, 1, win_cap))

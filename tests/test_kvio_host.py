@@ -104,3 +104,16 @@ def test_save_checks_before_copying(lib, tmp_path):
 
 def test_status_string_of_io_error(lib):
     assert lib.csa_status_string(IO) == b"file error"
+
+
+def test_file_info_rejects_a_header_whose_payload_size_overflows(lib, tmp_path):
+    """Sizes inside the per-field caps whose product with the 416-byte row
+    does not fit int64: reported as an overflow, not compared after a wrap."""
+    p = tmp_path / "kv.bin"
+    write_file(p, 1, 1)
+    raw = bytearray(open(p, "rb").read())
+    raw[16:32] = struct.pack("<qq", 1 << 24, 1 << 32)       # n_seq, n_entries at the caps
+    open(p, "wb").write(bytes(raw))
+    rc, _, _ = info(lib, p)
+    assert rc == IO
+    assert b"overflow" in lib.csa_last_error()
