@@ -36,12 +36,11 @@
 // its kind returns zeros.
 //
 // Two launch shapes:
-//   * split (decode batches): a query's tiles are cut into splits of KG x T
-//     tiles; a block holds KG key groups, and every group issues the loads of
-//     all its T tiles before the first one is used, so the dependent gather
-//     (slot id, then the entry bytes) is paid once per block rather than
-//     once per tile.  Splits write (O, max, sum) partials that
-//     attn_combine_kernel merges.
+//   * pair (decode batches): a query's key slots are cut into splits of
+//     four 32-slot pairs, each loaded whole before use, so the dependent
+//     gather (slot id, then the entry bytes) is paid once per block; the P V
+//     product contracts 32 keys per MFMA.  Splits write (O, max, sum)
+//     partials that attn_combine_kernel merges.
 //   * stream (prefill chunks, and decode with very large k): one block per
 //     query (or a few splits), tiles streamed with one (one group) or two
 //     (two groups) tiles of key bytes in flight.
@@ -460,218 +459,353 @@ __device__ __forceinline__ void attn_finish(Lds& lds, AttnState& st, const AttnA
 }
 
 // ---------------------------------------------------------------------------
-// Split kernel: block (query, split) holds KG key groups; group kg takes the
-// split's tiles t_begin + kg + KG i, i < T.  A group issues the loads of all
-// its tiles first (slot ids, then key bytes), then runs them as one batch:
-// the partial S of every tile, one barrier for the four waves' partials, one
-// softmax over all the group's keys (its exact max first, so no rescaling),
-// then P V tile by tile (the key slices are widened again from the
-// registers into the wave's LDS rows, which only the P V transpose needs).
-// The dependent chain per block is one load round trip, one barrier and one
-// softmax, however many tiles the group holds.
-//
-// A block whose tiles are all selected entries (or all window tokens) loads
-// only that kind of bytes; a block holding both (or the mixed tile) loads
-// every slot's entry and window bytes (load_slot).
-constexpr int PATH_ENTRY = 0, PATH_WINDOW = 1, PATH_ANY = 2;
+// Key loaders of a block whose slots are all selected entries (PATH_ENTRY)
+// or all window tokens (PATH_WINDOW): only that kind of bytes is loaded.
+constexpr int PATH_ENTRY = 0, PATH_WINDOW = 1;
 
+// The lane's QK bytes of key slot `slot` (channels 128 w + 32 g .. + 31);
+// entries are slots 0 .. k-1, window token i is slot k + i.
 template <int PATH>
-__device__ __forceinline__ RawKey load_slot_p(const QueryView& v, const AttnArgs& a, int t, bool live, int j, int g,
+__device__ __forceinline__ RawKey load_slot_p(const QueryView& v, const AttnArgs& a, int slot, bool live, int g,
                                               int w, int32_t id) {
-  if constexpr (PATH == PATH_ANY) {
-    return load_slot(v, a, t, live, j, g, w, id);
+  RawKey r;
+  r.a = make_uint4(0u, 0u, 0u, 0u);
+  r.b = make_uint4(0u, 0u, 0u, 0u);
+  r.sc = 0u;
+  if constexpr (PATH == PATH_ENTRY) {
+    const bool ent = live && slot < a.k && id >= 0 && id < a.kv_rows;
+    const uint32_t oc = ent ? (uint32_t)id * CODE_BYTES + 64u * w + 16u * g : AT_OOB;
+    const uint32_t os = ent ? (uint32_t)id * SCALE_BYTES + 8u * w + 2u * g : AT_OOB;
+    r.a = load_b128(v.codes, oc);
+    r.sc = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(v.scales, os, 0, 0);
+    r.kind = ent ? 1 : 0;
   } else {
-    RawKey r;
-    r.a = make_uint4(0u, 0u, 0u, 0u);
-    r.b = make_uint4(0u, 0u, 0u, 0u);
-    r.sc = 0u;
-    const int slot = t * AT_TILE + j;
-    if constexpr (PATH == PATH_ENTRY) {
-      const bool ent = live && slot < a.k && id >= 0 && id < a.kv_rows;
-      const uint32_t oc = ent ? (uint32_t)id * CODE_BYTES + 64u * w + 16u * g : AT_OOB;
-      const uint32_t os = ent ? (uint32_t)id * SCALE_BYTES + 8u * w + 2u * g : AT_OOB;
-      r.a = load_b128(v.codes, oc);
-      r.sc = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(v.scales, os, 0, 0);
-      r.kind = ent ? 1 : 0;
-    } else {
-      const int wi = slot - a.k;
-      const bool win = live && wi >= 0 && wi < NWIN && v.p - (NWIN - 1) + wi >= 0;
-      int row = v.wbase + wi;
-      row = row >= v.win_cap ? row - v.win_cap : row;
-      const uint32_t ow = win ? (uint32_t)row * D + AT_QCH * w + 32u * g : AT_OOB;
-      r.a = load_b128(v.win, ow);
-      r.b = load_b128(v.win, ow + 16u);
-      r.kind = win ? 2 : 0;
-    }
-    return r;
+    const int wi = slot - a.k;
+    const bool win = live && wi >= 0 && wi < NWIN && v.p - (NWIN - 1) + wi >= 0;
+    int row = v.wbase + wi;
+    row = row >= v.win_cap ? row - v.win_cap : row;
+    const uint32_t ow = win ? (uint32_t)row * D + AT_QCH * w + 32u * g : AT_OOB;
+    r.a = load_b128(v.win, ow);
+    r.b = load_b128(v.win, ow + 16u);
+    r.kind = win ? 2 : 0;
   }
+  return r;
 }
 
-// Key slice s of a slot for a block of the given PATH (t's kind decides
-// inside a PATH_ANY block; a scalar branch).
-template <int PATH>
-__device__ __forceinline__ f16x8 path_slice(int tk, const RawKey& r, int s) {
-  if constexpr (PATH == PATH_ENTRY) return entry_slice(r, s);
-  else if constexpr (PATH == PATH_WINDOW) return window_slice(r, s);
-  else {
-    if (tk == TK_ENTRY) return entry_slice(r, s);
-    if (tk == TK_WINDOW) return window_slice(r, s);
-    return r.kind == 2 ? window_slice(r, s) : entry_slice(r, s);
-  }
-}
+// ---------------------------------------------------------------------------
+// Pair kernel (decode batches): block (query, split) of four waves -- wave w
+// owns channels 128 w .. 128 w + 127 of every key -- takes E pairs of 32
+// selected entries (entry pairs split E .. split E + E - 1) and one pair of
+// 32 window tokens (window pair `split`; the window's four pairs go to
+// splits 0-3), all loaded up front.  Each pair holds one key format, fixed
+// at compile time, so no lane carries the registers of both.  The host
+// picks E and the number of splits so that the blocks fill the GPU about
+// once: a cold gather is bound by the cache lines a compute unit can have
+// in flight, so spreading a query over more compute units shortens it.
+//
+// Key order.  QK runs on two 16-key MFMA tiles per pair; tile 0 row 4 q + r
+// holds pair key 8 q + r and tile 1 row 4 q + r pair key 8 q + 4 + r (q, r <
+// 4).  The score fragment of lane (j, g) -- rows 4 g .. 4 g + 3 of both tiles,
+// column j -- is then head j over pair keys 8 g .. 8 g + 7, which is exactly
+// the A operand that lane feeds to the 16x16x32 P V product: P never moves
+// between lanes, and P V contracts 32 keys per instruction (the 16-key fp16
+// product runs at half the rate on this GPU).
+// Per block:
+//   1. slot ids, Q, and per pair the QK bytes (lane (j, g): the keys of row
+//      j of both tiles, its 32 channels) and the P V bytes (lane (c, g): pair
+//      keys 8 g .. 8 g + 7, channels 128 w + 8 c .. + 7) -- the same rows
+//      loaded in the two layouts the products need, instead of an LDS
+//      transpose per tile;
+//   2. partial S over the wave's channels for every pair -> LDS; barrier;
+//   3. wave p % 4 sums the four partials of pair p (in wave order) and
+//      publishes the pair's head maxima; barrier;
+//   4. the same wave forms P = 2^(S - M) of pair p against the block's head
+//      maxima M, splits it into fp16 hi / lo halves and publishes both with
+//      the pair's head sums; barrier;
+//   5. every wave: P V over all pairs, the hi products of a pair before its
+//      lo products (an accumulator's two updates are eight MFMAs apart).
+constexpr int AT_PAIR = 32;
+constexpr int AT_WIN_PAIRS = NWIN / AT_PAIR;   // window pairs (one per split 0-3)
+static_assert(NWIN % AT_PAIR == 0, "the window is whole pairs");
+constexpr int AT_E_MAX = 4;                    // entry pairs per block, at most
 
-template <int KG, int T>
-struct SplitLds {
-  union {
-    struct {
-      uint8_t k[KG * AT_WAVES][AT_TILE * AT_KPITCH];   // one tile's fp16 key slices per wave (P V)
-      f32x4 s[T][KG][AT_WAVES][64];                      // partial S of every tile
-    } loop;
-    struct {
-      float o[KG > 1 ? KG - 1 : 1][AT_WAVES][32][64];     // scaled O of groups 1..KG-1
-      float ml[KG][2][HEADS];                            // (max, sum) per group and head
-    } red;
-  };
+template <int NP>
+struct PairLds {
+  f32x4 s[NP][AT_WAVES][2][64];   // partial S^T fragments (tile 0, tile 1) per wave
+  f16x8 p[NP][2][64];             // P of every pair as A operands: hi, lo
+  float pmax[NP][HEADS];          // head maxima of each pair
+  float psum[NP][HEADS];          // head sums of each pair's P (hi + lo)
 };
 
-template <int KG, int T, int PATH>
-__device__ __forceinline__ void split_body(SplitLds<KG, T>& lds, const AttnArgs& a, int64_t qi, int split,
-                                           int t_begin, int t_end, int kg, int w, int lane, int j, int g) {
-  const int n_iter = (t_end - t_begin + KG - 1) / KG;   // <= T; the same in every group
-  // slot ids first, then Q: waiting for the ids (to address the keys) does
-  // not wait for Q
-  const QueryView v = query_view(a, qi);
-  int32_t id[T];
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-    const int t = t_begin + kg + KG * i;
-    id[i] = PATH == PATH_WINDOW ? -1 : slot_id(v, a.k, t, t < t_end, j);
-  }
-  float4 qraw[8];
-  load_q(a, qi, j, g, w, qraw);
-  RawKey rk[T];
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-    const int t = t_begin + kg + KG * i;
-    rk[i] = load_slot_p<PATH>(v, a, t, t < t_end, j, g, w, id[i]);
-  }
-  f16x8 qh[4], ql[4];
-  split_q(qraw, a.c_log2, qh, ql);
+// Row i < 16 of QK tile h of a pair is pair key 8 (i >> 2) + 4 h + (i & 3).
+__device__ __forceinline__ int pair_row_key(int h, int i) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
-  // ---- partial S of every tile (A operand straight from the registers) ----
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-    if (i >= n_iter) break;   // block-uniform
-    const int tk = tile_kind(t_begin + kg + KG * i, a.k);
-    f32x4 sh = {0.f, 0.f, 0.f, 0.f}, sl = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const f16x8 av = path_slice<PATH>(tk, rk[i], s);
-      sh = mfma_f16_16x16x32(av, qh[s], sh);
-      sl = mfma_f16_16x16x32(av, ql[s], sl);
-    }
-    lds.loop.s[i][kg][w][lane] = f32x4{sh[0] + sl[0], sh[1] + sl[1], sh[2] + sl[2], sh[3] + sl[3]};
-  }
-  __syncthreads();
-
-  // ---- one softmax over the group's keys (lane: head j, keys 4g + r) ------
-  float x[T][4];
-  float mx = -__builtin_huge_valf();
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-    if (i < n_iter) {
-      f32x4 S = lds.loop.s[i][kg][0][lane];
-#pragma unroll
-      for (int vv = 1; vv < AT_WAVES; ++vv) {
-        const f32x4 o = lds.loop.s[i][kg][vv][lane];
-        S[0] += o[0]; S[1] += o[1]; S[2] += o[2]; S[3] += o[3];
-      }
-      const uint32_t vmask = (uint32_t)(__ballot(rk[i].kind != 0) & 0xFFFFull);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x[i][r] = ((vmask >> (4 * g + r)) & 1u) ? S[r] : -__builtin_huge_valf();
-        mx = fmaxf(mx, x[i][r]);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[i][r] = -__builtin_huge_valf();
-    }
-  }
-  mx = max_xor32(max_xor16(mx));   // head j's max over the group's keys
-  const float base = (mx == -__builtin_huge_valf()) ? 0.f : mx;
-  AttnState st;
-  state_init(st);
-  st.m_run = mx;
-  f16x4 ph[T], pl[T];
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float pr = exp2_loop(x[i][r] - base);   // <= 1; 0 for an absent key
-      const _Float16 h = (_Float16)pr;
-      const _Float16 l = (_Float16)(pr - (float)h);
-      ph[i][r] = h;
-      pl[i][r] = l;
-      st.l_run += (float)h + (float)l;
-    }
-  }
-
-  // ---- P V tile by tile -----------------------------------------------------
-  uint8_t* krow = lds.loop.k[AT_WAVES * kg + w];
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-    if (i >= n_iter) break;
-    const int tk = tile_kind(t_begin + kg + KG * i, a.k);
-    __builtin_amdgcn_wave_barrier();   // the previous tile's LDS reads come first
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      *reinterpret_cast<f16x8*>(krow + j * AT_KPITCH + 64 * g + 16 * s) = path_slice<PATH>(tk, rk[i], s);
-    __builtin_amdgcn_wave_barrier();   // stores before the transposed reads (LDS keeps wave order)
-    uint4 vk[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) vk[kk] = *reinterpret_cast<const uint4*>(krow + (4 * g + kk) * AT_KPITCH + 16 * j);
-    const uint32_t w0[4] = {vk[0].x, vk[0].y, vk[0].z, vk[0].w};
-    const uint32_t w1[4] = {vk[1].x, vk[1].y, vk[1].z, vk[1].w};
-    const uint32_t w2[4] = {vk[2].x, vk[2].y, vk[2].z, vk[2].w};
-    const uint32_t w3[4] = {vk[3].x, vk[3].y, vk[3].z, vk[3].w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const f16x2 a0 = bits_f16x2(__builtin_amdgcn_perm(w1[c], w0[c], 0x05040100u));
-      const f16x2 a1 = bits_f16x2(__builtin_amdgcn_perm(w3[c], w2[c], 0x05040100u));
-      const f16x2 b0 = bits_f16x2(__builtin_amdgcn_perm(w1[c], w0[c], 0x07060302u));
-      const f16x2 b1 = bits_f16x2(__builtin_amdgcn_perm(w3[c], w2[c], 0x07060302u));
-      const f16x4 blo = {a0[0], a0[1], a1[0], a1[1]};
-      const f16x4 bhi = {b0[0], b0[1], b1[0], b1[1]};
-      st.acc_o[2 * c] = mfma_f16_16x16x16(ph[i], blo, st.acc_o[2 * c]);
-      st.acc_o[2 * c + 1] = mfma_f16_16x16x16(ph[i], bhi, st.acc_o[2 * c + 1]);
-      st.acc_o[2 * c] = mfma_f16_16x16x16(pl[i], blo, st.acc_o[2 * c]);
-      st.acc_o[2 * c + 1] = mfma_f16_16x16x16(pl[i], bhi, st.acc_o[2 * c + 1]);
-    }
-  }
-  attn_finish<KG>(lds, st, a, qi, split, kg, w, lane, j, g);
+// Key slot of key 0 of pair p of a block: entries are slots 0 .. k-1 (entry
+// pair e holds slots 32 e ..), window token i is slot k + i.
+template <int E>
+__device__ __forceinline__ int pair_slot0(const AttnArgs& a, int split, int p) {
+  return p < E ? AT_PAIR * (split * E + p) : a.k + AT_PAIR * split;
 }
 
-template <int KG, int T>
-__global__ __launch_bounds__(AT_THREADS * KG) void attn_split_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) SplitLds<KG, T> lds;
+// P V bytes of one key (lane column c, wave w): channels 128 w + 8 c .. + 7 --
+// four E2M1 code bytes and the E4M3 scale of their 16-channel group, or
+// eight E4M3 window bytes.  Absent keys read past the views (zeros).
+struct RawV {
+  uint32_t c;    // codes, or window bytes 0-3
+  uint32_t w1;   // window bytes 4-7
+  uint32_t sc;   // scale byte (entries)
+};
+
+template <int PATH>
+__device__ __forceinline__ RawV load_v(const QueryView& v, const AttnArgs& a, int slot, int c, int w, int32_t id,
+                                       bool* valid) {
+  RawV r;
+  r.c = 0u;
+  r.w1 = 0u;
+  r.sc = 0u;
+  if constexpr (PATH == PATH_ENTRY) {
+    const bool ent = slot < a.k && id >= 0 && id < a.kv_rows;
+    const uint32_t oc = ent ? (uint32_t)id * CODE_BYTES + 64u * w + 4u * c : AT_OOB;
+    const uint32_t os = ent ? (uint32_t)id * SCALE_BYTES + 8u * w + (uint32_t)(c >> 1) : AT_OOB;
+    r.c = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(v.codes, oc, 0, 0);
+    r.sc = (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(v.scales, os, 0, 0);
+    *valid = ent;
+  } else {
+    const int wi = slot - a.k;
+    const bool win = wi >= 0 && wi < NWIN && v.p - (NWIN - 1) + wi >= 0;
+    int row = v.wbase + wi;
+    row = row >= v.win_cap ? row - v.win_cap : row;
+    const uint32_t ow = win ? (uint32_t)row * D + AT_QCH * w + 8u * c : AT_OOB;
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(v.win, ow, 0, 0);
+    r.c = (uint32_t)x[0];
+    r.w1 = (uint32_t)x[1];
+    *valid = win;
+  }
+  return r;
+}
+
+// The eight B operands of a pair's P V (N-tile n: channel 128 w + 8 c + n of
+// pair keys 8 g .. 8 g + 7) from the lane's eight RawV (key kk = 8 g + kk).
+// Entry bytes widen with scale 1 and are multiplied by the group scale in
+// fp16 (E2M1 x E4M3 has at most 5 significant bits: exact).
+template <int PATH>
+__device__ __forceinline__ void pair_v_operands(const RawV (&rv)[8], f16x8 (&vb)[8]) {
+  uint32_t wv[8][4];   // key kk: channels (2 b, 2 b + 1) as an fp16 pair, b < 4
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    f16x2 e[4];
+    if constexpr (PATH == PATH_ENTRY) {
+      const _Float16 s = fp8x2_to_f16<0>(rv[kk].sc)[0];
+      const f16x2 sp = f16x2{s, s};
+      e[0] = fp4x2_to_f16<0>(rv[kk].c) * sp;
+      e[1] = fp4x2_to_f16<1>(rv[kk].c) * sp;
+      e[2] = fp4x2_to_f16<2>(rv[kk].c) * sp;
+      e[3] = fp4x2_to_f16<3>(rv[kk].c) * sp;
+    } else {
+      e[0] = fp8x2_to_f16<0>(rv[kk].c);
+      e[1] = fp8x2_to_f16<1>(rv[kk].c);
+      e[2] = fp8x2_to_f16<0>(rv[kk].w1);
+      e[3] = fp8x2_to_f16<1>(rv[kk].w1);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) wv[kk][b] = f16x2_bits(e[b]);
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    uint32_t lo[4], hi[4];   // channel 2 b / 2 b + 1 of key pairs (2 i, 2 i + 1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = __builtin_amdgcn_perm(wv[2 * i + 1][b], wv[2 * i][b], 0x05040100u);
+      hi[i] = __builtin_amdgcn_perm(wv[2 * i + 1][b], wv[2 * i][b], 0x07060302u);
+    }
+    vb[2 * b] = __builtin_bit_cast(f16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+    vb[2 * b + 1] = __builtin_bit_cast(f16x8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+  }
+}
+
+template <int E>
+__global__ __launch_bounds__(AT_THREADS) void attn_pair_kernel(AttnArgs a) {
+  constexpr int NP = E + 1;   // E entry pairs, then the window pair
+  __shared__ __attribute__((aligned(16))) PairLds<NP> lds;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = (tid >> 6) & (AT_WAVES - 1);
-  const int kg = __builtin_amdgcn_readfirstlane(tid >> 8);   // wave-uniform
+  const int lane = tid & 63, w = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
   const int64_t qi = blockIdx.x;   // query in x: see attn_grid
   const int split = blockIdx.y;
   if (qi >= a.n_queries) return;  // grid padding (the whole block)
-  const int n_tiles = (a.k + NWIN + AT_TILE - 1) / AT_TILE;
-  const int t_begin = split * a.tiles_per_split;
-  int t_end = t_begin + a.tiles_per_split;
-  t_end = t_end < n_tiles ? t_end : n_tiles;
-  const int k0 = tile_kind(t_begin, a.k), k1 = tile_kind(t_end - 1, a.k);   // block-uniform
-  if (k0 == TK_ENTRY && k1 == TK_ENTRY)
-    split_body<KG, T, PATH_ENTRY>(lds, a, qi, split, t_begin, t_end, kg, w, lane, j, g);
-  else if (k0 == TK_WINDOW && k1 == TK_WINDOW)
-    split_body<KG, T, PATH_WINDOW>(lds, a, qi, split, t_begin, t_end, kg, w, lane, j, g);
-  else
-    split_body<KG, T, PATH_ANY>(lds, a, qi, split, t_begin, t_end, kg, w, lane, j, g);
+  const QueryView v = query_view(a, qi);
+
+  // ---- 1. loads ---------------------------------------------------------------
+  int32_t idq[E][2], idv[E][8];
+#pragma unroll
+  for (int p = 0; p < E; ++p) {
+    const int base = pair_slot0<E>(a, split, p);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) idq[p][h] = slot_id(v, a.k, 0, true, base + pair_row_key(h, j));
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) idv[p][kk] = slot_id(v, a.k, 0, true, base + 8 * g + kk);
+  }
+  float4 qraw[8];
+  load_q(a, qi, j, g, w, qraw);
+  RawKey rk[NP][2];
+  RawV rv[NP][8];
+  uint32_t vbits[NP];   // bit kk: pair key 8 g + kk is present
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int base = pair_slot0<E>(a, split, p);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int slot = base + pair_row_key(h, j);
+      rk[p][h] = p < E ? load_slot_p<PATH_ENTRY>(v, a, slot, true, g, w, idq[p < E ? p : 0][h])
+                       : load_slot_p<PATH_WINDOW>(v, a, slot, true, g, w, -1);
+    }
+    vbits[p] = 0u;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      bool ok;
+      const int slot = base + 8 * g + kk;
+      rv[p][kk] = p < E ? load_v<PATH_ENTRY>(v, a, slot, j, w, idv[p < E ? p : 0][kk], &ok)
+                        : load_v<PATH_WINDOW>(v, a, slot, j, w, -1, &ok);
+      vbits[p] |= (ok ? 1u : 0u) << kk;
+    }
+  }
+  f16x8 qh[4], ql[4];
+  split_q(qraw, a.c_log2, qh, ql);
+
+  // ---- 2. partial S^T of every pair ------------------------------------------------
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 sh = {0.f, 0.f, 0.f, 0.f}, sl = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f16x8 av = p < E ? entry_slice(rk[p][h], s) : window_slice(rk[p][h], s);
+        sh = mfma_f16_16x16x32(av, qh[s], sh);
+        sl = mfma_f16_16x16x32(av, ql[s], sl);
+      }
+      lds.s[p][w][h][lane] = f32x4{sh[0] + sl[0], sh[1] + sl[1], sh[2] + sl[2], sh[3] + sl[3]};
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. wave p % 4: the scores of pair p and their head maxima -------------------
+  constexpr int MINE = (NP + AT_WAVES - 1) / AT_WAVES;   // pairs per wave, at most
+  float x[MINE][8];
+#pragma unroll
+  for (int m = 0; m < MINE; ++m) {
+    const int p = w + AT_WAVES * m;   // wave-uniform
+    if (p < NP) {
+      uint32_t vb_p = vbits[0];
+#pragma unroll
+      for (int q = 1; q < NP; ++q) vb_p = q == p ? vbits[q] : vb_p;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 S = lds.s[p][0][h][lane];
+#pragma unroll
+        for (int vv = 1; vv < AT_WAVES; ++vv) {
+          const f32x4 o = lds.s[p][vv][h][lane];
+          S[0] += o[0]; S[1] += o[1]; S[2] += o[2]; S[3] += o[3];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[m][4 * h + r] = S[r];
+      }
+      // x[m][kk] is pair key 8 g + kk (tile 0 rows for kk < 4, tile 1 rows
+      // for kk >= 4); its presence was found where the lane loaded it for P V
+      float mx = -__builtin_huge_valf();
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        x[m][kk] = ((vb_p >> kk) & 1u) ? x[m][kk] : -__builtin_huge_valf();
+        mx = fmaxf(mx, x[m][kk]);
+      }
+      mx = max_xor32(max_xor16(mx));
+      if (g == 0) lds.pmax[p][j] = mx;
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. P of the wave's pairs against the block's head maxima --------------------
+  float M = lds.pmax[0][j];
+#pragma unroll
+  for (int p = 1; p < NP; ++p) M = fmaxf(M, lds.pmax[p][j]);
+  const float base = (M == -__builtin_huge_valf()) ? 0.f : M;
+#pragma unroll
+  for (int m = 0; m < MINE; ++m) {
+    const int p = w + AT_WAVES * m;
+    if (p < NP) {
+      f16x8 ph, pl;
+      float psum = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const float pr = exp2_loop(x[m][kk] - base);   // <= 1; 0 for an absent key
+        const _Float16 hv = (_Float16)pr;
+        const _Float16 lv = (_Float16)(pr - (float)hv);
+        ph[kk] = hv;
+        pl[kk] = lv;
+        psum += (float)hv + (float)lv;
+      }
+      psum = sum_xor32(sum_xor16(psum));
+      lds.p[p][0][lane] = ph;
+      lds.p[p][1][lane] = pl;
+      if (g == 0) lds.psum[p][j] = psum;
+    }
+  }
+  __syncthreads();
+
+  // ---- 5. P V over all pairs ----------------------------------------------------------
+  f32x4 acc[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    f16x8 vb[8];
+    if (p < E) pair_v_operands<PATH_ENTRY>(rv[p], vb);
+    else pair_v_operands<PATH_WINDOW>(rv[p], vb);
+    const f16x8 ph = lds.p[p][0][lane], pl = lds.p[p][1][lane];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[n] = mfma_f16_16x16x32(ph, vb[n], acc[n]);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[n] = mfma_f16_16x16x32(pl, vb[n], acc[n]);
+  }
+
+  // ---- result: O of heads 4 g + r, channels 128 w + 8 j + n --------------------------
+  float lsum[4], mrow[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * g + r;
+    float L = lds.psum[0][h], Mh = lds.pmax[0][h];
+#pragma unroll
+    for (int p = 1; p < NP; ++p) {
+      L += lds.psum[p][h];
+      Mh = fmaxf(Mh, lds.pmax[p][h]);
+    }
+    lsum[r] = L;
+    mrow[r] = Mh;
+  }
+  if (a.n_splits == 1) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float inv = lsum[r] > 0.f ? 1.0f / lsum[r] : 0.f;
+      float4* dst = reinterpret_cast<float4*>(a.out + (qi * HEADS + 4 * g + r) * D + AT_QCH * w + 8 * j);
+      dst[0] = make_float4(acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv);
+      dst[1] = make_float4(acc[4][r] * inv, acc[5][r] * inv, acc[6][r] * inv, acc[7][r] * inv);
+    }
+  } else {
+    const int64_t ps = qi * a.n_splits + split;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float4* dst = reinterpret_cast<float4*>(a.part_o + (ps * HEADS + 4 * g + r) * D + AT_QCH * w + 8 * j);
+      dst[0] = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+      dst[1] = make_float4(acc[4][r], acc[5][r], acc[6][r], acc[7][r]);
+    }
+    if (w == 0 && j == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        a.part_ml[(ps * 2 + 0) * HEADS + 4 * g + r] = mrow[r];
+        a.part_ml[(ps * 2 + 1) * HEADS + 4 * g + r] = lsum[r];
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -791,46 +925,34 @@ dim3 attn_grid(int64_t Q, int y) {
   return dim3((unsigned)xq, (unsigned)y);
 }
 
-// Launch plan.  kind 0: split kernel (KG groups x T tiles per block, all
-// loaded up front); kind 1: stream kernel.
+// Launch plan.  kind 0: pair kernel (e entry pairs + one window pair per
+// block, all loaded up front); kind 1: stream kernel.
 struct AttnPlan {
-  int kind, kg, t, n_splits, tiles_per_split;
+  int kind, kg, e, n_splits, tiles_per_split;
 };
 
-#ifndef CSA_ATTN_SPLIT_KG
-#define CSA_ATTN_SPLIT_KG 1
-#endif
-#ifndef CSA_ATTN_SPLIT_T
-#define CSA_ATTN_SPLIT_T 8
-#endif
-constexpr int SPLIT_KG = CSA_ATTN_SPLIT_KG;     // key groups per split block
-constexpr int SPLIT_T = CSA_ATTN_SPLIT_T;       // tiles per group, loaded up front
-
-// Below 512 queries (decode batches) a query's tiles go to splits of
-// SPLIT_KG x SPLIT_T tiles when that needs at most AT_MAX_SPLITS splits (k up
-// to ~1.9K); each group holds every key it uses in registers before
-// computing.  Longer selections stream in 4 splits of two groups.  From 512
-// queries on (prefill) one group streams every tile of its query (no
-// partials).
-// Measured in the 1M / 128K decode steps (batch 32 / 64, k = 512, traced
-// inside the captured step): one group of 8 tiles per split (5 splits) ran
-// 12.4 / ~15 us per layer, the same as 10 splits of 4 tiles and as the
-// former streaming plan (4 splits of two groups, two tiles ahead: 12.2 /
-// 14.8 us, with plain fp16 Q and P); two groups of 4 or 5 tiles ran 15-16
-// us.  What sets the time is not the tile loop: a launch whose blocks exit
-// at once, plus the combine, already takes ~2/3 of it, and each split's Q
-// read and partial write add to it (twice the splits, ~+6 us).
+// Below 512 queries (decode batches) the pair kernel takes a query in
+// max(4, ceil(k / 32e)) splits of e entry pairs (the window's four pairs go
+// to splits 0-3), with e chosen so that the Q x splits blocks fill the GPU
+// about once (e <= AT_E_MAX, splits <= AT_MAX_SPLITS: k up to 2,048).
+// Longer selections stream in 4 splits of two groups.  From 512 queries on
+// (prefill) one group streams every tile of its query (no partials).
 AttnPlan attn_plan(int64_t Q, int32_t k) {
   const int n_tiles = (k + NWIN + AT_TILE - 1) / AT_TILE;
   AttnPlan pl;
   if (Q < 512) {
-    const int per = SPLIT_KG * SPLIT_T;
-    const int s = (n_tiles + per - 1) / per;
+    const int n_e = (k + AT_PAIR - 1) / AT_PAIR;
+    int want = (int)((256 + Q - 1) / Q);
+    want = want < AT_WIN_PAIRS ? AT_WIN_PAIRS : (want > AT_MAX_SPLITS ? AT_MAX_SPLITS : want);
+    int e = (n_e + want - 1) / want;
+    e = e < 1 ? 1 : (e > AT_E_MAX ? AT_E_MAX : e);
+    int s = (n_e + e - 1) / e;
+    s = s < AT_WIN_PAIRS ? AT_WIN_PAIRS : s;
     if (s <= AT_MAX_SPLITS) {
       pl.kind = 0;
-      pl.kg = SPLIT_KG;
-      pl.t = SPLIT_T;
-      pl.tiles_per_split = per;
+      pl.kg = 1;
+      pl.e = e;
+      pl.tiles_per_split = 0;
       pl.n_splits = s;
       return pl;
     }
@@ -847,7 +969,7 @@ AttnPlan attn_plan(int64_t Q, int32_t k) {
   s = s < 1 ? 1 : s;
   pl.kind = 1;
   pl.kg = kg;
-  pl.t = 0;
+  pl.e = 0;
   pl.tiles_per_split = (n_tiles + s - 1) / s;
   pl.n_splits = (n_tiles + pl.tiles_per_split - 1) / pl.tiles_per_split;
   return pl;
@@ -884,8 +1006,14 @@ hipError_t launch_sparse_attn(const float* q, const int32_t* q_pos, int64_t n_se
   }
   a.n_queries = Q;
   const dim3 grid = attn_grid(Q, a.n_splits);
-  if (pl.kind == 0)
-    hipLaunchKernelGGL((attn_split_kernel<SPLIT_KG, SPLIT_T>), grid, dim3(AT_THREADS * SPLIT_KG), 0, st, a);
+  if (pl.kind == 0) {
+    switch (pl.e) {
+      case 1: hipLaunchKernelGGL(attn_pair_kernel<1>, grid, dim3(AT_THREADS), 0, st, a); break;
+      case 2: hipLaunchKernelGGL(attn_pair_kernel<2>, grid, dim3(AT_THREADS), 0, st, a); break;
+      case 3: hipLaunchKernelGGL(attn_pair_kernel<3>, grid, dim3(AT_THREADS), 0, st, a); break;
+      default: hipLaunchKernelGGL(attn_pair_kernel<AT_E_MAX>, grid, dim3(AT_THREADS), 0, st, a); break;
+    }
+  }
   else if (pl.kg == 2)
     hipLaunchKernelGGL(attn_stream_kernel<2>, grid, dim3(AT_THREADS * 2), 0, st, a);
   else

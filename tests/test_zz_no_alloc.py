@@ -55,13 +55,14 @@ def test_noalloc_matches_workspace_entry_two_calls():
 
 
 def test_noalloc_rejects_more_than_the_scratch():
-    q, pos, codes, scales, idx, win = _case(5, 250, 1, 1000, 512, 128)
-    out = torch.full((250, 16, 512), 7.0, device=DEV)
+    n = 400   # decode batch whose split partials exceed the scratch
+    q, pos, codes, scales, idx, win = _case(5, n, 1, 1000, 512, 128)
+    out = torch.full((n, 16, 512), 7.0, device=DEV)
     lib = _lib.load()
-    need = lib.csa_sparse_attn_workspace_size(250, 512)
+    need = lib.csa_sparse_attn_workspace_size(n, 512)
     assert need > lib.csa_noalloc_scratch_bytes()
     with pytest.raises(ops.CsaError) as e:
-        ops.csa_sparse_attn_noalloc(q, pos, codes, scales, idx, win, 250, 1, out)
+        ops.csa_sparse_attn_noalloc(q, pos, codes, scales, idx, win, n, 1, out)
     assert e.value.status == 2 and "scratch" in e.value.message
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
