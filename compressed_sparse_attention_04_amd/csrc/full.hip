@@ -1,7 +1,7 @@
 // Fused Full-layer selection: the block pool, then the Top-K by rescoring
 // only the entries of the best blocks.
 //
-// P3 §02: a Full layer scores every causally visible entry, keeps the
+// "DeepSeek-V4.1 架构解析" §02: a Full layer scores every causally visible entry, keeps the
 // Top-512, and (hierarchical pool) the 2,048 blocks of 8 entries with the
 // largest block max.  Every Top-K entry lies in one of the top_k blocks by
 // block max (equal maxima go to the lower block, the same rule as for

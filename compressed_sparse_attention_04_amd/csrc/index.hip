@@ -1,6 +1,6 @@
 // Indexer scoring on the matrix cores.
 //
-// P3 §02: Full layers score every causally visible position; Reindex layers
+// "DeepSeek-V4.1 架构解析" §02: Full layers score every causally visible position; Reindex layers
 // rescore with their own indexer query, inside the hierarchical pool.
 // score_j = sum_h w_h * ReLU(q_h . k_j), 8 heads x 128 dims, E4M3 operands.
 //

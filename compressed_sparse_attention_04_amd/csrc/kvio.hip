@@ -1,6 +1,6 @@
 // Global-KV files: the MXFP4 entries (codes, scales) and indexer keys of a
 // group's sequences written to a file and read back, so that decoding resumes
-// from a persistent cache (P3 §03: the global KV is what stays in the
+// from a persistent cache ("DeepSeek-V4.1 架构解析" §03: the global KV is what stays in the
 // persistent cache; the window is rebuilt by replay instead).
 //
 // File layout, little-endian:

@@ -1,7 +1,7 @@
 // MXFP4 store path: quantize / dequantize, window append, and the fused
 // compress (4 tokens -> 1 entry) + RMSNorm + RoPE + quantize chain.
 //
-// P3 §02 (sequence compression), P2 §2.1 (4:1), P3 §03 (E2M1 values with an
+// "DeepSeek-V4.1 架构解析" §02 (sequence compression), the DeepSeek V4 overview page §2.1 (4:1), "DeepSeek-V4.1 架构解析" §03 (E2M1 values with an
 // E4M3 scale per 16 channels, RMSNorm before, quantize after RoPE; SWA KV in
 // FP8).
 #include "common.h"

@@ -1,6 +1,6 @@
 // Top-K selection and the hierarchical block pool.
 //
-// P3 §02: the first Full layer picks the Top-512 over every visible position,
+// "DeepSeek-V4.1 架构解析" §02: the first Full layer picks the Top-512 over every visible position,
 // then ranks 8-position blocks by their largest score and keeps 2,048 of them
 // (16,384 candidates) for the Reindex layers.  Equal scores go to the lower
 // column (and so the lower entry id); -inf and NaN columns are never selected.

@@ -1,7 +1,7 @@
 // Block-wide exact Top-K selection over keys held in registers (device
 // routines shared by the selection kernels and the fused Full-layer kernel).
 //
-// P3 §02: the Top-512 of the visible scores, ties to the lower position.
+// "DeepSeek-V4.1 架构解析" §02: the Top-512 of the visible scores, ties to the lower position.
 // The method is described in select.hip.
 #pragma once
 

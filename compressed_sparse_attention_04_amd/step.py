@@ -1,6 +1,6 @@
 """One CSA2 layer-group step driven through the C ABI.
 
-A step, in order (P3 §02 layer modes; P3 §03 window / MXFP4 store):
+A step, in order ("DeepSeek-V4.1 架构解析" §02 layer modes; "DeepSeek-V4.1 架构解析" §03 window / MXFP4 store):
   1. append the step's tokens to the FP8 window ring (a9);
   2. compress + RoPE + MXFP4-store the entries the step's tokens complete (a1, a2);
   3. run the layer group: Full (score, Top-K, optional pool), then Reuse and
@@ -10,7 +10,7 @@ they are built from token latents, and the 127 window tokens before the
 step's first token); it is not part of the timed work.
 
 A schedule (``ScheduleStep``) runs several groups in order, each with its own
-global KV; a decode token passes through every group (P3 §01, §02).
+global KV; a decode token passes through every group ("DeepSeek-V4.1 架构解析" §01, §02).
 """
 
 import math
@@ -151,7 +151,7 @@ def from_workload(wl, device=None):
 
 
 class ScheduleStep:
-    """Groups of layers run in order on one stream (P3 §02 schedule); every
+    """Groups of layers run in order on one stream ("DeepSeek-V4.1 架构解析" §02 schedule); every
     group is a LayerStep with its own global KV.  One workspace serves all."""
 
     def __init__(self, groups):

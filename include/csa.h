@@ -3,13 +3,14 @@
  * an AMD Instinct MI355X (gfx950).
  *
  * Sources of the method ("the pages"):
- *   P3  "DeepSeek-V4.1 架构解析：把长上下文的成本瓶颈从算力挪到存储"
+ *   "DeepSeek-V4.1 架构解析：把长上下文的成本瓶颈从算力挪到存储"
  *       (blog.yuzhonghai.cloud/deepseek-v41-arch), §02 CSA2 (layer modes
  *       Full / Reindex / Reuse, Top-512, the hierarchical pool of 2,048 blocks
  *       x 8 positions) and §03 精度与状态重建 (MXFP4 = E2M1 values with one E4M3
  *       scale per 16 channels, quantize after RoPE, FP4 for storage only, SWA
- *       KV in FP8, n_win = 128).
- *   P2  DeepSeek V4 overview (wmrh.cn/news/159405) §2.1 (4:1 compression).
+ *       KV in FP8, n_win = 128); cited below as "DeepSeek-V4.1 架构解析" §NN.
+ *   The DeepSeek V4 overview page (wmrh.cn/news/159405) §2.1 (4:1
+ *       compression of the predecessor).
  * The pages give no compressor or indexer formula and no dimensions; this
  * library implements the readings stated at each entry point.
  *
@@ -78,7 +79,7 @@ const char* csa_last_error(void);
 int32_t csa_version(void);
 
 /* ---------------------------------------------------------------- a2 ----
- * csa_quantize: MXFP4-quantize n post-RoPE entries (P3 §03).
+ * csa_quantize: MXFP4-quantize n post-RoPE entries ("DeepSeek-V4.1 架构解析" §03).
  *   e      [n, 512] float32, the quantizer input
  *   codes  [n, 256] uint8 out: channel 2k in the low nibble of byte k; each
  *          nibble = signbit(x) << 3 | RNE_E2M1(|x| / s) (saturating at 6,
@@ -92,14 +93,14 @@ csa_status csa_quantize(const float* e, int64_t n, uint8_t* codes, uint8_t* scal
                         hipStream_t stream);
 
 /* csa_dequantize: codes/scales of n entries -> float32 [n, 512] (s * E2M1(c)).
- * P3 §03: the FP4 cache is dequantized before attention. */
+ * "DeepSeek-V4.1 架构解析" §03: the FP4 cache is dequantized before attention. */
 csa_status csa_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t n,
                           float* out, hipStream_t stream);
 
 /* ----------------------------------------------------------- a1 + a2 ----
  * csa_compress_quant: compress every 4 token latents into one entry, RMSNorm,
- * RoPE, MXFP4-quantize and store (P3 §02 sequence compression; P2 §2.1 4:1;
- * P3 §03 RMSNorm magnitude ~1, quantize after RoPE).
+ * RoPE, MXFP4-quantize and store ("DeepSeek-V4.1 架构解析" §02 sequence compression; the DeepSeek V4 overview page §2.1 4:1;
+ * "DeepSeek-V4.1 架构解析" §03 RMSNorm magnitude ~1, quantize after RoPE).
  *   Entries are (sequence s < n_seq, r < n_per_seq).  Entry (s, r) reads the 4
  *   tokens x + s * x_seq_stride + r * 4 * 512 (float32 [4, 512]) and writes
  *   row s * out_seq_stride + r of codes [.., 256] / scales [.., 32].
@@ -122,7 +123,7 @@ csa_status csa_compress_quant(const float* x, int64_t n_seq, int64_t n_per_seq,
 
 /* ---------------------------------------------------------------- a9 ----
  * csa_window_append: write n_tok token latents of each of n_seq sequences into
- * the FP8 sliding-window ring (P3 §03: SWA KV kept in FP8; n_win = 128).
+ * the FP8 sliding-window ring ("DeepSeek-V4.1 架构解析" §03: SWA KV kept in FP8; n_win = 128).
  *   x       float32, token t of sequence s at x + s * x_seq_stride + t * 512
  *   pos0    int32 [n_seq]: position of token 0 of each sequence
  *   win     uint8 [n_seq, win_cap, 512]: token at position p goes to row
@@ -135,7 +136,7 @@ csa_status csa_window_append(const float* x, int64_t n_seq, int64_t n_tok, int64
 
 /* ---------------------------------------------------------------- f2 ----
  * csa_window_rebuild: rebuild n_ring window rings from their latest tokens
- * (P3 §03, SWA Bounded Replay: the window state is not kept in the
+ * ("DeepSeek-V4.1 架构解析" §03, SWA Bounded Replay: the window state is not kept in the
  * persistent cache; after a prefix-cache hit only the last n_win = 128
  * tokens are replayed).  One ring per (layer, sequence).
  *   x        float32: token i (0 <= i < n_tok) of ring r at
@@ -161,7 +162,7 @@ csa_status csa_window_rebuild(const float* x, int64_t n_ring, int64_t n_tok, int
                               hipStream_t stream);
 
 /* ---------------------------------------------------------------- f4 ----
- * Global-KV files (P3 §03: the global KV -- MXFP4 entries and indexer keys --
+ * Global-KV files ("DeepSeek-V4.1 架构解析" §03: the global KV -- MXFP4 entries and indexer keys --
  * is what the persistent cache keeps; the window is rebuilt by replay).  One
  * file holds n_seq sequences' first n_entries rows of codes [.., 256], scales
  * [.., 32] and k_fp8 [.., 128], in device buffers laid out [n_seq, seq_rows,
@@ -217,7 +218,7 @@ csa_status csa_probe_mfma_f8(float* out, int32_t blocks, int32_t iters, int32_t 
 csa_status csa_probe_read(const uint8_t* buf, int64_t bytes, float* out, hipStream_t stream);
 
 /* ---------------------------------------------------------------- a3 ----
- * csa_index_score: indexer scores of Q = n_seq * q_per_seq queries (P3 §02:
+ * csa_index_score: indexer scores of Q = n_seq * q_per_seq queries ("DeepSeek-V4.1 架构解析" §02:
  * Full layers score every causally visible position; Reindex layers rescore
  * with their own query, inside the hierarchical pool when one exists).
  *   Query q belongs to sequence q / q_per_seq and sits at token position
@@ -246,7 +247,7 @@ csa_status csa_index_score(const uint8_t* q_fp8, const float* w, const int32_t* 
 
 /* ---------------------------------------------------------------- a4 ----
  * csa_topk: for each of Q rows of scores float32 [Q, ncols], select the k
- * columns with the largest scores (P3 §02 Top-512); equal scores go to the
+ * columns with the largest scores ("DeepSeek-V4.1 架构解析" §02 Top-512); equal scores go to the
  * lower column (-0 equals +0); -inf and NaN columns are never selected.
  * Outputs the selected ids in
  * ascending order, -1 padded, into idx int32 [Q, k].
@@ -262,7 +263,7 @@ csa_status csa_topk(const float* scores, int64_t Q, int64_t ncols, const int32_t
                     int32_t k, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------- a5 ----
- * csa_block_pool: the hierarchical pool (P3 §02: rank 8-position blocks by
+ * csa_block_pool: the hierarchical pool ("DeepSeek-V4.1 架构解析" §02: rank 8-position blocks by
  * their largest index score, keep 2,048 blocks = 16,384 candidates).
  *   is_block_max = 1: values float32 [Q, ncols] are block maxima (one column
  *   per block); 0: values are per-entry scores and the block maxima over
@@ -279,8 +280,8 @@ csa_status csa_block_pool(const float* values, int32_t is_block_max, int64_t Q, 
                           hipStream_t stream);
 
 /* ---------------------------------------------------------------- a7 ----
- * csa_sparse_attn: sparse multi-query attention (P3 §02 the selected entries
- * are used for attention; P3 §03 the FP4 cache is dequantized before
+ * csa_sparse_attn: sparse multi-query attention ("DeepSeek-V4.1 架构解析" §02 the selected entries
+ * are used for attention; "DeepSeek-V4.1 架构解析" §03 the FP4 cache is dequantized before
  * attention and the SWA window stays FP8, n_win = 128).
  *   Query q (sequence q / q_per_seq, position q_pos[q]) attends with 16 heads
  *   q float32 [Q, 16, 512] over the union of
@@ -329,7 +330,7 @@ csa_status csa_sparse_attn_noalloc(const float* q, const int32_t* q_pos, int64_t
                                    float sm_scale, float* out, hipStream_t stream);
 
 /* ------------------------------------------------------------ a6 + a8 ----
- * Layer entry points (P3 §02 layer modes).
+ * Layer entry points ("DeepSeek-V4.1 架构解析" §02 layer modes).
  *   Full:    score every visible entry with (q_idx, w_idx) -> Top-k idx;
  *            when build_pool != 0 also the hierarchical pool -> pool_blocks.
  *   Reindex: reuse the Full layer's cache, indexer keys and pool; rescore

@@ -9,15 +9,16 @@ Everything here is plain numpy in float64 (the method's own precision choices,
 such as "round to fp32 before quantizing", are applied explicitly where the
 method makes them).  Each function cites the passage it follows.
 
-Citation key
-------------
-P3  "DeepSeek-V4.1 架构解析：把长上下文的成本瓶颈从算力挪到存储"
+Sources
+-------
+"DeepSeek-V4.1 架构解析：把长上下文的成本瓶颈从算力挪到存储"
     (blog.yuzhonghai.cloud/deepseek-v41-arch), sections
     "02 CSA2：大多数层不再自己算注意力" (layer modes, Top-512, the 2,048-block x 8
     hierarchical pool) and "03 精度与状态重建" (MXFP4 = E2M1 values with one E4M3
     scale per 16 channels, no global scale, 448 x 6 = 2688 range, quantize after
-    RoPE, FP4 for storage only, SWA KV in FP8, n_win = 128).
-P2  "DeepSeek V4" overview (wmrh.cn/news/159405), section 2.1 (4:1 sequence
+    RoPE, FP4 for storage only, SWA KV in FP8, n_win = 128); cited in the
+    docstrings as "DeepSeek-V4.1 架构解析" §NN.
+The DeepSeek V4 overview page (wmrh.cn/news/159405), section 2.1 (4:1 sequence
     compression of the CSA predecessor).
 
 Readings where the pages are silent (the pages give no formula for the

@@ -1,7 +1,7 @@
 """Sparse multi-query attention over selected entries plus the FP8 window.
 
-P3 §02: the selected Top-K entries are "taken to do attention"; CSA2 shrinks the
-number of KV heads (one shared latent serves all query heads).  P3 §03: the
+"DeepSeek-V4.1 架构解析" §02: the selected Top-K entries are "taken to do attention"; CSA2 shrinks the
+number of KV heads (one shared latent serves all query heads).  "DeepSeek-V4.1 架构解析" §03: the
 FP4 cache is dequantized before attention, the sliding-window (SWA) KV stays in
 FP8, and the window is n_win = 128 tokens.
 

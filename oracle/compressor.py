@@ -1,8 +1,8 @@
 """Sequence compression (m = 4 tokens -> 1 entry), RMSNorm and RoPE.
 
-P3 §02 lists "compress the sequence dimension: every m tokens become one entry"
-among CSA2's three compression means; P2 §2.1 gives the predecessor's ratio of
-4:1.  P3 §03 says RMSNorm brings the entry's magnitude to about 1 (so the L2
+"DeepSeek-V4.1 架构解析" §02 lists "compress the sequence dimension: every m tokens become one entry"
+among CSA2's three compression means; the DeepSeek V4 overview page §2.1 gives the predecessor's ratio of
+4:1.  "DeepSeek-V4.1 架构解析" §03 says RMSNorm brings the entry's magnitude to about 1 (so the L2
 norm of a 512-d latent is at most sqrt(512) ~ 22.6), that RoPE is applied before
 quantization, and that RoPE preserves the norm.
 

@@ -1,6 +1,6 @@
 """Number formats of the KV cache: E4M3 (FP8) and E2M1 (FP4).
 
-P3 §03: the main KV is stored as MXFP4 -- E2M1 values with an E4M3 scale per 16
+"DeepSeek-V4.1 架构解析" §03: the main KV is stored as MXFP4 -- E2M1 values with an E4M3 scale per 16
 channels -- and the SWA KV stays in FP8.  The page's range argument
 (448 x 6 = 2688) fixes the E4M3 variant: the largest finite value is 448, i.e.
 the "FN" variant (no infinities; exponent 15 / mantissa 7 is NaN), and the

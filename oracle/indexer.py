@@ -1,6 +1,6 @@
 """Indexer scoring over the causally visible entries.
 
-P3 §02: a Full-mode layer computes its own indexer K and scores every causally
+"DeepSeek-V4.1 架构解析" §02: a Full-mode layer computes its own indexer K and scores every causally
 visible position to pick the Top-512; a Reindex layer reuses the previous
 layer's global KV and indexer K but scores with its own indexer query; with the
 hierarchical pool, Reindex layers score only inside the 16,384-entry pool.

@@ -1,13 +1,13 @@
 """The three CSA2 layer modes and window maintenance, one query at a time.
 
-P3 §02: each layer has a statically assigned mode.
+"DeepSeek-V4.1 架构解析" §02: each layer has a statically assigned mode.
   Full     computes its own main KV, indexer K and Top-K indices;
   Reindex  reuses the previous layer's global KV and indexer K, rescoring with
            its own indexer query to pick a new Top-K (only inside the
            hierarchical pool when one was built);
   Reuse    keeps the most recent Top-K indices and only runs attention.
-P3 §02 also says the first Full layer builds the pool from its own scores.
-P3 §03: the SWA KV is kept in FP8 and bounded to n_win = 128 tokens.
+"DeepSeek-V4.1 架构解析" §02 also says the first Full layer builds the pool from its own scores.
+"DeepSeek-V4.1 架构解析" §03: the SWA KV is kept in FP8 and bounded to n_win = 128 tokens.
 
 Reading where the page is silent: a Reuse layer uses the indices of the most
 recent Full or Reindex layer before it; window tokens are the raw token
@@ -44,7 +44,7 @@ def window_encode(x_tokens):
 
 
 def window_rebuild(x_last, p_last, win_cap):
-    """SWA Bounded Replay (P3 §03): the window ring rebuilt from the latest
+    """SWA Bounded Replay ("DeepSeek-V4.1 架构解析" §03): the window ring rebuilt from the latest
     tokens only.  x_last float32 [n_tok, 512] are the tokens at positions
     p_last - n_tok + 1 .. p_last (n_tok <= win_cap); the token at position t
     goes to row t % win_cap, rows no given token reaches stay zero.  Returns

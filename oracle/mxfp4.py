@@ -1,6 +1,6 @@
 """MXFP4 KV-cache entries: E2M1 values with one E4M3 scale per 16 channels.
 
-P3 §03 fixes the format (E2M1 elements, an E4M3 scale per 16 channels, no
+"DeepSeek-V4.1 架构解析" §03 fixes the format (E2M1 elements, an E4M3 scale per 16 channels, no
 second-level/global scale) and that quantization happens after RoPE and only
 for storage (entries are dequantized before attention).
 

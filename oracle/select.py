@@ -1,6 +1,6 @@
 """Top-K selection and the hierarchical block pool.
 
-P3 §02: the first Full layer of the decoder scans every visible position and
+"DeepSeek-V4.1 架构解析" §02: the first Full layer of the decoder scans every visible position and
 picks the Top-512; it then ranks blocks of 8 positions by the largest index
 score inside each block and keeps 2,048 blocks, a shared pool of 16,384
 candidates in which the following Reindex layers search.

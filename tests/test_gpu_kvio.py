@@ -1,4 +1,4 @@
-"""GPU round trip of the global-KV files (P3 §03: the global KV is what the
+"""GPU round trip of the global-KV files ("DeepSeek-V4.1 架构解析" §03: the global KV is what the
 persistent cache keeps, the window is rebuilt by replay): the bytes written
 are the device rows with the documented header and checksum, loading restores
 them bit-exactly, a damaged file is reported, and decoding resumed from a

@@ -1,4 +1,4 @@
-"""GPU parity of the V4.1 CSA2 layer schedule (P3 §02): three encoder groups
+"""GPU parity of the V4.1 CSA2 layer schedule ("DeepSeek-V4.1 架构解析" §02): three encoder groups
 of a Full layer and five Reuse layers, then the decoder group (a Full layer
 that builds the block pool, three Reuse layers, and four times a Reindex
 layer and three Reuse layers), every group with its own global KV and every

@@ -1,4 +1,4 @@
-"""Pins of the oracle's window rebuild (P3 §03, SWA Bounded Replay: only the
+"""Pins of the oracle's window rebuild ("DeepSeek-V4.1 架构解析" §03, SWA Bounded Replay: only the
 latest n_win = 128 tokens are replayed).  The rebuild places each replayed
 token directly at its ring row; the pins compare it with a different
 computation, a ring that receives every token of the history one at a time,

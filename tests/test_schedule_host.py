@@ -1,5 +1,5 @@
 """The V4.1 CSA2 layer schedule as the workloads define it, against the counts
-the page states (P3 §02: 18 CSA2 encoder layers in three groups of six, each
+the page states ("DeepSeek-V4.1 架构解析" §02: 18 CSA2 encoder layers in three groups of six, each
 led by its only Full layer; 20 decoder layers: one Full and three Reuse, then
 four groups of one Reindex and three Reuse; the decoder's first Full layer
 builds the 2,048-block pool its Reindex layers search).  CPU only."""

@@ -92,13 +92,13 @@ def small_config(kind="decode", n_seq=2, ctx_tokens=1024, chunk=1, layers=("F",)
                   build_pool, synthetic_cache)
 
 
-# The V4.1 CSA2 layer schedule (P3 §02, layer modes): the 18 CSA2 encoder
+# The V4.1 CSA2 layer schedule ("DeepSeek-V4.1 架构解析" §02, layer modes): the 18 CSA2 encoder
 # layers form three groups of one Full layer and five Reuse layers; the 20
 # decoder layers are a Full layer and three Reuse layers, then four times a
 # Reindex layer and three Reuse layers, and the decoder's Full layer builds
 # the block pool its Reindex layers search.  Every group has its own global
 # KV (entries and indexer keys, from its Full layer); every layer has its own
-# 128-token window (P3 §03: the window state is per layer).
+# 128-token window ("DeepSeek-V4.1 架构解析" §03: the window state is per layer).
 V41_ENCODER_GROUP = ["F"] + ["U"] * 5
 V41_DECODER_GROUP = ["F", "U", "U", "U"] + ["I", "U", "U", "U"] * 4
 V41_GROUPS = [(V41_ENCODER_GROUP, False)] * 3 + [(V41_DECODER_GROUP, True)]
