@@ -74,6 +74,7 @@ struct LayerPlan {
   int64_t Q = 0, ncols = 0, nblk = 0;
   size_t off_scores = 0, off_bm = 0, off_blocks = 0, off_sel = 0, off_attn = 0, total = 0;
   bool pooled = false, fused_full = false;
+  bool fused_scores = false;   // fused Full layer that gathers the scan's scores
 };
 
 LayerPlan plan_layer(int32_t mode, const csa_layer_args* a) {
@@ -86,7 +87,16 @@ LayerPlan plan_layer(int32_t mode, const csa_layer_args* a) {
     const int32_t nb = a->build_pool ? a->n_pool_blocks : a->top_k;
     p.nblk = (p.ncols + 7) / 8;
     p.fused_full = mode == CSA_MODE_FULL && full_select_supported(p.nblk, nb, a->top_k);
-    if (!p.fused_full) {
+    // Small decode batches: the scan also writes every score and the fused
+    // selection gathers the chosen blocks' scores, instead of one block per
+    // query gathering and rescoring their 512 KiB of keys (~17 us, latency
+    // bound on a few compute units).  The score stores are 64-byte pieces
+    // that cost the scan far more than their bytes (32 x 1M entries: +28 us
+    // against -12 us of selection; 64 x 128K: -9 us per step), so only
+    // batches with at most 2^22 scores take this path; many queries (prefill)
+    // keep the rescoring, spread over the GPU.
+    p.fused_scores = p.fused_full && p.Q < 512 && p.Q * p.ncols <= ((int64_t)1 << 22);
+    if (!p.fused_full || p.fused_scores) {
       p.off_scores = off;
       off += round_up((size_t)(p.Q * p.ncols) * sizeof(float));
     }
@@ -468,7 +478,7 @@ static csa_status run_attention(const char* fn, const csa_layer_args* a, const L
 static csa_status run_index(const char* fn, int32_t mode, const csa_layer_args* a, const LayerPlan& p,
                             hipStream_t st) {
   char* ws = reinterpret_cast<char*>(a->ws);
-  float* scores = p.fused_full ? nullptr : reinterpret_cast<float*>(ws + p.off_scores);
+  float* scores = (p.fused_full && !p.fused_scores) ? nullptr : reinterpret_cast<float*>(ws + p.off_scores);
   float* bm = (mode == CSA_MODE_FULL) ? reinterpret_cast<float*>(ws + p.off_bm) : nullptr;
   ScoreArgs s{a->q_idx, a->w_idx, a->q_pos, a->n_seq, a->q_per_seq, a->k_fp8, a->k_rows, a->n_entries,
               p.pooled ? a->pool_blocks : nullptr, a->n_pool_blocks, scores, bm};
@@ -482,7 +492,8 @@ static csa_status run_index(const char* fn, int32_t mode, const csa_layer_args* 
   if (p.fused_full)
     return hip_status(launch_full_select(bm, p.nblk, p.Q, a->build_pool ? a->n_pool_blocks : a->top_k,
                                          a->build_pool ? a->pool_blocks : nullptr, a->top_k, a->idx, a->q_idx,
-                                         a->w_idx, a->q_pos, a->q_per_seq, a->k_fp8, a->k_rows, a->n_entries, st),
+                                         a->w_idx, a->q_pos, a->q_per_seq, a->k_fp8, a->k_rows, a->n_entries,
+                                         p.fused_scores ? scores : nullptr, st),
                       fn);
   int32_t* blocks = a->build_pool ? a->pool_blocks : reinterpret_cast<int32_t*>(ws + p.off_blocks);
   const int32_t nb = a->build_pool ? a->n_pool_blocks : a->top_k;

@@ -48,6 +48,7 @@ struct FullSelArgs {
   int64_t q_per_seq;
   const uint8_t* k_fp8;     // [n_seq, k_rows, 128]
   int64_t k_rows, n_entries;
+  const float* scores;      // [Q, n_entries] written by the scan, or null
 };
 
 // NT threads; block maxima per thread; rescored entries per thread; top_k
@@ -115,8 +116,38 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void fu
   }
   __syncthreads();
 
-  // ---- B. rescore the entries of the top_k blocks ---------------------------
-  {
+  // ---- B. the scores of the top_k blocks' entries ----------------------------
+  if (a.scores) {
+    // decode batches: the scan wrote every column's score (-inf past the
+    // visible entries), so gather the 8 scores of each chosen block -- every
+    // load issued before any is used, each from an existing column
+    constexpr int GPT = 8 * KMAX / NT;   // slots per thread
+    const float* srow = a.scores + q * a.n_entries;
+    float v[GPT];
+    bool ok[GPT];
+#pragma unroll
+    for (int u = 0; u < GPT; ++u) {
+      const int slot = tid + NT * u;   // block slot >> 3, entry slot & 7
+      const int i = slot >> 3;
+      const int32_t b = i < K ? top[i] : -1;
+      const int64_t col = 8 * (int64_t)b + (slot & 7);
+      ok[u] = b >= 0 && col < a.n_entries;
+    }
+    if (a.n_entries > 0) {   // block-uniform: an empty row has nothing to read
+#pragma unroll
+      for (int u = 0; u < GPT; ++u) {
+        const int slot = tid + NT * u;
+        const int32_t b = (slot >> 3) < K ? top[slot >> 3] : -1;
+        v[u] = srow[ok[u] ? 8 * (int64_t)b + (slot & 7) : 0];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < GPT; ++u) {
+      const int slot = tid + NT * u;
+      if (slot < 8 * K) sc[slot] = ok[u] ? v[u] : -__builtin_huge_valf();
+    }
+  } else {
+    // rescore the entries of the top_k blocks
     const int64_t seq = q / a.q_per_seq;
     const int nv_pos = visible_count(a.q_pos[q]);
     const int64_t nv = nv_pos < a.n_entries ? nv_pos : a.n_entries;
@@ -222,9 +253,9 @@ bool full_select_supported(int64_t nblk, int32_t nb, int32_t k) {
 hipError_t launch_full_select(const float* block_max, int64_t nblk, int64_t Q, int32_t nb, int32_t* pool,
                               int32_t k, int32_t* idx, const uint8_t* q_fp8, const float* w, const int32_t* q_pos,
                               int64_t q_per_seq, const uint8_t* k_fp8, int64_t k_rows, int64_t n_entries,
-                              hipStream_t st) {
+                              const float* scores, hipStream_t st) {
   if (Q == 0) return hipSuccess;
-  FullSelArgs a{block_max, nblk, nb, pool, k, idx, q_fp8, w, q_pos, q_per_seq, k_fp8, k_rows, n_entries};
+  FullSelArgs a{block_max, nblk, nb, pool, k, idx, q_fp8, w, q_pos, q_per_seq, k_fp8, k_rows, n_entries, scores};
   const dim3 grid(1, (unsigned)Q);
   // many queries: 512-thread blocks, two per compute unit (top_k <= 512,
   // nblk <= 16,384); a few queries: 1,024 threads, the shortest block

@@ -58,10 +58,12 @@ hipError_t launch_pool_topk(const float* block_max, int64_t nblk, const float* s
 // full.hip: Full layer from block maxima alone (pool, then the Top-K of the
 // rescored entries of the top_k blocks).
 bool full_select_supported(int64_t nblk, int32_t nb, int32_t k);
+// scores: the scan's scores [Q, n_entries] (decode batches: gathered for
+// the chosen blocks), or null (their entries are rescored from k_fp8).
 hipError_t launch_full_select(const float* block_max, int64_t nblk, int64_t Q, int32_t nb, int32_t* pool,
                               int32_t k, int32_t* idx, const uint8_t* q_fp8, const float* w, const int32_t* q_pos,
                               int64_t q_per_seq, const uint8_t* k_fp8, int64_t k_rows, int64_t n_entries,
-                              hipStream_t st);
+                              const float* scores, hipStream_t st);
 
 // attn.hip
 size_t attn_workspace_bytes(int64_t Q, int32_t k);
