@@ -381,6 +381,20 @@ def test_sparse_attn(n_seq, q_per_seq, k, p_base):
     check_attn(np_(out), _attn_ref(codes, scales, win, q, idx, pos, q_per_seq, win_cap))
 
 
+# Decode plans: E entry pairs + one window pair per block for E = 1..4 (Q and
+# k chosen so that each E occurs), k not a multiple of the 32-slot pair, the
+# largest k of the pair plan (2,048: 16 splits) and the first k past it,
+# which the stream kernel takes in splits.
+@pytest.mark.parametrize("n_seq,k", [(32, 640), (32, 2048), (8, 2049), (64, 500), (3, 33), (16, 96)])
+def test_sparse_attn_decode_plans(n_seq, k):
+    rng = np.random.default_rng(7 * k + n_seq)
+    rows, win_cap = 2600, 128
+    codes, scales, win, q, idx, pos = _attn_case(rng, n_seq, 1, rows, k, win_cap, 9000)
+    out = ops.csa_sparse_attn(t_(q), t_(pos), t_(codes), t_(scales), t_(idx), t_(win), n_seq, 1)
+    torch.cuda.synchronize()
+    check_attn(np_(out), _attn_ref(codes, scales, win, q, idx, pos, 1, win_cap))
+
+
 def test_sparse_attn_dense_case_and_empty_selection():
     """K >= visible: attention over every entry + window; and no entry selected."""
     rng = np.random.default_rng(11)
