@@ -75,6 +75,8 @@ struct LayerPlan {
   size_t off_scores = 0, off_bm = 0, off_blocks = 0, off_sel = 0, off_attn = 0, total = 0;
   bool pooled = false, fused_full = false;
   bool fused_scores = false;   // fused Full layer that gathers the scan's scores
+  bool split_full = false;     // fused Full layer whose rescoring runs in a second kernel
+  size_t off_split = 0;
 };
 
 LayerPlan plan_layer(int32_t mode, const csa_layer_args* a) {
@@ -96,6 +98,10 @@ LayerPlan plan_layer(int32_t mode, const csa_layer_args* a) {
     // batches with at most 2^22 scores take this path; many queries (prefill)
     // keep the rescoring, spread over the GPU.
     p.fused_scores = p.fused_full && p.Q < 512 && p.Q * p.ncols <= ((int64_t)1 << 22);
+    // The other decode batches rescore the chosen blocks in a second kernel
+    // with several blocks per query (one block per query spends ~17 us
+    // gathering a query's 512 KiB of keys).
+    p.split_full = p.fused_full && !p.fused_scores && p.Q < 512;
     if (!p.fused_full || p.fused_scores) {
       p.off_scores = off;
       off += round_up((size_t)(p.Q * p.ncols) * sizeof(float));
@@ -116,6 +122,10 @@ LayerPlan plan_layer(int32_t mode, const csa_layer_args* a) {
     }
     p.off_sel = off;
     off += round_up(sel);
+    if (p.split_full) {
+      p.off_split = off;
+      off += round_up(full_split_workspace_bytes(p.Q, a->top_k));
+    }
   }
   p.off_attn = off;
   off += round_up(attn_workspace_bytes(p.Q, a->top_k));
@@ -493,7 +503,8 @@ static csa_status run_index(const char* fn, int32_t mode, const csa_layer_args* 
     return hip_status(launch_full_select(bm, p.nblk, p.Q, a->build_pool ? a->n_pool_blocks : a->top_k,
                                          a->build_pool ? a->pool_blocks : nullptr, a->top_k, a->idx, a->q_idx,
                                          a->w_idx, a->q_pos, a->q_per_seq, a->k_fp8, a->k_rows, a->n_entries,
-                                         p.fused_scores ? scores : nullptr, st),
+                                         p.fused_scores ? scores : nullptr, p.split_full ? ws + p.off_split : nullptr,
+                                         st),
                       fn);
   int32_t* blocks = a->build_pool ? a->pool_blocks : reinterpret_cast<int32_t*>(ws + p.off_blocks);
   const int32_t nb = a->build_pool ? a->n_pool_blocks : a->top_k;

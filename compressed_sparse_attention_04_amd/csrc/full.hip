@@ -49,7 +49,103 @@ struct FullSelArgs {
   const uint8_t* k_fp8;     // [n_seq, k_rows, 128]
   int64_t k_rows, n_entries;
   const float* scores;      // [Q, n_entries] written by the scan, or null
+  // split selection (decode batches): the pool kernel writes the chosen
+  // blocks to top_out [Q, K] and zeroes ticket [Q]; full_rescore_kernel
+  // rescores them in several blocks per query, publishes the scores in
+  // sc_out [Q, 8 K] and the last block of a query selects the Top-K
+  int32_t* top_out;
+  int32_t* ticket;
+  float* sc_out;
 };
+
+// Rescore the entries of blocks list[0 .. n) of query q (-1 = no block)
+// with the scan's own arithmetic (the same fragments and fp32 sums, so the
+// same bits): out[8 i + e] = score of entry 8 list[i] + e, -inf when absent
+// or not visible.  Every wave of the NW-wave block calls it with its own LDS
+// staging slot; n <= 64 NW.
+//
+// Wave wv takes fragments f = wv + NW i, i < n_mine, each two of the blocks
+// (halves).  Lane L < 2 n_mine keeps half L's block: its number of visible
+// entries (cnt) and the block to read (row 0's block when it has none, so
+// every load reads existing rows); every half reads them back as
+// wave-uniform values.  Loads are unconditional and the groups of FS_GROUP
+// fragments alternate between two register sets, so no register with a load
+// in flight is copied.  32-bit: entries < 2^30.
+template <int NW>
+__device__ __forceinline__ void rescore_blocks(const FullSelArgs& a, int64_t q, const int32_t* list, int n,
+                                               float* out, uint4* stage, int wv, int lane) {
+  const int64_t seq = q / a.q_per_seq;
+  const int nv_pos = visible_count(a.q_pos[q]);
+  const int64_t nv = nv_pos < a.n_entries ? nv_pos : a.n_entries;
+  const int n_frag = (n + 1) / 2;   // two blocks per 16-entry fragment
+  if (nv == 0) {   // nothing visible: every slot is empty (and no row may be read)
+    for (int i = 64 * wv + lane; i < 16 * n_frag; i += 64 * NW) out[i] = -__builtin_huge_valf();
+    return;
+  }
+  const int rowa = lane & 15;
+  const Frag16 afrag = load_qfrag(a.q_fp8, q, rowa, rowa < IH, lane);
+  float w4[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) w4[r] = (lane < 32) ? a.w[q * IH + 4 * (lane >> 4) + r] : 0.f;
+  const uint8_t* kbase = a.k_fp8 + seq * a.k_rows * ID;
+  constexpr int FS_GROUP = 4;
+  const int n_mine = (n_frag - wv + NW - 1) / NW;   // <= 32
+  int my_cnt = 0, my_blkc = 0;
+  {
+    const int f = wv + NW * (lane >> 1), bi = 2 * f + (lane & 1);
+    const int32_t blk = ((lane >> 1) < n_mine && bi < n) ? list[bi] : -1;
+    const int rem = (int)nv - 8 * blk;
+    my_cnt = blk < 0 ? 0 : (rem <= 0 ? 0 : (rem >= 8 ? 8 : rem));
+    my_blkc = my_cnt > 0 ? blk : 0;
+  }
+  const int lrow_k = lane >> 3;
+  const uint32_t off_row[2] = {(uint32_t)(lrow_k * ID + 16 * stage_chunk(lane, 0)),
+                               (uint32_t)(lrow_k * ID + 16 * stage_chunk(lane, 1))};
+  const uint32_t off_zero[2] = {(uint32_t)(16 * stage_chunk(lane, 0)), (uint32_t)(16 * stage_chunk(lane, 1))};
+  auto load_group = [&](int grp, uint4 (&v)[FS_GROUP][2]) {
+#pragma unroll
+    for (int u = 0; u < FS_GROUP; ++u) {
+      const int i = grp * FS_GROUP + u;   // may pass n_mine: reads row 0, never used
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int hl = (2 * i + h) & 63;
+        const int cnt = __builtin_amdgcn_readlane(my_cnt, hl);
+        const uint8_t* base = kbase + (int64_t)__builtin_amdgcn_readlane(my_blkc, hl) * (8 * ID);
+        v[u][h] = load16<false>(base + (lrow_k < cnt ? off_row[h] : off_zero[h]));
+      }
+    }
+  };
+  auto compute_group = [&](int grp, const uint4 (&v)[FS_GROUP][2]) {
+#pragma unroll
+    for (int u = 0; u < FS_GROUP; ++u) {
+      const int i = grp * FS_GROUP + u;
+      if (i >= n_mine) break;   // wave-uniform
+      const int f = wv + NW * i;
+      __builtin_amdgcn_wave_barrier();
+      stage[lane] = v[u][0];
+      stage[64 + lane] = v[u][1];
+      __builtin_amdgcn_wave_barrier();
+      const f32x4 acc = frag_mma(afrag, to_frag(read_staged(stage, lane)));
+      const float sco = head_sum(acc, w4);
+      // lane m < 16 holds column m: entry m % 8 of half m / 8, valid when
+      // m % 8 is below that half's visible count (<= 8): bit m of a
+      // wave-uniform mask built on the scalar unit
+      const uint32_t c0 = __builtin_amdgcn_readlane(my_cnt, (2 * i) & 63);
+      const uint32_t c1 = __builtin_amdgcn_readlane(my_cnt, (2 * i + 1) & 63);
+      const uint32_t m16 = ((1u << c0) - 1u) | (((1u << c1) - 1u) << 8);
+      if (lane < 16) out[16 * f + lane] = __builtin_amdgcn_inverse_ballot_w64((uint64_t)m16) ? sco : -__builtin_huge_valf();
+    }
+  };
+  const int n_groups = (n_mine + FS_GROUP - 1) / FS_GROUP;
+  uint4 ra[FS_GROUP][2], rb[FS_GROUP][2];
+  load_group(0, ra);
+  for (int grp = 0; grp < n_groups; grp += 2) {
+    if (grp + 1 < n_groups) load_group(grp + 1, rb);
+    compute_group(grp, ra);
+    if (grp + 2 < n_groups) load_group(grp + 2, ra);
+    if (grp + 1 < n_groups) compute_group(grp + 1, rb);
+  }
+}
 
 // NT threads; block maxima per thread; rescored entries per thread; top_k
 // bound (8 KMAX rescored scores in LDS).  The pool (phase A) and the key
@@ -115,6 +211,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void fu
     }
   }
   __syncthreads();
+  if (a.top_out) {   // split selection: the chosen blocks go to full_rescore_kernel
+    for (int j = tid; j < K; j += NT) a.top_out[q * K + j] = top[j];
+    if (tid == 0) a.ticket[q] = 0;
+    return;
+  }
 
   // ---- B. the scores of the top_k blocks' entries ----------------------------
   if (a.scores) {
@@ -147,86 +248,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void fu
       if (slot < 8 * K) sc[slot] = ok[u] ? v[u] : -__builtin_huge_valf();
     }
   } else {
-    // rescore the entries of the top_k blocks
-    const int64_t seq = q / a.q_per_seq;
-    const int nv_pos = visible_count(a.q_pos[q]);
-    const int64_t nv = nv_pos < a.n_entries ? nv_pos : a.n_entries;
-    const int rowa = lane & 15;
-    const Frag16 afrag = load_qfrag(a.q_fp8, q, rowa, rowa < IH, lane);
-    float w4[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) w4[r] = (lane < 32) ? a.w[q * IH + 4 * (lane >> 4) + r] : 0.f;
-    const uint8_t* kbase = a.k_fp8 + seq * a.k_rows * ID;
-    uint4* stage = ps.stage_all[wv];
-    const int n_frag = (K + 1) / 2;   // two blocks per 16-entry fragment; wave wv takes f = wv + 16 i
-    if (nv == 0) {   // nothing visible: every rescored slot is empty (and no row may be read)
-      for (int i = tid; i < 16 * n_frag; i += NT) sc[i] = -__builtin_huge_valf();
-    } else {
-      // Wave wv takes fragments f = wv + 16 i, i < n_mine, each two of the
-      // chosen blocks (halves).  Lane L < 2 n_mine keeps half L's block: its
-      // number of visible entries (cnt) and the block to read (row 0's block
-      // when it has none, so every load reads existing rows); every half
-      // reads them back as wave-uniform values.  Loads are unconditional and
-      // the groups of FS_GROUP fragments alternate between two register sets,
-      // so no register with a load in flight is copied.  32-bit: entries < 2^30.
-      constexpr int FS_GROUP = 4;
-      const int n_mine = (n_frag - wv + FS_WAVES - 1) / FS_WAVES;   // <= 32 (K <= 1,024)
-      int my_cnt = 0, my_blkc = 0;
-      {
-        const int f = wv + FS_WAVES * (lane >> 1), bi = 2 * f + (lane & 1);
-        const int32_t blk = ((lane >> 1) < n_mine && bi < K) ? top[bi] : -1;
-        const int rem = (int)nv - 8 * blk;
-        my_cnt = blk < 0 ? 0 : (rem <= 0 ? 0 : (rem >= 8 ? 8 : rem));
-        my_blkc = my_cnt > 0 ? blk : 0;
-      }
-      const int lrow_k = lane >> 3;
-      const uint32_t off_row[2] = {(uint32_t)(lrow_k * ID + 16 * stage_chunk(lane, 0)),
-                                   (uint32_t)(lrow_k * ID + 16 * stage_chunk(lane, 1))};
-      const uint32_t off_zero[2] = {(uint32_t)(16 * stage_chunk(lane, 0)), (uint32_t)(16 * stage_chunk(lane, 1))};
-      auto load_group = [&](int grp, uint4 (&v)[FS_GROUP][2]) {
-#pragma unroll
-        for (int u = 0; u < FS_GROUP; ++u) {
-          const int i = grp * FS_GROUP + u;   // may pass n_mine: reads row 0, never used
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int hl = (2 * i + h) & 63;
-            const int cnt = __builtin_amdgcn_readlane(my_cnt, hl);
-            const uint8_t* base = kbase + (int64_t)__builtin_amdgcn_readlane(my_blkc, hl) * (8 * ID);
-            v[u][h] = load16<false>(base + (lrow_k < cnt ? off_row[h] : off_zero[h]));
-          }
-        }
-      };
-      auto compute_group = [&](int grp, const uint4 (&v)[FS_GROUP][2]) {
-#pragma unroll
-        for (int u = 0; u < FS_GROUP; ++u) {
-          const int i = grp * FS_GROUP + u;
-          if (i >= n_mine) break;   // wave-uniform
-          const int f = wv + FS_WAVES * i;
-          __builtin_amdgcn_wave_barrier();
-          stage[lane] = v[u][0];
-          stage[64 + lane] = v[u][1];
-          __builtin_amdgcn_wave_barrier();
-          const f32x4 acc = frag_mma(afrag, to_frag(read_staged(stage, lane)));
-          const float sco = head_sum(acc, w4);
-          // lane n < 16 holds column n: entry n % 8 of half n / 8, valid when
-          // n % 8 is below that half's visible count (<= 8): bit n of a
-          // wave-uniform mask built on the scalar unit
-          const uint32_t c0 = __builtin_amdgcn_readlane(my_cnt, (2 * i) & 63);
-          const uint32_t c1 = __builtin_amdgcn_readlane(my_cnt, (2 * i + 1) & 63);
-          const uint32_t m16 = ((1u << c0) - 1u) | (((1u << c1) - 1u) << 8);
-          if (lane < 16) sc[16 * f + lane] = __builtin_amdgcn_inverse_ballot_w64((uint64_t)m16) ? sco : -__builtin_huge_valf();
-        }
-      };
-      const int n_groups = (n_mine + FS_GROUP - 1) / FS_GROUP;
-      uint4 ra[FS_GROUP][2], rb[FS_GROUP][2];
-      load_group(0, ra);
-      for (int grp = 0; grp < n_groups; grp += 2) {
-        if (grp + 1 < n_groups) load_group(grp + 1, rb);
-        compute_group(grp, ra);
-        if (grp + 2 < n_groups) load_group(grp + 2, ra);
-        if (grp + 1 < n_groups) compute_group(grp + 1, rb);
-      }
-    }
+    rescore_blocks<FS_WAVES>(a, q, top, K, sc, ps.stage_all[wv], wv, lane);
   }
   __syncthreads();
 
@@ -246,6 +268,62 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void fu
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split Full-layer selection, second kernel: block (r, q) of 16 waves
+// rescores the chosen blocks r P .. r P + P - 1 of query q (P = ceil(K / R),
+// R = gridDim.x), so one query's 512 KiB of key gathers spread over R
+// compute units instead of one.  The scores go out as device-coherent
+// stores (written through to memory, sc1), each thread waits for its own
+// stores, and thread 0 then takes the query's ticket (an agent-scope atomic
+// add, which the pool kernel zeroed).  The block that draws the last ticket
+// reads every score back with device-coherent loads and selects the Top-K,
+// ties to the lower entry; no fence that writes back a whole L2 is needed.
+constexpr int FR_THREADS = 1024;
+constexpr int FR_WAVES = FR_THREADS / 64;
+constexpr int FR_MAX_BLOCKS = 64 * FR_WAVES;   // blocks one rescoring block takes (rescore_blocks' bound)
+
+template <int PER2>
+__global__ __launch_bounds__(FR_THREADS) void full_rescore_kernel(FullSelArgs a) {
+  __shared__ SelShared s;
+  __shared__ int32_t top[FS_KMAX];
+  __shared__ float sc[8 * FR_MAX_BLOCKS];
+  __shared__ uint4 stage_all[FR_WAVES][128];
+  __shared__ int32_t last;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t q = blockIdx.y;
+  const int K = a.K, R = gridDim.x, r = blockIdx.x;
+  const int per = (K + R - 1) / R;
+  const int b0 = r * per, nb = (b0 + per < K ? b0 + per : K) - b0;   // this block's slots of top
+  for (int j = tid; j < K; j += FR_THREADS) top[j] = a.top_out[q * K + j];
+  __syncthreads();
+  if (nb > 0) rescore_blocks<FR_WAVES>(a, q, top + b0, nb, sc, stage_all[wv], wv, lane);
+  __syncthreads();
+  float* srow = a.sc_out + q * (int64_t)(8 * K);
+  for (int i = tid; i < 8 * nb; i += FR_THREADS)
+    __hip_atomic_store(srow + 8 * b0 + i, sc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's stores have reached memory
+  __syncthreads();
+  if (tid == 0) last = __hip_atomic_fetch_add(a.ticket + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (last != R - 1) return;   // block-uniform: another block selects
+
+  // ---- the last block: Top-K of the query's 8 K scores ----------------------------
+  const int n = 8 * K;
+  const int pw = 64 * PER2 * wv + lane;
+  uint32_t key[PER2];
+#pragma unroll
+  for (int u = 0; u < PER2; ++u) {
+    const int p = pw + 64 * u;
+    key[u] = select_key(__hip_atomic_load(srow + (p < n ? p : 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  }
+#pragma unroll
+  for (int u = 0; u < PER2; ++u) key[u] = pw + 64 * u < n ? key[u] : 0u;
+  const uint32_t n_sel = block_select<FR_THREADS, PER2>(s, key, (uint32_t)K, [&](int p, uint32_t, uint32_t slot) {
+    a.idx[q * K + slot] = 8 * top[p >> 3] + (p & 7);
+  });
+  for (int j = (int)n_sel + tid; j < K; j += FR_THREADS) a.idx[q * K + j] = -1;
+}
+
 bool full_select_supported(int64_t nblk, int32_t nb, int32_t k) {
   return nblk <= SEL_CHUNK_MAX && nb <= SEL_POOL_MAX && k <= FS_KMAX && nb >= k;
 }
@@ -253,9 +331,23 @@ bool full_select_supported(int64_t nblk, int32_t nb, int32_t k) {
 hipError_t launch_full_select(const float* block_max, int64_t nblk, int64_t Q, int32_t nb, int32_t* pool,
                               int32_t k, int32_t* idx, const uint8_t* q_fp8, const float* w, const int32_t* q_pos,
                               int64_t q_per_seq, const uint8_t* k_fp8, int64_t k_rows, int64_t n_entries,
-                              const float* scores, hipStream_t st) {
+                              const float* scores, void* split_ws, hipStream_t st) {
   if (Q == 0) return hipSuccess;
-  FullSelArgs a{block_max, nblk, nb, pool, k, idx, q_fp8, w, q_pos, q_per_seq, k_fp8, k_rows, n_entries, scores};
+  FullSelArgs a{block_max, nblk, nb, pool, k, idx, q_fp8, w, q_pos, q_per_seq, k_fp8, k_rows, n_entries, scores,
+                nullptr, nullptr, nullptr};
+  int R = 0;
+  if (split_ws) {
+    // blocks per query: about one per compute unit in all, each rescoring
+    // at most FR_MAX_BLOCKS chosen blocks
+    R = (int)((256 + Q - 1) / Q);
+    R = R > 16 ? 16 : R;
+    const int r_min = (k + FR_MAX_BLOCKS - 1) / FR_MAX_BLOCKS;
+    R = R < r_min ? r_min : R;
+    char* p = reinterpret_cast<char*>(split_ws);
+    a.top_out = reinterpret_cast<int32_t*>(p);
+    a.ticket = reinterpret_cast<int32_t*>(p + full_split_top_bytes(Q, k));
+    a.sc_out = reinterpret_cast<float*>(p + full_split_top_bytes(Q, k) + full_split_ticket_bytes(Q));
+  }
   const dim3 grid(1, (unsigned)Q);
   // many queries: 512-thread blocks, two per compute unit (top_k <= 512,
   // nblk <= 16,384); a few queries: 1,024 threads, the shortest block
@@ -269,7 +361,20 @@ hipError_t launch_full_select(const float* block_max, int64_t nblk, int64_t Q, i
   else if (!big1) hipLaunchKernelGGL((full_select_kernel<FS_THREADS, 16, 8, FS_KMAX>), grid, blk, 0, st, a);
   else if (!big2) hipLaunchKernelGGL((full_select_kernel<FS_THREADS, 32, 4, FS_KMAX>), grid, blk, 0, st, a);
   else hipLaunchKernelGGL((full_select_kernel<FS_THREADS, 32, 8, FS_KMAX>), grid, blk, 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !split_ws) return e;
+  const dim3 g2((unsigned)R, (unsigned)Q);
+  if (8 * (int64_t)k <= FR_THREADS * 4)
+    hipLaunchKernelGGL(full_rescore_kernel<4>, g2, dim3(FR_THREADS), 0, st, a);
+  else
+    hipLaunchKernelGGL(full_rescore_kernel<8>, g2, dim3(FR_THREADS), 0, st, a);
   return hipGetLastError();
+}
+
+size_t full_split_top_bytes(int64_t Q, int32_t k) { return ((size_t)Q * k * 4 + 255) / 256 * 256; }
+size_t full_split_ticket_bytes(int64_t Q) { return ((size_t)Q * 4 + 255) / 256 * 256; }
+size_t full_split_workspace_bytes(int64_t Q, int32_t k) {
+  return full_split_top_bytes(Q, k) + full_split_ticket_bytes(Q) + (size_t)Q * 8 * k * 4;
 }
 
 }  // namespace csa

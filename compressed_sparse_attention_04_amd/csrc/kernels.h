@@ -60,10 +60,15 @@ hipError_t launch_pool_topk(const float* block_max, int64_t nblk, const float* s
 bool full_select_supported(int64_t nblk, int32_t nb, int32_t k);
 // scores: the scan's scores [Q, n_entries] (decode batches: gathered for
 // the chosen blocks), or null (their entries are rescored from k_fp8).
+// split_ws (full_split_workspace_bytes, 256-byte aligned), or null: the
+// rescoring and the Top-K run in a second kernel of several blocks per query.
 hipError_t launch_full_select(const float* block_max, int64_t nblk, int64_t Q, int32_t nb, int32_t* pool,
                               int32_t k, int32_t* idx, const uint8_t* q_fp8, const float* w, const int32_t* q_pos,
                               int64_t q_per_seq, const uint8_t* k_fp8, int64_t k_rows, int64_t n_entries,
-                              const float* scores, hipStream_t st);
+                              const float* scores, void* split_ws, hipStream_t st);
+size_t full_split_top_bytes(int64_t Q, int32_t k);
+size_t full_split_ticket_bytes(int64_t Q);
+size_t full_split_workspace_bytes(int64_t Q, int32_t k);
 
 // attn.hip
 size_t attn_workspace_bytes(int64_t Q, int32_t k);

@@ -76,6 +76,53 @@ def test_full_layer_sizes(n_ent, top_k, n_pool, build_pool):
     _full_layer(n_ent, top_k, n_pool, build_pool)
 
 
+# A decode-sized batch with more than 2^22 scores (2 sequences x 64 queries x
+# 45,000 entries): the Full layer's selection runs split, the chosen blocks
+# rescored by several blocks per query and the Top-K taken by the block that
+# draws the query's last ticket.  Every query: pool bit-exact, Top-K set,
+# attention on the GPU's own selection.
+@pytest.mark.parametrize("keys", ["normal", "few"])
+def test_full_layer_split_selection(keys):
+    n_seq, qps, n_ent, top_k, n_pool = 2, 64, 45000, 512, 2048
+    Q, win_cap = n_seq * qps, 128 + qps
+    rng = np.random.default_rng(4242 + len(keys))
+    codes = rng.integers(0, 256, (n_seq, n_ent, 256)).astype(np.uint8)
+    scales = rng.integers(0x28, 0x31, (n_seq, n_ent, 32)).astype(np.uint8)
+    if keys == "normal":
+        k8 = formats.e4m3_encode(rng.standard_normal((n_seq, n_ent, 128)))
+    else:   # a few distinct rows: block maxima tie everywhere
+        rows = formats.e4m3_encode(rng.standard_normal((n_seq, 4, 128)))
+        k8 = np.ascontiguousarray(rows[np.arange(n_seq)[:, None], rng.integers(0, 4, (n_seq, n_ent))])
+    q8 = formats.e4m3_encode(rng.standard_normal((Q, 8, 128)))
+    w = rng.random((Q, 8)).astype(np.float32)
+    q_attn = rng.standard_normal((Q, 16, 512)).astype(np.float32)
+    win = formats.e4m3_encode(rng.standard_normal((n_seq, win_cap, 512)))
+    pos = np.array([4 * n_ent - qps + (i % qps) for i in range(Q)], np.int32)
+    idx = torch.empty((Q, top_k), dtype=torch.int32, device=DEV)
+    out = torch.empty((Q, 16, 512), dtype=torch.float32, device=DEV)
+    pool = torch.empty((Q, n_pool), dtype=torch.int32, device=DEV)
+    call = ops.LayerCall(ops.MODE_FULL, codes=t_(codes), scales=t_(scales), k_fp8=t_(k8), win=t_(win),
+                         q_pos=t_(pos), q_attn=t_(q_attn), idx=idx, out=out, n_seq=n_seq, q_per_seq=qps,
+                         n_entries=n_ent, q_idx=t_(q8), w_idx=t_(w), pool_blocks=pool, build_pool=True,
+                         top_k=top_k, n_pool_blocks=n_pool)
+    call()
+    torch.cuda.synchronize()
+    gi, go, gp = np_(idx), np_(out), np_(pool)
+    kv = [formats.e4m3_decode(k8[s]) for s in range(n_seq)]
+    for qi in range(Q):
+        s = qi // qps
+        wp = oracle.window_positions(pos[qi])
+        ref = oracle.layer_full(codes[s], scales[s], k8[s], q8[qi], w[qi], q_attn[qi], pos[qi],
+                                win[s, wp % win_cap], SM, build_pool=True, k=top_k, n_blocks=n_pool,
+                                n_entries=n_ent, k_values=kv[s], attend=False)
+        assert np.array_equal(gp[qi], ref.pool), qi
+        if check_topk_set(gi[qi], ref.scores, ref.idx, top_k) == 0:
+            assert np.array_equal(np.sort(gi[qi]), np.sort(ref.idx)), qi
+        if qi % 8 == 0:
+            check_attn(go[qi], oracle.sparse_attention(q_attn[qi], codes[s], scales[s], gi[qi],
+                                                       win[s, wp % win_cap], SM))
+
+
 @pytest.mark.parametrize("n_ent,top_k,n_pool,build_pool,keys", [(3000, 1024, 1024, True, "const"),
                                                                 (45000, 512, 2048, True, "few"),
                                                                 (45000, 512, 2048, True, "const"),
