@@ -47,12 +47,25 @@ __global__ __launch_bounds__(NT) void select_kernel(
     int64_t nblk_map, int32_t K, int32_t* __restrict__ idx, uint32_t* __restrict__ out_keys,
     int32_t* __restrict__ out_cols) {
   __shared__ SelShared s;
+  // The chunk's slice of col_blocks (MODE 0 with col_blocks, MODE 2), staged
+  // while the keys load, so that writing an id reads LDS instead of waiting
+  // on a global load after the selection.
+  constexpr int MAPN = MODE == 1 ? 1 : NT * PER / 8;
+  __shared__ int32_t bmap[MAPN];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t q = blockIdx.y;
   const int64_t total = MODE == 0 ? ncols : n_in;
   const int64_t start = (int64_t)blockIdx.x * (NT * PER);
   const int n = (int)((total - start) < NT * PER ? (total - start) : NT * PER);
   const int pw = 64 * PER * wv + lane;       // position of key[u] is pw + 64 u
+  const bool staged = MODE != 1 && col_blocks != nullptr;
+  if (staged) {
+    // blocks start / 8 .. of the row (start is a multiple of 8); entries of
+    // the chunk past the row's blocks are never selected
+    const int64_t b0 = start >> 3;
+    const int nb = (int)((nblk_map - b0) < MAPN ? (nblk_map - b0) : MAPN);
+    for (int i = tid; i < nb; i += NT) bmap[i] = col_blocks[q * nblk_map + b0 + i];
+  }
 
   uint32_t key[PER];   // 0 = not selectable
   if (MODE == 0) {
@@ -69,10 +82,11 @@ __global__ __launch_bounds__(NT) void select_kernel(
     int64_t col;
     if (MODE == 0) col = pos;
     else if (MODE == 1) col = cand_cols[q * n_in + pos];
-    else col = 8 * (int64_t)col_blocks[q * nblk_map + (pos >> 3)] + (pos & 7);
+    else col = 8 * (int64_t)bmap[p >> 3] + (pos & 7);
     if (FINAL) {
       int64_t id = col;
-      if (MODE != 2 && col_blocks) id = 8 * (int64_t)col_blocks[q * nblk_map + (col >> 3)] + (col & 7);
+      if (MODE == 0 && col_blocks) id = 8 * (int64_t)bmap[p >> 3] + (col & 7);
+      else if (MODE == 1 && col_blocks) id = 8 * (int64_t)col_blocks[q * nblk_map + (col >> 3)] + (col & 7);
       idx[q * K + slot] = (int32_t)id;
     } else {
       const int64_t o = (q * gridDim.x + blockIdx.x) * (int64_t)K + slot;

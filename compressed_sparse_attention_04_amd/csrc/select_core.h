@@ -142,23 +142,48 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Exclusive block scan of v; *total = the block sum.  Two barriers.
+// Cross-wave combination of one word per wave (arr[0 .. W-1] in LDS, W <=
+// 16): lane i < W of every wave reads arr[i] and the wave's first 16-lane row
+// combines the words on the DPP network, so a thread reads one word instead
+// of W and the sums take four steps instead of W.
+// Sum over all waves; *before (if given) = the sum over waves below this one.
+template <int W>
+__device__ __forceinline__ uint32_t waves_sum(const uint32_t* arr, uint32_t* before) {
+  static_assert(W >= 1 && W <= 16, "one DPP row");
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint32_t x = lane < W ? arr[lane] : 0u;
+  x += dpp<DPP_ROW_SHR1>(0u, x);
+  x += dpp<DPP_ROW_SHR2>(0u, x);
+  x += dpp<DPP_ROW_SHR4>(0u, x);
+  x += dpp<DPP_ROW_SHR8>(0u, x);   // lane i < 16: arr[0] + ... + arr[i]
+  if (before) *before = wv == 0 ? 0u : (uint32_t)__builtin_amdgcn_readlane((int)x, wv - 1);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, W - 1);
+}
+// Max (OP 0) or min (OP 1) over all waves.
+template <int W, int OP>
+__device__ __forceinline__ uint32_t waves_reduce(const uint32_t* arr) {
+  static_assert(W >= 1 && W <= 16, "one DPP row");
+  auto f = [](uint32_t a, uint32_t b) { return OP == 0 ? (a > b ? a : b) : (a < b ? a : b); };
+  const uint32_t id = OP == 1 ? 0xFFFFFFFFu : 0u;
+  const int lane = threadIdx.x & 63;
+  uint32_t x = lane < W ? arr[lane] : id;
+  x = f(x, dpp<DPP_XOR1>(id, x));
+  x = f(x, dpp<DPP_XOR2>(id, x));
+  x = f(x, dpp<DPP_ROW_HALF_MIRROR>(id, x));
+  x = f(x, dpp<DPP_ROW_MIRROR>(id, x));   // every lane of row 0: the result
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+}
+
+// Exclusive block scan of v; *total = the block sum.  One barrier: the
+// caller passes another barrier before s.wred[0] is written again.
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(SelShared& s, uint32_t v, uint32_t* total) {
-  constexpr int W = NT / 64;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) s.wred[0][wv] = incl;
   __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < W; ++w) {
-    const uint32_t x = s.wred[0][w];
-    before += w < wv ? x : 0u;
-    all += x;
-  }
-  __syncthreads();
-  *total = all;
+  uint32_t before;
+  *total = waves_sum<NT / 64>(s.wred[0], &before);
   return before + incl - v;
 }
 
@@ -171,7 +196,8 @@ __device__ __forceinline__ int value_bin(uint32_t key, float vmax, float inv) {
 
 // Thread t owns bins BPT t .. BPT t + BPT - 1 of h (already loaded): the bin
 // where the running count from bin 0 reaches `need`, and how many of that
-// bin's keys are needed.  Exactly one thread returns true.
+// bin's keys are needed.  Exactly one thread returns true.  Every caller
+// passes a barrier before s.wred is written again (see block_excl_scan).
 template <int NT, int BPT>
 __device__ __forceinline__ bool find_bin(SelShared& s, const uint32_t (&h)[BPT], uint32_t need, int* bin,
                                          uint32_t* left) {
@@ -221,14 +247,9 @@ __device__ __forceinline__ void block_threshold(SelShared& s, const uint32_t (&k
   }
   if (tid == 0) s.n_cand = 0;
   __syncthreads();
-  uint32_t nval = 0;
-  kmax = 0; kmin = 0xFFFFFFFFu;
-#pragma unroll
-  for (int w = 0; w < W; ++w) {
-    kmax = s.wred[0][w] > kmax ? s.wred[0][w] : kmax;
-    kmin = s.wred[1][w] < kmin ? s.wred[1][w] : kmin;
-    nval += s.wred[2][w];
-  }
+  kmax = waves_reduce<W, 0>(s.wred[0]);
+  kmin = waves_reduce<W, 1>(s.wred[1]);
+  const uint32_t nval = waves_sum<W>(s.wred[2], nullptr);
   if (nval <= K) {
     *T_out = 0;
     *take_out = 0;
@@ -337,15 +358,9 @@ __device__ __forceinline__ uint32_t block_compact(SelShared& s, const uint32_t (
     s.wred[1][wv] = eq_w;
   }
   __syncthreads();
-  uint32_t gt_before = 0, eq_before = 0, gt_tot = 0, eq_tot = 0;
-#pragma unroll
-  for (int v = 0; v < W; ++v) {
-    const uint32_t g = s.wred[0][v], e = s.wred[1][v];
-    gt_before += v < wv ? g : 0u;
-    eq_before += v < wv ? e : 0u;
-    gt_tot += g;
-    eq_tot += e;
-  }
+  uint32_t gt_before, eq_before;
+  const uint32_t gt_tot = waves_sum<W>(s.wred[0], &gt_before);
+  const uint32_t eq_tot = waves_sum<W>(s.wred[1], &eq_before);
   uint32_t slot_base = gt_before + (eq_before < take_eq ? eq_before : take_eq);
   uint32_t eq_seen = eq_before;
 #pragma unroll
@@ -415,14 +430,9 @@ __device__ __forceinline__ uint32_t block_select(SelShared& s, const uint32_t (&
     }
     if (tid == 0) s.tlo = 0xFFFFFFFFu;
     __syncthreads();
-    uint32_t kmax = 0, kmin = 0xFFFFFFFFu, nval = 0, sval = 0;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      kmax = s.wred[0][w] > kmax ? s.wred[0][w] : kmax;
-      kmin = s.wred[1][w] < kmin ? s.wred[1][w] : kmin;
-      nval += s.wred[2][w] & 0xFFFFu;
-      sval += s.wred[2][w] >> 16;
-    }
+    const uint32_t kmax = waves_reduce<W, 0>(s.wred[0]), kmin = waves_reduce<W, 1>(s.wred[1]);
+    const uint32_t packed = waves_sum<W>(s.wred[2], nullptr);   // sum of the 16-bit fields: no carry
+    const uint32_t nval = packed & 0xFFFFu, sval = packed >> 16;
     const uint32_t m = (uint32_t)(1.5f * (float)K * (float)sval / (float)(nval > 0 ? nval : 1)) + 8u;
     if (nval > K && m < sval) {
       const float vmax = key_value(kmax), vmin = key_value(kmin);
@@ -447,12 +457,8 @@ __device__ __forceinline__ uint32_t block_select(SelShared& s, const uint32_t (&
       for (int u = 0; u < PER; ++u) c_w += (uint32_t)__popcll(__ballot(key[u] >= tlo));
       if (lane == 0) s.wred[0][wv] = c_w;
       __syncthreads();
-      uint32_t C = 0, off = 0;
-#pragma unroll
-      for (int w = 0; w < W; ++w) {
-        C += s.wred[0][w];
-        off += w < wv ? s.wred[0][w] : 0u;
-      }
+      uint32_t off;
+      const uint32_t C = waves_sum<W>(s.wred[0], &off);
       if (C >= K && C <= SEL_CAND_MAX) {
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
