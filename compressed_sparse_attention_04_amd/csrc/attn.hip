@@ -503,19 +503,21 @@ __device__ __forceinline__ RawKey load_slot_p(const QueryView& v, const AttnArgs
 // once: a cold gather is bound by the cache lines a compute unit can have
 // in flight, so spreading a query over more compute units shortens it.
 //
-// Key order.  QK runs on two 16-key MFMA tiles per pair; tile 0 row 4 q + r
-// holds pair key 8 q + r and tile 1 row 4 q + r pair key 8 q + 4 + r (q, r <
-// 4).  The score fragment of lane (j, g) -- rows 4 g .. 4 g + 3 of both tiles,
-// column j -- is then head j over pair keys 8 g .. 8 g + 7, which is exactly
-// the A operand that lane feeds to the 16x16x32 P V product: P never moves
-// between lanes, and P V contracts 32 keys per instruction (the 16-key fp16
-// product runs at half the rate on this GPU).
+// Key order.  QK runs on two 16-key MFMA tiles per pair; row 4 q + r of tile
+// h holds pair key q + 4 (2 r + h) (q, r < 4).  The score fragment of lane
+// (j, g) -- rows 4 g .. 4 g + 3 of both tiles, column j -- is then head j
+// over the eight pair keys g + 4 m, which is exactly the A operand that lane
+// feeds to the 16x16x32 P V product: P never moves between lanes, and P V
+// contracts 32 keys per instruction (the 16-key fp16 product runs at half
+// the rate on this GPU).
 // Per block:
-//   1. slot ids, Q, and per pair the QK bytes (lane (j, g): the keys of row
-//      j of both tiles, its 32 channels) and the P V bytes (lane (c, g): pair
-//      keys 8 g .. 8 g + 7, channels 128 w + 8 c .. + 7) -- the same rows
-//      loaded in the two layouts the products need, instead of an LDS
-//      transpose per tile;
+//   1. the pairs' slot ids (one word per lane, each id then read from the
+//      lane that loaded it), Q, and per pair the QK bytes (lane (j, g): the
+//      key of row j of each tile, its 32 channels -- four lanes read 64
+//      contiguous bytes of a row).  Each wave passes its bytes through its
+//      own LDS rows into the P V layout (lane (c, g): the keys g + 4 m,
+//      channels 128 w + 8 c .. + 7), so a key is read from memory once and
+//      a wave has few enough loads to keep them all in flight;
 //   2. partial S over the wave's channels for every pair -> LDS; barrier;
 //   3. wave p % 4 sums the four partials of pair p (in wave order) and
 //      publishes the pair's head maxima; barrier;
@@ -537,8 +539,21 @@ struct PairLds {
   float psum[NP][HEADS];          // head sums of each pair's P (hi + lo)
 };
 
-// Row i < 16 of QK tile h of a pair is pair key 8 (i >> 2) + 4 h + (i & 3).
-__device__ __forceinline__ int pair_row_key(int h, int i) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+// Row i < 16 of QK tile h of a pair is pair key (i >> 2) + 4 (2 (i & 3) + h).
+__device__ __forceinline__ int pair_row_key(int h, int i) { return (i >> 2) + 4 * (2 * (i & 3) + h); }
+// Element kk < 8 of lane group g's P V operands (tile kk >> 2, row
+// 4 g + (kk & 3)): pair key g + 4 (2 (kk & 3) + (kk >> 2)).
+__device__ __forceinline__ int pair_v_key(int g, int kk) { return pair_row_key(kk >> 2, 4 * g + (kk & 3)); }
+
+// One wave's LDS rows for turning the QK layout into the P V layout: per
+// entry pair the wave's 64 code bytes and 8 scale bytes of each key, and
+// the wave's 128 bytes of each window token.
+template <int E>
+struct PairStage {
+  uint8_t code[E][AT_PAIR][64];
+  uint8_t scale[E][AT_PAIR][8];
+  uint8_t win[AT_PAIR][128];
+};
 
 // Key slot of key 0 of pair p of a block: entries are slots 0 .. k-1 (entry
 // pair e holds slots 32 e ..), window token i is slot k + i.
@@ -549,43 +564,49 @@ __device__ __forceinline__ int pair_slot0(const AttnArgs& a, int split, int p) {
 
 // P V bytes of one key (lane column c, wave w): channels 128 w + 8 c .. + 7 --
 // four E2M1 code bytes and the E4M3 scale of their 16-channel group, or
-// eight E4M3 window bytes.  Absent keys read past the views (zeros).
+// eight E4M3 window bytes.  An absent key holds zeros (its QK loads read
+// past the views).
 struct RawV {
   uint32_t c;    // codes, or window bytes 0-3
   uint32_t w1;   // window bytes 4-7
   uint32_t sc;   // scale byte (entries)
 };
 
-template <int PATH>
-__device__ __forceinline__ RawV load_v(const QueryView& v, const AttnArgs& a, int slot, int c, int w, int32_t id,
-                                       bool* valid) {
+// stage_*: the QK bytes lane (j, g) loaded for pair key K to the wave's LDS
+// rows; unstage_*: the P V bytes of pair key K for lane (c, g) -- four code
+// bytes and the scale byte of channels 128 w + 8 c .. + 7, or eight window
+// bytes.  LDS operations of one wave complete in order, so no barrier is
+// needed between the two.
+template <int E>
+__device__ __forceinline__ void stage_entry(PairStage<E>& st, int p, int K, int g, const RawKey& r) {
+  *reinterpret_cast<uint4*>(&st.code[p][K][16 * g]) = r.a;
+  *reinterpret_cast<uint16_t*>(&st.scale[p][K][2 * g]) = (uint16_t)r.sc;
+}
+template <int E>
+__device__ __forceinline__ void stage_window(PairStage<E>& st, int K, int g, const RawKey& r) {
+  *reinterpret_cast<uint4*>(&st.win[K][32 * g]) = r.a;
+  *reinterpret_cast<uint4*>(&st.win[K][32 * g + 16]) = r.b;
+}
+template <int E>
+__device__ __forceinline__ RawV unstage_entry(const PairStage<E>& st, int p, int K, int c) {
   RawV r;
-  r.c = 0u;
+  r.c = *reinterpret_cast<const uint32_t*>(&st.code[p][K][4 * c]);
   r.w1 = 0u;
+  r.sc = st.scale[p][K][c >> 1];
+  return r;
+}
+template <int E>
+__device__ __forceinline__ RawV unstage_window(const PairStage<E>& st, int K, int c) {
+  const uint2 x = *reinterpret_cast<const uint2*>(&st.win[K][8 * c]);
+  RawV r;
+  r.c = x.x;
+  r.w1 = x.y;
   r.sc = 0u;
-  if constexpr (PATH == PATH_ENTRY) {
-    const bool ent = slot < a.k && id >= 0 && id < a.kv_rows;
-    const uint32_t oc = ent ? (uint32_t)id * CODE_BYTES + 64u * w + 4u * c : AT_OOB;
-    const uint32_t os = ent ? (uint32_t)id * SCALE_BYTES + 8u * w + (uint32_t)(c >> 1) : AT_OOB;
-    r.c = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(v.codes, oc, 0, 0);
-    r.sc = (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(v.scales, os, 0, 0);
-    *valid = ent;
-  } else {
-    const int wi = slot - a.k;
-    const bool win = wi >= 0 && wi < NWIN && v.p - (NWIN - 1) + wi >= 0;
-    int row = v.wbase + wi;
-    row = row >= v.win_cap ? row - v.win_cap : row;
-    const uint32_t ow = win ? (uint32_t)row * D + AT_QCH * w + 8u * c : AT_OOB;
-    const auto x = __builtin_amdgcn_raw_buffer_load_b64(v.win, ow, 0, 0);
-    r.c = (uint32_t)x[0];
-    r.w1 = (uint32_t)x[1];
-    *valid = win;
-  }
   return r;
 }
 
 // The eight B operands of a pair's P V (N-tile n: channel 128 w + 8 c + n of
-// pair keys 8 g .. 8 g + 7) from the lane's eight RawV (key kk = 8 g + kk).
+// the lane's pair keys) from its eight RawV (element kk: pair_v_key(g, kk)).
 // Entry bytes widen with scale 1 and are multiplied by the group scale in
 // fp16 (E2M1 x E4M3 has at most 5 significant bits: exact).
 template <int PATH>
@@ -627,6 +648,7 @@ template <int E>
 __global__ __launch_bounds__(AT_THREADS) void attn_pair_kernel(AttnArgs a) {
   constexpr int NP = E + 1;   // E entry pairs, then the window pair
   __shared__ __attribute__((aligned(16))) PairLds<NP> lds;
+  __shared__ __attribute__((aligned(16))) PairStage<E> stage_all[AT_WAVES];
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
@@ -636,38 +658,63 @@ __global__ __launch_bounds__(AT_THREADS) void attn_pair_kernel(AttnArgs a) {
   const QueryView v = query_view(a, qi);
 
   // ---- 1. loads ---------------------------------------------------------------
-  int32_t idq[E][2], idv[E][8];
+  // slot ids: lane l holds key l % 32 of entry pair 2 i + l / 32
+  constexpr int NI = (E + 1) / 2;
+  int32_t ids[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int p = 2 * i + (lane >> 5);
+    ids[i] = slot_id(v, a.k, 0, p < E, AT_PAIR * (split * E + p) + (lane & 31));
+  }
+  // the window pair's QK bytes and Q do not wait for the ids
+  RawKey rk[NP][2];
+  const int wbase = pair_slot0<E>(a, split, E);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) rk[E][h] = load_slot_p<PATH_WINDOW>(v, a, wbase + pair_row_key(h, j), true, g, w, -1);
+  float4 qraw[8];
+  load_q(a, qi, j, g, w, qraw);
+  uint32_t vbits[NP];   // bit kk: pair key pair_v_key(g, kk) is present
 #pragma unroll
   for (int p = 0; p < E; ++p) {
     const int base = pair_slot0<E>(a, split, p);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) idq[p][h] = slot_id(v, a.k, 0, true, base + pair_row_key(h, j));
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) idv[p][kk] = slot_id(v, a.k, 0, true, base + 8 * g + kk);
-  }
-  float4 qraw[8];
-  load_q(a, qi, j, g, w, qraw);
-  RawKey rk[NP][2];
-  RawV rv[NP][8];
-  uint32_t vbits[NP];   // bit kk: pair key 8 g + kk is present
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    const int base = pair_slot0<E>(a, split, p);
+    const int32_t id = ids[p >> 1];
+    const bool ok = base + (lane & 31) < a.k && id >= 0 && id < a.kv_rows;
+    const uint32_t vm = (uint32_t)(__ballot(ok) >> (32 * (p & 1)));   // bit K: pair key K
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int slot = base + pair_row_key(h, j);
-      rk[p][h] = p < E ? load_slot_p<PATH_ENTRY>(v, a, slot, true, g, w, idq[p < E ? p : 0][h])
-                       : load_slot_p<PATH_WINDOW>(v, a, slot, true, g, w, -1);
+      const int K = pair_row_key(h, j);
+      const int32_t idk = __shfl(id, K + 32 * (p & 1));
+      rk[p][h] = load_slot_p<PATH_ENTRY>(v, a, base + K, true, g, w, idk);
     }
     vbits[p] = 0u;
 #pragma unroll
+    for (int kk = 0; kk < 8; ++kk) vbits[p] |= ((vm >> pair_v_key(g, kk)) & 1u) << kk;
+  }
+  {
+    vbits[E] = 0u;
+#pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      bool ok;
-      const int slot = base + 8 * g + kk;
-      rv[p][kk] = p < E ? load_v<PATH_ENTRY>(v, a, slot, j, w, idv[p < E ? p : 0][kk], &ok)
-                        : load_v<PATH_WINDOW>(v, a, slot, j, w, -1, &ok);
-      vbits[p] |= (ok ? 1u : 0u) << kk;
+      const int wi = wbase + pair_v_key(g, kk) - a.k;
+      const bool ok = wi >= 0 && wi < NWIN && v.p - (NWIN - 1) + wi >= 0;
+      vbits[E] |= (ok ? 1u : 0u) << kk;
     }
+  }
+  // P V bytes through the wave's LDS rows
+  PairStage<E>& stg = stage_all[w];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int K = pair_row_key(h, j);
+#pragma unroll
+    for (int p = 0; p < E; ++p) stage_entry<E>(stg, p, K, g, rk[p][h]);
+    stage_window<E>(stg, K, g, rk[E][h]);
+  }
+  RawV rv[NP][8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const int K = pair_v_key(g, kk);
+#pragma unroll
+    for (int p = 0; p < E; ++p) rv[p][kk] = unstage_entry<E>(stg, p, K, j);
+    rv[E][kk] = unstage_window<E>(stg, K, j);
   }
   f16x8 qh[4], ql[4];
   split_q(qraw, a.c_log2, qh, ql);
@@ -710,8 +757,8 @@ __global__ __launch_bounds__(AT_THREADS) void attn_pair_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[m][4 * h + r] = S[r];
       }
-      // x[m][kk] is pair key 8 g + kk (tile 0 rows for kk < 4, tile 1 rows
-      // for kk >= 4); its presence was found where the lane loaded it for P V
+      // x[m][kk] (tile kk >> 2, row 4 g + (kk & 3)) is pair key
+      // pair_v_key(g, kk), whose presence is bit kk of the pair's vbits
       float mx = -__builtin_huge_valf();
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
