@@ -165,6 +165,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void fu
   const int64_t q = blockIdx.y;
   const int NB = a.NB, K = a.K;
 
+  // ---- split selection with a pool: block x = 0 selects the pool (for the
+  // Reindex layers), block x = 1 the top_k best blocks straight from all the
+  // maxima (the same blocks as the best of the pool: the pool holds the NB
+  // best blocks under the same order), so neither waits for the other.
+  if (a.top_out && NB > K) {
+    const int pw = 64 * PER * wv + lane;
+    uint32_t key[PER];
+    load_keys<PER>(a.block_max + q * a.nblk, pw, (int)a.nblk, key);
+    if (blockIdx.x == 0) {
+      const uint32_t n_pool = block_select<NT, PER>(s, key, (uint32_t)NB, [&](int p, uint32_t, uint32_t slot) {
+        if (a.pool_out) a.pool_out[q * NB + slot] = p;
+      });
+      if (a.pool_out)
+        for (int j = (int)n_pool + tid; j < NB; j += NT) a.pool_out[q * NB + j] = -1;
+    } else {
+      const uint32_t n_top = block_select<NT, PER>(s, key, (uint32_t)K, [&](int p, uint32_t, uint32_t slot) {
+        a.top_out[q * K + slot] = p;
+      });
+      for (int j = (int)n_top + tid; j < K; j += NT) a.top_out[q * K + j] = -1;
+      if (tid == 0) a.ticket[q] = 0;
+    }
+    return;
+  }
+
   // ---- A. pool, and the top_k blocks ------------------------------------------
   {
     const int pw = 64 * PER * wv + lane;
@@ -348,7 +372,8 @@ hipError_t launch_full_select(const float* block_max, int64_t nblk, int64_t Q, i
     a.ticket = reinterpret_cast<int32_t*>(p + full_split_top_bytes(Q, k));
     a.sc_out = reinterpret_cast<float*>(p + full_split_top_bytes(Q, k) + full_split_ticket_bytes(Q));
   }
-  const dim3 grid(1, (unsigned)Q);
+  // split selection with a pool: two blocks per query (pool, best blocks)
+  const dim3 grid(split_ws && nb > k ? 2 : 1, (unsigned)Q);
   // many queries: 512-thread blocks, two per compute unit (top_k <= 512,
   // nblk <= 16,384); a few queries: 1,024 threads, the shortest block
   if (Q >= 512 && k <= 512 && nblk <= 512 * 32) {
