@@ -45,6 +45,9 @@ SIGNATURES = {
     "csa_compress_quant": (c_i32, [c_void_p, c_i64, c_i64, c_i64, c_void_p, c_void_p, c_i32, c_f32,
                                    c_void_p, c_void_p, c_i64, c_void_p, c_void_p, c_size, c_void_p]),
     "csa_window_append": (c_i32, [c_void_p, c_i64, c_i64, c_i64, c_void_p, c_void_p, c_i64, c_void_p]),
+    "csa_compress_quant_append": (c_i32, [c_void_p, c_i64, c_i64, c_i64, c_void_p, c_void_p, c_i32, c_f32,
+                                          c_void_p, c_void_p, c_i64, c_void_p, c_void_p, c_size,
+                                          c_void_p, c_i64, c_i64, c_i64, c_void_p, c_void_p, c_i64, c_void_p]),
     "csa_window_rebuild": (c_i32, [c_void_p, c_i64, c_i64, c_i64, c_void_p, c_void_p, c_i64, c_void_p]),
     "csa_kv_save": (c_i32, [ctypes.c_char_p, c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_i64, c_void_p, c_size,
                             c_void_p]),

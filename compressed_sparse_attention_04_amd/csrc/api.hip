@@ -179,14 +179,11 @@ size_t csa_compress_quant_workspace_size(int64_t n_entries) {
   return n_entries <= 0 ? 0 : compress_workspace_bytes(n_entries);
 }
 
-csa_status csa_compress_quant(const float* x, int64_t n_seq, int64_t n_per_seq, int64_t x_seq_stride,
-                              const float* w, const float* rope_cs, int32_t rope_dim, float eps,
-                              uint8_t* codes, uint8_t* scales, int64_t out_seq_stride, float* e_out,
-                              void* ws, size_t ws_bytes, hipStream_t stream) {
-  const char* fn = "csa_compress_quant";
-  CHECK(n_seq >= 0 && n_per_seq >= 0, CSA_ERR_INVALID_ARG, "%s: negative size", fn);
-  int64_t n = n_seq * n_per_seq;
-  if (n == 0) return CSA_OK;
+static csa_status check_compress(const char* fn, const float* x, int64_t n_seq, int64_t n_per_seq,
+                                 int64_t x_seq_stride, const float* w, const float* rope_cs, int32_t rope_dim,
+                                 float eps, uint8_t* codes, uint8_t* scales, int64_t out_seq_stride,
+                                 float* e_out, void* ws, size_t ws_bytes) {
+  const int64_t n = n_seq * n_per_seq;
   CHECK_PTR(x); CHECK_PTR(w); CHECK_PTR(codes); CHECK_PTR(scales);
   CHECK(rope_dim >= 0 && rope_dim <= D && rope_dim % 2 == 0, CSA_ERR_UNSUPPORTED,
         "%s: rope_dim must be even and in [0, 512] (got %d)", fn, rope_dim);
@@ -203,6 +200,31 @@ csa_status csa_compress_quant(const float* x, int64_t n_seq, int64_t n_per_seq, 
   size_t need = compress_workspace_bytes(n);
   CHECK(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
   CHECK_ALIGN(ws, 16);
+  return CSA_OK;
+}
+
+static csa_status check_window_append(const char* fn, const float* x, int64_t n_seq, int64_t n_tok,
+                                      int64_t x_seq_stride, const int32_t* pos0, uint8_t* win,
+                                      int64_t win_cap) {
+  CHECK_PTR(x); CHECK_PTR(pos0); CHECK_PTR(win);
+  CHECK(win_cap >= NWIN, CSA_ERR_UNSUPPORTED, "%s: win_cap must be >= 128", fn);
+  CHECK(n_tok <= win_cap, CSA_ERR_INVALID_ARG, "%s: n_tok exceeds win_cap", fn);
+  CHECK(x_seq_stride % 4 == 0, CSA_ERR_ALIGNMENT, "%s: x_seq_stride must be a multiple of 4", fn);
+  CHECK(n_seq == 1 || x_seq_stride >= n_tok * D, CSA_ERR_INVALID_ARG, "%s: x_seq_stride too small", fn);
+  CHECK_ALIGN(x, 16); CHECK_ALIGN(pos0, 4); CHECK_ALIGN(win, 16);
+  return CSA_OK;
+}
+
+csa_status csa_compress_quant(const float* x, int64_t n_seq, int64_t n_per_seq, int64_t x_seq_stride,
+                              const float* w, const float* rope_cs, int32_t rope_dim, float eps,
+                              uint8_t* codes, uint8_t* scales, int64_t out_seq_stride, float* e_out,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "csa_compress_quant";
+  CHECK(n_seq >= 0 && n_per_seq >= 0, CSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (n_seq * n_per_seq == 0) return CSA_OK;
+  const csa_status st = check_compress(fn, x, n_seq, n_per_seq, x_seq_stride, w, rope_cs, rope_dim, eps, codes,
+                                       scales, out_seq_stride, e_out, ws, ws_bytes);
+  if (st != CSA_OK) return st;
   return hip_status(launch_compress_quant(x, n_seq, n_per_seq, x_seq_stride, w, rope_cs, rope_dim, eps,
                                           codes, scales, out_seq_stride, e_out, ws, stream), fn);
 }
@@ -213,13 +235,37 @@ csa_status csa_window_append(const float* x, int64_t n_seq, int64_t n_tok, int64
   const char* fn = "csa_window_append";
   CHECK(n_seq >= 0 && n_tok >= 0, CSA_ERR_INVALID_ARG, "%s: negative size", fn);
   if (n_seq * n_tok == 0) return CSA_OK;
-  CHECK_PTR(x); CHECK_PTR(pos0); CHECK_PTR(win);
-  CHECK(win_cap >= NWIN, CSA_ERR_UNSUPPORTED, "%s: win_cap must be >= 128", fn);
-  CHECK(n_tok <= win_cap, CSA_ERR_INVALID_ARG, "%s: n_tok exceeds win_cap", fn);
-  CHECK(x_seq_stride % 4 == 0, CSA_ERR_ALIGNMENT, "%s: x_seq_stride must be a multiple of 4", fn);
-  CHECK(n_seq == 1 || x_seq_stride >= n_tok * D, CSA_ERR_INVALID_ARG, "%s: x_seq_stride too small", fn);
-  CHECK_ALIGN(x, 16); CHECK_ALIGN(pos0, 4); CHECK_ALIGN(win, 16);
+  const csa_status st = check_window_append(fn, x, n_seq, n_tok, x_seq_stride, pos0, win, win_cap);
+  if (st != CSA_OK) return st;
   return hip_status(launch_window_append(x, n_seq, n_tok, x_seq_stride, pos0, win, win_cap, stream), fn);
+}
+
+// ------------------------------- compression and window append, one launch ----
+csa_status csa_compress_quant_append(const float* x, int64_t n_seq, int64_t n_per_seq, int64_t x_seq_stride,
+                                     const float* w, const float* rope_cs, int32_t rope_dim, float eps,
+                                     uint8_t* codes, uint8_t* scales, int64_t out_seq_stride, float* e_out,
+                                     void* ws, size_t ws_bytes, const float* xw, int64_t nw_seq, int64_t nw_tok,
+                                     int64_t xw_seq_stride, const int32_t* pos0, uint8_t* win, int64_t win_cap,
+                                     hipStream_t stream) {
+  const char* fn = "csa_compress_quant_append";
+  CHECK(n_seq >= 0 && n_per_seq >= 0 && nw_seq >= 0 && nw_tok >= 0, CSA_ERR_INVALID_ARG, "%s: negative size",
+        fn);
+  const bool comp = n_seq * n_per_seq > 0, app = nw_seq * nw_tok > 0;
+  if (comp) {
+    const csa_status st = check_compress(fn, x, n_seq, n_per_seq, x_seq_stride, w, rope_cs, rope_dim, eps, codes,
+                                         scales, out_seq_stride, e_out, ws, ws_bytes);
+    if (st != CSA_OK) return st;
+  }
+  if (app) {
+    const csa_status st = check_window_append(fn, xw, nw_seq, nw_tok, xw_seq_stride, pos0, win, win_cap);
+    if (st != CSA_OK) return st;
+  }
+  if (!comp && !app) return CSA_OK;
+  const WindowAppendArgs ap{xw, nw_seq, nw_tok, xw_seq_stride, pos0, win, win_cap};
+  if (!comp) return hip_status(launch_window_append(xw, nw_seq, nw_tok, xw_seq_stride, pos0, win, win_cap, stream), fn);
+  return hip_status(launch_compress_quant(x, n_seq, n_per_seq, x_seq_stride, w, rope_cs, rope_dim, eps, codes,
+                                          scales, out_seq_stride, e_out, ws, stream, app ? &ap : nullptr),
+                    fn);
 }
 
 csa_status csa_window_rebuild(const float* x, int64_t n_ring, int64_t n_tok, int64_t x_ring_stride,

@@ -15,11 +15,22 @@ hipError_t launch_window_append(const float* x, int64_t n_seq, int64_t n_tok, in
                                 const int32_t* pos0, uint8_t* win, int64_t win_cap, hipStream_t st);
 hipError_t launch_window_rebuild(const float* x, int64_t n_ring, int64_t n_tok, int64_t x_ring_stride,
                                  const int32_t* p_last, uint8_t* win, int64_t win_cap, hipStream_t st);
+// A window append: token t of sequence s at x + s * x_seq_stride + t * 512
+// goes to row (pos0[s] + t) % win_cap of ring s.
+struct WindowAppendArgs {
+  const float* x;
+  int64_t n_seq, n_tok, x_seq_stride;
+  const int32_t* pos0;
+  uint8_t* win;
+  int64_t win_cap;
+};
 size_t compress_workspace_bytes(int64_t n);
+// append (optional): a window append done in the same launches
 hipError_t launch_compress_quant(const float* x, int64_t n_seq, int64_t n_per_seq,
                                  int64_t x_seq_stride, const float* w, const float* rope_cs,
                                  int rope_dim, float eps, uint8_t* codes, uint8_t* scales,
-                                 int64_t out_seq_stride, float* e_out, void* ws, hipStream_t st);
+                                 int64_t out_seq_stride, float* e_out, void* ws, hipStream_t st,
+                                 const WindowAppendArgs* append = nullptr);
 
 // index.hip
 struct ScoreArgs {

@@ -69,20 +69,16 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
 
 // ---------------------------------------------------------------------------
 // Window append: 32 lanes per token, 16 channels per lane, one 16-byte store.
-__global__ __launch_bounds__(256) void window_append_kernel(const float* __restrict__ x,
-                                                            int64_t n_seq, int64_t n_tok,
-                                                            int64_t x_seq_stride,
-                                                            const int32_t* __restrict__ pos0,
-                                                            uint8_t* __restrict__ win,
-                                                            int64_t win_cap) {
-  int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// Thread t of the launch (t = 256 block + thread) takes lane t % 32 of token
+// t / 32.
+__device__ __forceinline__ void window_append_thread(const WindowAppendArgs& a, int64_t t) {
   int64_t tok = t >> 5;
   int lane = (int)(t & 31);
-  if (tok >= n_seq * n_tok) return;
-  int64_t s = tok / n_tok, i = tok % n_tok;
-  int64_t p = (int64_t)pos0[s] + i;
+  if (tok >= a.n_seq * a.n_tok) return;
+  int64_t s = tok / a.n_tok, i = tok % a.n_tok;
+  int64_t p = (int64_t)a.pos0[s] + i;
   if (p < 0) return;
-  const float4* src = reinterpret_cast<const float4*>(x + s * x_seq_stride + i * D + 16 * lane);
+  const float4* src = reinterpret_cast<const float4*>(a.x + s * a.x_seq_stride + i * D + 16 * lane);
   uint32_t w[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -90,9 +86,15 @@ __global__ __launch_bounds__(256) void window_append_kernel(const float* __restr
     w[k] = e4m3_encode(f.x) | (e4m3_encode(f.y) << 8) | (e4m3_encode(f.z) << 16) |
            (e4m3_encode(f.w) << 24);
   }
-  uint8_t* dst = win + (s * win_cap + p % win_cap) * D + 16 * lane;
+  uint8_t* dst = a.win + (s * a.win_cap + p % a.win_cap) * D + 16 * lane;
   *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
 }
+
+__global__ __launch_bounds__(256) void window_append_kernel(WindowAppendArgs a) {
+  window_append_thread(a, (int64_t)blockIdx.x * 256 + threadIdx.x);
+}
+
+int64_t window_append_blocks(const WindowAppendArgs& a) { return (a.n_seq * a.n_tok * 32 + 255) / 256; }
 
 // ---------------------------------------------------------------------------
 // Window rebuild from the latest tokens: 32 lanes per ring row, 16 channels
@@ -214,15 +216,14 @@ __global__ __launch_bounds__(256) void compress_gemm_kernel(const float* __restr
 // with 16-byte stores (codes: 16 lanes x 16 B, scales: 2 lanes x 16 B).
 constexpr int CE_MAX_SPLIT = 16;
 
-__global__ __launch_bounds__(256) void compress_epilogue_kernel(
-    const double* __restrict__ ypart, int n_split, int64_t n_seq, int64_t n_per_seq,
+__device__ __forceinline__ void compress_epilogue_entry(
+    int64_t entry, const double* __restrict__ ypart, int n_split, int64_t n_seq, int64_t n_per_seq,
     const float* __restrict__ rope_cs, int rope_dim, float eps, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, int64_t out_seq_stride, float* __restrict__ e_out) {
   __shared__ double red[4];
   __shared__ __attribute__((aligned(16))) uint8_t row_codes[CODE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t row_scales[SCALE_BYTES];
   const int64_t n = n_seq * n_per_seq;
-  const int64_t entry = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   double2 part[CE_MAX_SPLIT];
 #pragma unroll
@@ -270,6 +271,29 @@ __global__ __launch_bounds__(256) void compress_epilogue_kernel(
         reinterpret_cast<const uint4*>(row_scales)[t - 16];
 }
 
+__global__ __launch_bounds__(256) void compress_epilogue_kernel(
+    const double* __restrict__ ypart, int n_split, int64_t n_seq, int64_t n_per_seq,
+    const float* __restrict__ rope_cs, int rope_dim, float eps, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, int64_t out_seq_stride, float* __restrict__ e_out) {
+  compress_epilogue_entry(blockIdx.x, ypart, n_split, n_seq, n_per_seq, rope_cs, rope_dim, eps, codes, scales,
+                          out_seq_stride, e_out);
+}
+
+// The epilogue and a window append in one launch (independent outputs):
+// blocks below n finish entries, the blocks after them append tokens.
+__global__ __launch_bounds__(256) void compress_epilogue_append_kernel(
+    const double* __restrict__ ypart, int n_split, int64_t n_seq, int64_t n_per_seq,
+    const float* __restrict__ rope_cs, int rope_dim, float eps, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, int64_t out_seq_stride, float* __restrict__ e_out, WindowAppendArgs ap) {
+  const int64_t n = n_seq * n_per_seq;
+  if ((int64_t)blockIdx.x >= n) {   // block-uniform, before any barrier
+    window_append_thread(ap, ((int64_t)blockIdx.x - n) * 256 + threadIdx.x);
+    return;
+  }
+  compress_epilogue_entry(blockIdx.x, ypart, n_split, n_seq, n_per_seq, rope_cs, rope_dim, eps, codes, scales,
+                          out_seq_stride, e_out);
+}
+
 // ------------------------------------------------------------- launchers --
 hipError_t launch_quantize(const float* e, int64_t n, uint8_t* codes, uint8_t* scales,
                            hipStream_t st) {
@@ -289,11 +313,9 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_
 
 hipError_t launch_window_append(const float* x, int64_t n_seq, int64_t n_tok, int64_t x_seq_stride,
                                 const int32_t* pos0, uint8_t* win, int64_t win_cap, hipStream_t st) {
-  int64_t tokens = n_seq * n_tok;
-  if (tokens == 0) return hipSuccess;
-  int64_t blocks = (tokens * 32 + 255) / 256;
-  hipLaunchKernelGGL(window_append_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, n_seq, n_tok,
-                     x_seq_stride, pos0, win, win_cap);
+  const WindowAppendArgs a{x, n_seq, n_tok, x_seq_stride, pos0, win, win_cap};
+  if (n_seq * n_tok == 0) return hipSuccess;
+  hipLaunchKernelGGL(window_append_kernel, dim3((unsigned)window_append_blocks(a)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -322,9 +344,15 @@ size_t compress_workspace_bytes(int64_t n) {
 hipError_t launch_compress_quant(const float* x, int64_t n_seq, int64_t n_per_seq,
                                  int64_t x_seq_stride, const float* w, const float* rope_cs,
                                  int rope_dim, float eps, uint8_t* codes, uint8_t* scales,
-                                 int64_t out_seq_stride, float* e_out, void* ws, hipStream_t st) {
+                                 int64_t out_seq_stride, float* e_out, void* ws, hipStream_t st,
+                                 const WindowAppendArgs* append) {
   int64_t n = n_seq * n_per_seq;
-  if (n == 0) return hipSuccess;
+  const int64_t app_blocks = (append && append->n_seq * append->n_tok > 0) ? window_append_blocks(*append) : 0;
+  if (n == 0) {
+    if (app_blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(window_append_kernel, dim3((unsigned)app_blocks), dim3(256), 0, st, *append);
+    return hipGetLastError();
+  }
   int split = compress_split_k(n);
   double* ypart = reinterpret_cast<double*>(ws);
   dim3 grid(D / CG_BN, (unsigned)((n + CG_BM - 1) / CG_BM), split);
@@ -332,8 +360,13 @@ hipError_t launch_compress_quant(const float* x, int64_t n_seq, int64_t n_per_se
                      w, ypart, (4 * D) / split);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(compress_epilogue_kernel, dim3((unsigned)n), dim3(256), 0, st, ypart, split,
-                     n_seq, n_per_seq, rope_cs, rope_dim, eps, codes, scales, out_seq_stride, e_out);
+  if (app_blocks > 0)
+    hipLaunchKernelGGL(compress_epilogue_append_kernel, dim3((unsigned)(n + app_blocks)), dim3(256), 0, st, ypart,
+                       split, n_seq, n_per_seq, rope_cs, rope_dim, eps, codes, scales, out_seq_stride, e_out,
+                       *append);
+  else
+    hipLaunchKernelGGL(compress_epilogue_kernel, dim3((unsigned)n), dim3(256), 0, st, ypart, split,
+                       n_seq, n_per_seq, rope_cs, rope_dim, eps, codes, scales, out_seq_stride, e_out);
   return hipGetLastError();
 }
 

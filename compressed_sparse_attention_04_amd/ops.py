@@ -118,17 +118,9 @@ def _ptr_off(t, offset):
     return ctypes.c_void_p(t.data_ptr() + int(offset) * t.element_size())
 
 
-def csa_compress_quant(x, w, rope_cs, codes, scales, n_seq, n_per_seq, x_seq_stride=None,
-                       out_seq_stride=None, x_offset=0, out_offset=0, rope_dim=64, eps=1e-6,
-                       e_out=None, stream=None):
-    """Compress 4-token groups, RMSNorm, RoPE, quantize and store into codes/scales.
-
-    x: contiguous float32 tensor; entry (s, r) reads its 4 tokens at element
-    x_offset + s * x_seq_stride + r * 2048.  codes / scales: contiguous uint8
-    tensors of 256- / 32-byte rows; entry (s, r) goes to row
-    out_offset + s * out_seq_stride + r.  rope_cs: float32
-    [n_seq, n_per_seq, rope_dim / 2, 2].
-    """
+def _compress_args(x, w, rope_cs, codes, scales, n_seq, n_per_seq, x_seq_stride, out_seq_stride, x_offset,
+                   out_offset, rope_dim, eps, e_out):
+    """Checks and C arguments (with the workspace) of a compression call."""
     _need(x, "x", torch.float32)
     dev = x.device
     _need(w, "w", torch.float32, dev, shape=(4, D, D))
@@ -152,10 +144,40 @@ def csa_compress_quant(x, w, rope_cs, codes, scales, n_seq, n_per_seq, x_seq_str
         if e_out.numel() != n * D:
             raise ValueError("e_out must hold [n, 512] floats")
     ws = _workspace(_lib.load().csa_compress_quant_workspace_size(n), dev)
-    _call("csa_compress_quant", _ptr_off(x, x_offset), n_seq, n_per_seq, xs, _p(w),
-          _p(rope_cs) if rope_dim else None, rope_dim, ctypes.c_float(eps),
-          _ptr_off(codes, out_offset * (D // 2)), _ptr_off(scales, out_offset * (D // 16)), os_,
-          _p(e_out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    args = (_ptr_off(x, x_offset), n_seq, n_per_seq, xs, _p(w),
+            _p(rope_cs) if rope_dim else None, rope_dim, ctypes.c_float(eps),
+            _ptr_off(codes, out_offset * (D // 2)), _ptr_off(scales, out_offset * (D // 16)), os_,
+            _p(e_out), _p(ws), 0 if ws is None else ws.numel())
+    return args, ws
+
+
+def csa_compress_quant(x, w, rope_cs, codes, scales, n_seq, n_per_seq, x_seq_stride=None,
+                       out_seq_stride=None, x_offset=0, out_offset=0, rope_dim=64, eps=1e-6,
+                       e_out=None, stream=None):
+    """Compress 4-token groups, RMSNorm, RoPE, quantize and store into codes/scales.
+
+    x: contiguous float32 tensor; entry (s, r) reads its 4 tokens at element
+    x_offset + s * x_seq_stride + r * 2048.  codes / scales: contiguous uint8
+    tensors of 256- / 32-byte rows; entry (s, r) goes to row
+    out_offset + s * out_seq_stride + r.  rope_cs: float32
+    [n_seq, n_per_seq, rope_dim / 2, 2].
+    """
+    args, ws = _compress_args(x, w, rope_cs, codes, scales, n_seq, n_per_seq, x_seq_stride, out_seq_stride,
+                              x_offset, out_offset, rope_dim, eps, e_out)
+    _call("csa_compress_quant", *args, _stream(stream))
+    _keep(stream, ws)
+
+
+def csa_compress_quant_append(x, w, rope_cs, codes, scales, n_seq, n_per_seq, xw, pos0, win, nw_seq, nw_tok,
+                              x_seq_stride=None, out_seq_stride=None, x_offset=0, out_offset=0, rope_dim=64,
+                              eps=1e-6, e_out=None, xw_seq_stride=None, xw_offset=0, stream=None):
+    """csa_compress_quant(x, ...) and csa_window_append(xw, pos0, win, nw_seq,
+    nw_tok, ...) in one call (two launches instead of three); arguments as in
+    those two functions."""
+    args, ws = _compress_args(x, w, rope_cs, codes, scales, n_seq, n_per_seq, x_seq_stride, out_seq_stride,
+                              x_offset, out_offset, rope_dim, eps, e_out)
+    wargs = _append_args(xw, pos0, win, nw_seq, nw_tok, xw_seq_stride, xw_offset)
+    _call("csa_compress_quant_append", *args, *wargs, _stream(stream))
     _keep(stream, ws)
 
 
@@ -167,6 +189,11 @@ def csa_window_append(x, pos0, win, n_seq, n_tok, x_seq_stride=None, x_offset=0,
     Token t of sequence s is read at element x_offset + s * x_seq_stride + t * 512
     and lands in row (pos0[s] + t) % cap.
     """
+    _call("csa_window_append", *_append_args(x, pos0, win, n_seq, n_tok, x_seq_stride, x_offset), _stream(stream))
+
+
+def _append_args(x, pos0, win, n_seq, n_tok, x_seq_stride, x_offset):
+    """Checks and C arguments of a window append."""
     _need(x, "x", torch.float32)
     dev = x.device
     _need(pos0, "pos0", torch.int32, dev, shape=(n_seq,))
@@ -176,8 +203,7 @@ def csa_window_append(x, pos0, win, n_seq, n_tok, x_seq_stride=None, x_offset=0,
     xs = x_seq_stride if x_seq_stride is not None else n_tok * D
     if n_seq * n_tok and (x_offset < 0 or x_offset + (n_seq - 1) * xs + n_tok * D > x.numel()):
         raise ValueError("x is too small")
-    _call("csa_window_append", _ptr_off(x, x_offset), n_seq, n_tok, xs, _p(pos0), _p(win), win.shape[1],
-          _stream(stream))
+    return (_ptr_off(x, x_offset), n_seq, n_tok, xs, _p(pos0), _p(win), win.shape[1])
 
 
 def csa_window_rebuild(x, p_last, win, n_ring, n_tok, x_ring_stride=None, x_offset=0, stream=None):

@@ -123,12 +123,12 @@ class LayerStep:
 
     def step(self):
         tail = self.x_tail.shape[1]
-        ops.csa_window_append(self._win_src(), self.pos_step, self._win_rings(), self.n_win * self.S, self.n_step,
-                              x_seq_stride=tail * D, x_offset=(N_WIN - 1) * D)
-        ops.csa_compress_quant(self.x_tail, self.w, self.rope_cs, self.codes, self.scales,
-                               n_seq=self.S, n_per_seq=self.new, x_seq_stride=tail * D,
-                               x_offset=(tail - M * self.new) * D, out_seq_stride=self.cap,
-                               out_offset=self.prior, rope_dim=self.rope_dim, eps=self.eps)
+        ops.csa_compress_quant_append(self.x_tail, self.w, self.rope_cs, self.codes, self.scales,
+                                      n_seq=self.S, n_per_seq=self.new, xw=self._win_src(), pos0=self.pos_step,
+                                      win=self._win_rings(), nw_seq=self.n_win * self.S, nw_tok=self.n_step,
+                                      x_seq_stride=tail * D, x_offset=(tail - M * self.new) * D,
+                                      out_seq_stride=self.cap, out_offset=self.prior, rope_dim=self.rope_dim,
+                                      eps=self.eps, xw_seq_stride=tail * D, xw_offset=(N_WIN - 1) * D)
         for call in self.calls:
             call()
 

@@ -134,6 +134,25 @@ csa_status csa_window_append(const float* x, int64_t n_seq, int64_t n_tok, int64
                              const int32_t* pos0, uint8_t* win, int64_t win_cap,
                              hipStream_t stream);
 
+/* ------------------------------- compression and window append together ----
+ * csa_compress_quant_append: csa_compress_quant and csa_window_append of the
+ * same step in one call, for a decode or prefill step that completes entries
+ * and appends its tokens: the two write different arrays, so the append's
+ * threads run as extra blocks of the compression's second launch (two
+ * launches instead of three).  The first fourteen arguments are those of
+ * csa_compress_quant, the next seven (xw, nw_seq, nw_tok, xw_seq_stride,
+ * pos0, win, win_cap) those of csa_window_append; either part may be empty
+ * (n_seq * n_per_seq == 0 or nw_seq * nw_tok == 0), and an empty part's
+ * arguments are not checked.  Results, validation and status codes are
+ * those of the two calls; nothing is enqueued when either part is invalid.
+ */
+csa_status csa_compress_quant_append(const float* x, int64_t n_seq, int64_t n_per_seq, int64_t x_seq_stride,
+                                     const float* w, const float* rope_cs, int32_t rope_dim, float eps,
+                                     uint8_t* codes, uint8_t* scales, int64_t out_seq_stride, float* e_out,
+                                     void* ws, size_t ws_bytes, const float* xw, int64_t nw_seq, int64_t nw_tok,
+                                     int64_t xw_seq_stride, const int32_t* pos0, uint8_t* win, int64_t win_cap,
+                                     hipStream_t stream);
+
 /* ---------------------------------------------------------------- f2 ----
  * csa_window_rebuild: rebuild n_ring window rings from their latest tokens
  * ("DeepSeek-V4.1 架构解析" §03, SWA Bounded Replay: the window state is not kept in the

@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 28
+    assert len(names) == 29
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
@@ -59,6 +59,30 @@ def test_quantize_validation(lib):
     assert b"NULL" in lib.csa_last_error()
     assert lib.csa_quantize(P, -1, P, P, None) == INVALID
     assert lib.csa_quantize(P_ODD, 4, P, P, None) == ALIGN
+
+
+def test_compress_append_validation(lib):
+    """The fused call checks each non-empty part as the separate calls do and
+    enqueues nothing when either is invalid."""
+    f = lib.csa_compress_quant_append
+    need = lib.csa_compress_quant_workspace_size(10)
+    comp = [P, 1, 10, 10 * 2048, P, P, 64, ctypes.c_float(1e-6), P, P, 10, None, P, need]
+    none_comp = [None, 0, 0, 0, None, None, 0, ctypes.c_float(1e-6), None, None, 0, None, None, 0]
+    app = [P, 2, 1, 4096, P, P, 128]
+    none_app = [None, 0, 0, 0, None, None, 0]
+    assert f(*none_comp, *none_app, None) == OK                           # both parts empty
+    a = list(app); a[0] = None
+    assert f(*none_comp, *a, None) == INVALID                             # window part: x missing
+    a = list(app); a[6] = 127
+    assert f(*none_comp, *a, None) == UNSUPPORTED                         # window part: win_cap < 128
+    a = list(app); a[5] = P_ODD
+    assert f(*comp, *a, None) == ALIGN                                    # valid compression, bad window
+    a = list(comp); a[6] = 63
+    assert f(*a, *app, None) == UNSUPPORTED                               # bad compression, valid window
+    a = list(comp); a[13] = need - 1
+    assert f(*a, *none_app, None) == WORKSPACE
+    assert f(*none_comp[:1], -1, *none_comp[2:], *none_app, None) == INVALID
+    assert b"csa_compress_quant_append" in lib.csa_last_error()
 
 
 def test_compress_validation(lib):

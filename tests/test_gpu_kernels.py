@@ -81,6 +81,40 @@ def test_window_append_bit_exact(n_seq, n_tok, cap, p0):
         assert np.array_equal(got[s], expect)
 
 
+@pytest.mark.parametrize("n_per,n_tok", [(3, 1), (0, 2), (2, 0), (5, 130)])
+def test_compress_quant_append_matches_separate_calls(n_per, n_tok):
+    """csa_compress_quant_append writes the same bytes as csa_compress_quant
+    followed by csa_window_append (either part may be empty)."""
+    rng = np.random.default_rng(10 * n_per + n_tok)
+    n_seq, rows, cap = 3, 12, 160
+    x = rng.standard_normal((n_seq, 4 * max(n_per, 1), 512)).astype(np.float32)
+    w = (rng.standard_normal((4, 512, 512)) / np.sqrt(2048)).astype(np.float32)
+    ang = rng.uniform(0, 100, (n_seq, n_per, 32))
+    cs = np.stack([np.cos(ang), np.sin(ang)], -1).astype(np.float32)
+    xw = (rng.standard_normal((n_seq, max(n_tok, 1), 512)) * 3).astype(np.float32)
+    pos0 = np.array([50 + 9 * s for s in range(n_seq)], np.int32)
+    outs = []
+    for fused in (False, True):
+        codes = torch.full((n_seq, rows, 256), 0x5A, dtype=torch.uint8, device=DEV)
+        scales = torch.full((n_seq, rows, 32), 0x5A, dtype=torch.uint8, device=DEV)
+        win = torch.full((n_seq, cap, 512), 0xAB, dtype=torch.uint8, device=DEV)
+        kw = dict(x_seq_stride=4 * max(n_per, 1) * 512, out_seq_stride=rows, out_offset=2)
+        if fused:
+            ops.csa_compress_quant_append(t_(x), t_(w), t_(cs), codes, scales, n_seq, n_per, t_(xw), t_(pos0), win,
+                                          n_seq, n_tok, xw_seq_stride=max(n_tok, 1) * 512, **kw)
+        else:
+            ops.csa_compress_quant(t_(x), t_(w), t_(cs), codes, scales, n_seq, n_per, **kw)
+            ops.csa_window_append(t_(xw), t_(pos0), win, n_seq, n_tok, x_seq_stride=max(n_tok, 1) * 512)
+        torch.cuda.synchronize()
+        outs.append((np_(codes), np_(scales), np_(win)))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    if n_per:
+        assert (outs[1][0][:, 2:2 + n_per] != 0x5A).any()
+    if n_tok:
+        assert (outs[1][2] != 0xAB).any()
+
+
 def test_compress_quant_chain():
     """The GPU chain (fp64 GEMM, RMSNorm, RoPE; one rounding to fp32) gives the
     fp32 rounding of the oracle's fp64 result, up to one fp32 ulp where the
