@@ -221,6 +221,10 @@ __device__ __forceinline__ bool find_bin(SelShared& s, const uint32_t (&h)[BPT],
   return true;
 }
 
+template <int NT, int PER>
+__device__ __forceinline__ void threshold_from_hist(SelShared& s, const uint32_t (&key)[PER], uint32_t K, float vmax,
+                                                    float inv, uint32_t* T_out, uint32_t* take_out);
+
 // Steps 1-3: the K-th largest key *T of the block's keys and how many keys
 // equal to it are taken (*take_eq); T = 0 when at most K keys are valid (every
 // valid key is taken).  Every thread of the block calls it.
@@ -264,6 +268,19 @@ __device__ __forceinline__ void block_threshold(SelShared& s, const uint32_t (&k
   for (int u = 0; u < PER; ++u)
     if (key[u] != 0) atomicAdd(&s.hist[value_bin(key[u], vmax, inv)], 1u);
   __syncthreads();
+  threshold_from_hist<NT, PER>(s, key, K, vmax, inv, T_out, take_out);
+}
+
+// Steps 2-3 once the value histogram of the valid keys (value_bin with vmax,
+// inv; at least K of them) is in hist and s.n_cand is 0: the bin of the K-th
+// largest key, then that key T exactly among the bin's keys (pairwise
+// ranking when the bin holds at most SEL_RANK_MAX keys, else a radix select)
+// and how many keys equal to T are taken.
+template <int NT, int PER>
+__device__ __forceinline__ void threshold_from_hist(SelShared& s, const uint32_t (&key)[PER], uint32_t K, float vmax,
+                                                    float inv, uint32_t* T_out, uint32_t* take_out) {
+  constexpr int BPT = SEL_BINS / NT;
+  const int tid = threadIdx.x;
   {
     uint32_t h[BPT];
 #pragma unroll
@@ -377,10 +394,12 @@ __device__ __forceinline__ uint32_t block_compact(SelShared& s, const uint32_t (
   return gt_tot + (eq_tot < take_eq ? eq_tot : take_eq);
 }
 
-// Steps 1-4 over a candidate list of n keys in LDS (position order), CP per
-// thread; emit(p, key, slot) with p from cpos.
+// Steps 2-4 over the n >= K candidates gathered in LDS (ckey / cpos,
+// position order), CP per thread, whose values lie in [vlo, vmax] (hist is
+// clear and s.n_cand is 0); emit(p, key, slot) with p from cpos.
 template <int NT, int CP, class Emit>
-__device__ __forceinline__ uint32_t select_candidates(SelShared& s, uint32_t n, uint32_t K, Emit emit) {
+__device__ __forceinline__ uint32_t select_candidates(SelShared& s, uint32_t n, uint32_t K, float vmax, float vlo,
+                                                      Emit emit) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   uint32_t ck[CP];
 #pragma unroll
@@ -388,8 +407,14 @@ __device__ __forceinline__ uint32_t select_candidates(SelShared& s, uint32_t n, 
     const uint32_t c = 64 * CP * wv + 64 * i + lane;
     ck[i] = c < n ? s.ckey[c] : 0u;
   }
+  const float range = vmax - vlo;
+  const float inv = (range > 0.0f && range < __builtin_huge_valf()) ? (float)SEL_BINS / range : 0.0f;
+#pragma unroll
+  for (int i = 0; i < CP; ++i)
+    if (ck[i] != 0) atomicAdd(&s.hist[value_bin(ck[i], vmax, inv)], 1u);
+  __syncthreads();
   uint32_t T, take_eq;
-  block_threshold<NT, CP>(s, ck, K, &T, &take_eq);
+  threshold_from_hist<NT, CP>(s, ck, K, vmax, inv, &T, &take_eq);
   return block_compact<NT, CP>(s, ck, T, take_eq, K, [&](int i, uint32_t slot) {
     const uint32_t c = 64 * CP * wv + 64 * i + lane;
     emit((int)s.cpos[c], ck[i], slot);
@@ -401,34 +426,37 @@ __device__ __forceinline__ uint32_t select_candidates(SelShared& s, uint32_t n, 
 // with p.  Returns the number selected (min(K, valid keys)).
 //
 // With 8+ keys per thread the K-th largest key is first bounded from below
-// with a sample (one key per thread, spread over each wave's run): T_lo = the
-// smallest sample key of the sample bin where the sample count reaches m,
-// about 1.5 K n_sample / n (+8).  If the keys >= T_lo number between K and
+// with a sample (one key per thread, spread over each wave's run): T_lo is
+// the lower edge of the sample-histogram bin (between the smallest sample
+// and the largest key) where the sample count reaches m, about
+// 1.5 K n_sample / n (+8).  If the keys >= T_lo number between K and
 // SEL_CAND_MAX, they hold the K best (every other key is smaller), so they
-// are gathered in position order and selected exactly; otherwise the exact
-// selection runs over all keys.
+// are gathered in position order and selected exactly, their histogram
+// spanning [T_lo, largest key]; otherwise the exact selection runs over all
+// keys.
 template <int NT, int PER, class Emit>
 __device__ __forceinline__ uint32_t block_select(SelShared& s, const uint32_t (&key)[PER], uint32_t K, Emit emit) {
   constexpr int W = NT / 64, BPT = SEL_BINS / NT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int pw = 64 * PER * wv + lane;
   if constexpr (PER >= 8) {
-    uint32_t nv_w = 0, smp = 0;
+    uint32_t nv_w = 0, smp = 0, kmx = 0;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       nv_w += (uint32_t)__popcll(__ballot(key[u] != 0));
       smp = (u == (lane & (PER - 1))) ? key[u] : smp;
+      kmx = key[u] > kmx ? key[u] : kmx;
     }
-    const uint32_t smax = wave_reduce<0>(smp), smin = wave_reduce<1>(smp != 0 ? smp : 0xFFFFFFFFu);
+    kmx = wave_reduce<0>(kmx);
+    const uint32_t smin = wave_reduce<1>(smp != 0 ? smp : 0xFFFFFFFFu);
     const uint32_t sv_w = (uint32_t)__popcll(__ballot(smp != 0));
     __syncthreads();   // earlier readers of the shared state are done
     for (int b = tid; b < SEL_BINS; b += NT) s.hist[b] = 0;
     if (lane == 0) {
-      s.wred[0][wv] = smax;
+      s.wred[0][wv] = kmx;
       s.wred[1][wv] = smin;
       s.wred[2][wv] = nv_w | (sv_w << 16);   // <= 32768 keys, <= 1024 samples
     }
-    if (tid == 0) s.tlo = 0xFFFFFFFFu;
     __syncthreads();
     const uint32_t kmax = waves_reduce<W, 0>(s.wred[0]), kmin = waves_reduce<W, 1>(s.wred[1]);
     const uint32_t packed = waves_sum<W>(s.wred[2], nullptr);   // sum of the 16-bit fields: no carry
@@ -446,16 +474,23 @@ __device__ __forceinline__ uint32_t block_select(SelShared& s, const uint32_t (&
         for (int j = 0; j < BPT; ++j) h[j] = s.hist[BPT * tid + j];
         int bin;
         uint32_t left;
-        if (find_bin<NT, BPT>(s, h, m, &bin, &left)) s.bstar = (uint32_t)bin;
+        if (find_bin<NT, BPT>(s, h, m, &bin, &left)) {
+          uint32_t t = kmin;
+          if (inv != 0.0f) {
+            const float e = vmax - (float)(bin + 1) / inv;   // the bin's lower edge
+            if (e > vmin) t = select_key(e);
+          }
+          s.tlo = t;
+        }
       }
-      __syncthreads();
-      if (smp != 0 && value_bin(smp, vmax, inv) == (int)s.bstar) atomicMin(&s.tlo, smp);
       __syncthreads();
       const uint32_t tlo = s.tlo;
       uint32_t c_w = 0;
 #pragma unroll
       for (int u = 0; u < PER; ++u) c_w += (uint32_t)__popcll(__ballot(key[u] >= tlo));
       if (lane == 0) s.wred[0][wv] = c_w;
+      for (int b = tid; b < SEL_BINS; b += NT) s.hist[b] = 0;   // for the candidates' histogram
+      if (tid == 0) s.n_cand = 0;
       __syncthreads();
       uint32_t off;
       const uint32_t C = waves_sum<W>(s.wred[0], &off);
@@ -472,8 +507,9 @@ __device__ __forceinline__ uint32_t block_select(SelShared& s, const uint32_t (&
           off += (uint32_t)__popcll(mk);
         }
         __syncthreads();
-        if (C <= 4 * NT) return select_candidates<NT, 4>(s, C, K, emit);
-        return select_candidates<NT, SEL_CAND_MAX / NT>(s, C, K, emit);
+        const float vlo = key_value(tlo);
+        if (C <= 4 * NT) return select_candidates<NT, 4>(s, C, K, vmax, vlo, emit);
+        return select_candidates<NT, SEL_CAND_MAX / NT>(s, C, K, vmax, vlo, emit);
       }
     }
   }
