@@ -94,8 +94,11 @@ __device__ __forceinline__ void rescore_blocks(const FullSelArgs& a, int64_t q, 
   {
     const int f = wv + NW * (lane >> 1), bi = 2 * f + (lane & 1);
     const int32_t blk = ((lane >> 1) < n_mine && bi < n) ? list[bi] : -1;
-    const int rem = (int)nv - 8 * blk;
-    my_cnt = blk < 0 ? 0 : (rem <= 0 ? 0 : (rem >= 8 ? 8 : rem));
+    // a block past the visible entries (or any id outside them) has no
+    // visible entry; the test comes before the multiply, so 8 * blk <= nv
+    const bool in_range = blk >= 0 && blk <= ((int)nv >> 3);
+    const int rem = in_range ? (int)nv - 8 * blk : 0;
+    my_cnt = rem <= 0 ? 0 : (rem >= 8 ? 8 : rem);
     my_blkc = my_cnt > 0 ? blk : 0;
   }
   const int lrow_k = lane >> 3;
