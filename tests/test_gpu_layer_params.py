@@ -77,13 +77,15 @@ def test_full_layer_sizes(n_ent, top_k, n_pool, build_pool):
 
 
 # A decode-sized batch with more than 2^22 scores (2 sequences x 64 queries x
-# 45,000 entries): the Full layer's selection runs split, the chosen blocks
-# rescored by several blocks per query and the Top-K taken by the block that
-# draws the query's last ticket.  Every query: pool bit-exact, Top-K set,
-# attention on the GPU's own selection.
-@pytest.mark.parametrize("keys", ["normal", "few"])
-def test_full_layer_split_selection(keys):
-    n_seq, qps, n_ent, top_k, n_pool = 2, 64, 45000, 512, 2048
+# 45,000 entries): the Full layer's selection runs split -- the pool and the
+# best blocks selected by two blocks per query (one without a pool), the
+# chosen blocks rescored by several blocks per query and the Top-K taken by
+# the block that draws the query's last ticket.  Every query: pool
+# bit-exact, Top-K set, attention on the GPU's own selection.
+@pytest.mark.parametrize("keys,build_pool", [("normal", True), ("few", True), ("normal", False)])
+def test_full_layer_split_selection(keys, build_pool):
+    n_seq, qps, n_ent, top_k = 2, 64, 45000, 512
+    n_pool = 2048 if build_pool else top_k
     Q, win_cap = n_seq * qps, 128 + qps
     rng = np.random.default_rng(4242 + len(keys))
     codes = rng.integers(0, 256, (n_seq, n_ent, 256)).astype(np.uint8)
@@ -100,22 +102,24 @@ def test_full_layer_split_selection(keys):
     pos = np.array([4 * n_ent - qps + (i % qps) for i in range(Q)], np.int32)
     idx = torch.empty((Q, top_k), dtype=torch.int32, device=DEV)
     out = torch.empty((Q, 16, 512), dtype=torch.float32, device=DEV)
-    pool = torch.empty((Q, n_pool), dtype=torch.int32, device=DEV)
+    pool = torch.empty((Q, n_pool), dtype=torch.int32, device=DEV) if build_pool else None
     call = ops.LayerCall(ops.MODE_FULL, codes=t_(codes), scales=t_(scales), k_fp8=t_(k8), win=t_(win),
                          q_pos=t_(pos), q_attn=t_(q_attn), idx=idx, out=out, n_seq=n_seq, q_per_seq=qps,
-                         n_entries=n_ent, q_idx=t_(q8), w_idx=t_(w), pool_blocks=pool, build_pool=True,
+                         n_entries=n_ent, q_idx=t_(q8), w_idx=t_(w), pool_blocks=pool, build_pool=build_pool,
                          top_k=top_k, n_pool_blocks=n_pool)
     call()
     torch.cuda.synchronize()
-    gi, go, gp = np_(idx), np_(out), np_(pool)
+    gi, go = np_(idx), np_(out)
+    gp = np_(pool) if build_pool else None
     kv = [formats.e4m3_decode(k8[s]) for s in range(n_seq)]
     for qi in range(Q):
         s = qi // qps
         wp = oracle.window_positions(pos[qi])
         ref = oracle.layer_full(codes[s], scales[s], k8[s], q8[qi], w[qi], q_attn[qi], pos[qi],
-                                win[s, wp % win_cap], SM, build_pool=True, k=top_k, n_blocks=n_pool,
+                                win[s, wp % win_cap], SM, build_pool=build_pool, k=top_k, n_blocks=n_pool,
                                 n_entries=n_ent, k_values=kv[s], attend=False)
-        assert np.array_equal(gp[qi], ref.pool), qi
+        if build_pool:
+            assert np.array_equal(gp[qi], ref.pool), qi
         if check_topk_set(gi[qi], ref.scores, ref.idx, top_k) == 0:
             assert np.array_equal(np.sort(gi[qi]), np.sort(ref.idx)), qi
         if qi % 8 == 0:
