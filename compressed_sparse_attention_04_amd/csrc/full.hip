@@ -351,6 +351,26 @@ __global__ __launch_bounds__(FR_THREADS) void full_rescore_kernel(FullSelArgs a)
   for (int j = (int)n_sel + tid; j < K; j += FR_THREADS) a.idx[q * K + j] = -1;
 }
 
+// Block maxima per thread: the fewest of 4, 8, 16, 24, 32 that hold nblk (a
+// row's padding slots still cost every per-key step of the selection).
+static int fs_keys_per_thread(int64_t nblk, int nt) {
+  const int per[5] = {4, 8, 16, 24, 32};
+  for (int i = 0; i < 4; ++i)
+    if ((int64_t)nt * per[i] >= nblk) return per[i];
+  return 32;
+}
+
+template <int NT, int PER2, int KMAX>
+void launch_full_select_per(int per, dim3 grid, hipStream_t st, const FullSelArgs& a) {
+  switch (per) {
+    case 4: hipLaunchKernelGGL((full_select_kernel<NT, 4, PER2, KMAX>), grid, dim3(NT), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((full_select_kernel<NT, 8, PER2, KMAX>), grid, dim3(NT), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((full_select_kernel<NT, 16, PER2, KMAX>), grid, dim3(NT), 0, st, a); break;
+    case 24: hipLaunchKernelGGL((full_select_kernel<NT, 24, PER2, KMAX>), grid, dim3(NT), 0, st, a); break;
+    default: hipLaunchKernelGGL((full_select_kernel<NT, 32, PER2, KMAX>), grid, dim3(NT), 0, st, a); break;
+  }
+}
+
 bool full_select_supported(int64_t nblk, int32_t nb, int32_t k) {
   return nblk <= SEL_CHUNK_MAX && nb <= SEL_POOL_MAX && k <= FS_KMAX && nb >= k;
 }
@@ -380,15 +400,13 @@ hipError_t launch_full_select(const float* block_max, int64_t nblk, int64_t Q, i
   // many queries: 512-thread blocks, two per compute unit (top_k <= 512,
   // nblk <= 16,384); a few queries: 1,024 threads, the shortest block
   if (Q >= 512 && k <= 512 && nblk <= 512 * 32) {
-    hipLaunchKernelGGL((full_select_kernel<512, 32, 8, 512>), grid, dim3(512), 0, st, a);
+    launch_full_select_per<512, 8, 512>(fs_keys_per_thread(nblk, 512), grid, st, a);
     return hipGetLastError();
   }
-  const dim3 blk(FS_THREADS);
-  const bool big1 = nblk > FS_THREADS * 16, big2 = 8 * (int64_t)k > FS_THREADS * 4;
-  if (!big1 && !big2) hipLaunchKernelGGL((full_select_kernel<FS_THREADS, 16, 4, FS_KMAX>), grid, blk, 0, st, a);
-  else if (!big1) hipLaunchKernelGGL((full_select_kernel<FS_THREADS, 16, 8, FS_KMAX>), grid, blk, 0, st, a);
-  else if (!big2) hipLaunchKernelGGL((full_select_kernel<FS_THREADS, 32, 4, FS_KMAX>), grid, blk, 0, st, a);
-  else hipLaunchKernelGGL((full_select_kernel<FS_THREADS, 32, 8, FS_KMAX>), grid, blk, 0, st, a);
+  if (8 * (int64_t)k <= FS_THREADS * 4)
+    launch_full_select_per<FS_THREADS, 4, FS_KMAX>(fs_keys_per_thread(nblk, FS_THREADS), grid, st, a);
+  else
+    launch_full_select_per<FS_THREADS, 8, FS_KMAX>(fs_keys_per_thread(nblk, FS_THREADS), grid, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split_ws) return e;
   const dim3 g2((unsigned)R, (unsigned)Q);

@@ -444,7 +444,7 @@ __device__ __forceinline__ uint32_t block_select(SelShared& s, const uint32_t (&
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       nv_w += (uint32_t)__popcll(__ballot(key[u] != 0));
-      smp = (u == (lane & (PER - 1))) ? key[u] : smp;
+      smp = (u == lane % PER) ? key[u] : smp;
       kmx = key[u] > kmx ? key[u] : kmx;
     }
     kmx = wave_reduce<0>(kmx);
