@@ -167,10 +167,11 @@ def time_kernel(fn, reps):
 # fits it (at most 32,768 blocks, a pool of at most 4,096 blocks, top_k at
 # most 1,024 and no larger than the pool).  That kernel rescores the best
 # blocks, so the dense scan writes block maxima only -- except for decode
-# batches with at most 2^22 scores (fewer than 512 queries), where the scan
-# also writes every score and the selection gathers the best blocks' scores.
+# batches (fewer than 512 queries) with at most 2^22 scores and prefill
+# chunks with at most 2^29, where the scan also writes every score and the
+# selection gathers the best blocks' scores.
 FUSED_MAX_BLOCKS, FUSED_MAX_POOL, FUSED_MAX_K = 32768, 4096, 1024
-GATHER_MAX_QUERIES, GATHER_MAX_SCORES = 512, 1 << 22
+GATHER_DECODE_QUERIES, GATHER_DECODE_SCORES, GATHER_PREFILL_SCORES = 512, 1 << 22, 1 << 29
 
 
 def dense_score_call(wl, st):
@@ -185,7 +186,8 @@ def dense_score_call(wl, st):
     nblk = (nc + 7) // 8
     nb = W.POOL_BLOCKS if cfg.build_pool else W.TOP_K
     fused = nblk <= FUSED_MAX_BLOCKS and nb <= FUSED_MAX_POOL and W.TOP_K <= FUSED_MAX_K and nb >= W.TOP_K
-    gather = fused and Q < GATHER_MAX_QUERIES and Q * nc <= GATHER_MAX_SCORES
+    gather = fused and ((Q < GATHER_DECODE_QUERIES and Q * nc <= GATHER_DECODE_SCORES) or
+                        (Q >= GATHER_DECODE_QUERIES and Q * nc <= GATHER_PREFILL_SCORES))
     scores = torch.empty((Q, nc), dtype=torch.float32, device="cuda") if (gather or not fused) else None
     bm = torch.empty((Q, nblk), dtype=torch.float32, device="cuda") if (fused or cfg.build_pool) else None
     lib = ops._lib.load()

@@ -89,15 +89,20 @@ LayerPlan plan_layer(int32_t mode, const csa_layer_args* a) {
     const int32_t nb = a->build_pool ? a->n_pool_blocks : a->top_k;
     p.nblk = (p.ncols + 7) / 8;
     p.fused_full = mode == CSA_MODE_FULL && full_select_supported(p.nblk, nb, a->top_k);
-    // Small decode batches: the scan also writes every score and the fused
-    // selection gathers the chosen blocks' scores, instead of one block per
-    // query gathering and rescoring their 512 KiB of keys (~17 us, latency
-    // bound on a few compute units).  The score stores are 64-byte pieces
-    // that cost the scan far more than their bytes (32 x 1M entries: +28 us
-    // against -12 us of selection; 64 x 128K: -9 us per step), so only
-    // batches with at most 2^22 scores take this path; many queries (prefill)
-    // keep the rescoring, spread over the GPU.
-    p.fused_scores = p.fused_full && p.Q < 512 && p.Q * p.ncols <= ((int64_t)1 << 22);
+    // The scan can also write every score, so that the fused selection
+    // gathers the chosen blocks' scores instead of rescoring their 512 KiB
+    // of keys per query.  Small decode batches: one block per query
+    // rescoring is ~17 us of latency, but the score stores are 64-byte
+    // pieces that cost the HBM-bound decode scan far more than their bytes
+    // (32 x 1M entries: +28 us against -12 us of selection; 64 x 128K: -9 us
+    // per step), so only batches with at most 2^22 scores take this path.
+    // Prefill chunks: the MFMA-bound tile scan absorbs the stores, and the
+    // rescoring re-reads 512 KiB of keys per query (2,048 queries at 32K:
+    // step 0.352 -> 0.303 ms; 4,096 at 256K, 1.1 GB of scores: 2.918 ->
+    // 2.895 ms), so chunks with at most 2^29 scores (2 GiB of workspace)
+    // take it too.
+    p.fused_scores = p.fused_full && ((p.Q < 512 && p.Q * p.ncols <= ((int64_t)1 << 22)) ||
+                                      (p.Q >= 512 && p.Q * p.ncols <= ((int64_t)1 << 29)));
     // The other decode batches rescore the chosen blocks in a second kernel
     // with several blocks per query (one block per query spends ~17 us
     // gathering a query's 512 KiB of keys).
