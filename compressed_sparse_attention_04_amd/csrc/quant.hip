@@ -166,11 +166,12 @@ __global__ __launch_bounds__(256) void compress_gemm_kernel(const float* __restr
   const int wr = (wave >> 1) * 16;          // wave's row offset in the tile
   const int wc = (wave & 1) * 32;           // wave's column offset
   f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
-  for (int k0 = kbeg; k0 < kend; k0 += CG_BK) {
-    float4 av = a_src ? *reinterpret_cast<const float4*>(a_src + k0 + a_k4)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  // chunk k0's A and B values in registers; the next chunk's loads are
+  // issued before this chunk's products, so they overlap them
+  float4 av, bv[2];
+  auto load_chunk = [&](int k0) {
+    av = a_src ? *reinterpret_cast<const float4*>(a_src + k0 + a_k4) : make_float4(0.f, 0.f, 0.f, 0.f);
     const int ti = k0 / D, c0 = k0 % D;     // token slot and channel of this chunk
-    float4 bv[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       int idx = tid + 256 * u;
@@ -178,7 +179,10 @@ __global__ __launch_bounds__(256) void compress_gemm_kernel(const float* __restr
       bv[u] = *reinterpret_cast<const float4*>(w + (int64_t)ti * D * D + (int64_t)(o0 + row) * D +
                                                c0 + k4);
     }
-    __syncthreads();
+  };
+  load_chunk(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += CG_BK) {
+    __syncthreads();   // the previous chunk's products have read the tiles
     As[a_row][a_k4] = av.x; As[a_row][a_k4 + 1] = av.y;
     As[a_row][a_k4 + 2] = av.z; As[a_row][a_k4 + 3] = av.w;
 #pragma unroll
@@ -189,6 +193,7 @@ __global__ __launch_bounds__(256) void compress_gemm_kernel(const float* __restr
       Bs[row][k4 + 2] = bv[u].z; Bs[row][k4 + 3] = bv[u].w;
     }
     __syncthreads();
+    if (k0 + CG_BK < kend) load_chunk(k0 + CG_BK);
 #pragma unroll
     for (int kk = 0; kk < CG_BK; kk += 4) {
       double a = As[wr + (lane & 15)][kk + (lane >> 4)];
