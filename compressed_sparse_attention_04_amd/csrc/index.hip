@@ -364,33 +364,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int fr = tid >> 7, h = (tid >> 6) & 1, li = tid & 63;
   const int n_row = 8 * h + (li >> 3);
   const int chunk = stage_chunk(li, h);
+  constexpr int N_ROUNDS = ST_COLS / ST_ROUND;
+  static_assert(N_ROUNDS % 2 == 0, "rounds go in pairs (two register sets)");
+  // Key bytes through a view of the sequence's first nc rows: a column at or
+  // past nc, or a round past the block's last, reads past the view and gets
+  // zeros.  The loads are unconditional, so the compiler counts the memory
+  // operations in flight: a round waits only for the key loads issued a
+  // round earlier, never for the score stores issued since.
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nc * ID, 0x00020000);
   auto load_round = [&](int r, int sub) {
     const int col = c0 + ST_ROUND * r + 32 * sub + 16 * fr + n_row;
-    return col < nc ? *reinterpret_cast<const uint4*>(kbase + (int64_t)col * ID + 16 * chunk)
-                    : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t off = (r < N_ROUNDS && col < nc) ? (uint32_t)col * ID + 16u * (uint32_t)chunk : OOB;
+    const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+    return make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
   };
-  constexpr int N_ROUNDS = ST_COLS / ST_ROUND;
-  uint4 nxt[2];
-  stage[0][fr][64 * h + li] = load_round(0, 0);
-  stage[0][2 + fr][64 * h + li] = load_round(0, 1);
-  nxt[0] = load_round(1, 0);
-  nxt[1] = load_round(1, 1);
-  for (int r = 0; r < N_ROUNDS; ++r) {
+  // Round r: the keys of round r + 1 (held) go to the other staging buffer
+  // after the loads of round r + 2 (into spare) are issued, then the round's
+  // fragments are computed from buffer r & 1.
+  auto round = [&](int r, uint4 (&held)[2], uint4 (&spare)[2]) {
     __syncthreads();   // round r is in buffer r & 1; the other buffer's readers are done
-    if (r + 1 < N_ROUNDS) {
-      stage[(r + 1) & 1][fr][64 * h + li] = nxt[0];
-      stage[(r + 1) & 1][2 + fr][64 * h + li] = nxt[1];
-    }
-    if (r + 2 < N_ROUNDS) {
-      nxt[0] = load_round(r + 2, 0);
-      nxt[1] = load_round(r + 2, 1);
-    }
+    spare[0] = load_round(r + 2, 0);
+    spare[1] = load_round(r + 2, 1);
+    stage[(r + 1) & 1][fr][64 * h + li] = held[0];
+    stage[(r + 1) & 1][2 + fr][64 * h + li] = held[1];
     // Each key fragment against the wave's 8 query pairs: 8 independent
     // accumulators with the k-steps interleaved across them (a chain of
     // dependent MFMAs on one accumulator would wait on each result), then
     // the epilogues, two query pairs per cross-lane swap.
     const int rbase = c0 + ST_ROUND * r;
-    if (rbase >= nc) continue;   // uniform; the round's barrier above is shared
+    if (rbase >= nc) return;   // uniform: nothing of this round is a column
 #pragma unroll
     for (int f2 = 0; f2 < ST_FR; ++f2) {
       const int cbase = rbase + 16 * f2;
@@ -423,6 +426,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score_max8(v[p])), brs[p], vo_b, 0, 0);
       }
     }
+  };
+  uint4 ra[2], rb[2];
+  stage[0][fr][64 * h + li] = load_round(0, 0);
+  stage[0][2 + fr][64 * h + li] = load_round(0, 1);
+  ra[0] = load_round(1, 0);
+  ra[1] = load_round(1, 1);
+  for (int r = 0; r < N_ROUNDS; r += 2) {
+    round(r, ra, rb);
+    round(r + 1, rb, ra);
   }
 }
 
