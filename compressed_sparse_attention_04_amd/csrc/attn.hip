@@ -24,11 +24,11 @@
 //   3. online softmax in float32 (log2 domain; every wave computes the same);
 //   4. P V on the matrix cores with P split the same way: P_hi V + P_lo V
 //      (16x16x16, exact products, float32 accumulation), so the weights
-//      enter at ~2^-22 relative; the denominator sums the same split
-//      weights.  The
-//      fp16 key slices go through the wave's own LDS rows so that each lane
-//      gathers 4 keys of one channel (output channel of N-tile n in lane
-//      column c is 128 w + 8 c + n: 16 contiguous bytes per key).
+//      enter at ~2^-22 relative (the denominator sums the float32 weights,
+//      which the two halves match to that order).  The fp16 key slices go
+//      through the wave's own LDS rows,
+//      and a transposed LDS read gives each lane 4 keys of one channel
+//      (N-tile n, lane column c: channel 128 w + 16 n + c).
 // Key bytes are read through buffer views of the query's rows: an absent
 // key (a -1 id, an id past the cache, a window position before 0, padding)
 // reads past the view and gets zeros, so no load sits under a branch: every
@@ -203,6 +203,16 @@ __device__ __forceinline__ f16x8 key_slice(const RawKey& r, int s) {
 // unnormalized weights stay <= 2^8 and O is rarely rescaled.
 constexpr float AT_RESCALE = 8.0f;
 
+// Four fp16 values of one channel across four key rows in LDS: lanes
+// 4 r + c of each 16-lane group point at 8 bytes (4 channels) of row r, and
+// lane i of the group receives channel i of rows 0 .. 3 (gfx950's
+// ds_read_b64_tr_b16).
+__device__ __forceinline__ f16x4 lds_read_tr16(const uint8_t* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(f16x4, v);
+}
+
 // 2^x on the transcendental unit alone (v_exp_f32, ~1 ulp): the loop's
 // arguments are <= AT_RESCALE or -inf (-> 0), and a weight that underflows to
 // 0 is below anything the fp32 sums could hold, so the denormal range
@@ -224,7 +234,7 @@ struct AttnLds {
 };
 
 // Running state of one wave: O of heads 4 g + r (rows) x channels
-// 128 w + 8 j + n (acc_o[n][r]); max and sum of head j.
+// 128 w + 16 n + j (acc_o[n][r]); max and sum of head j.
 struct AttnState {
   f32x4 acc_o[8];
   float m_run, l_run;
@@ -321,43 +331,30 @@ __device__ __forceinline__ void attn_tile(int tk, AttnState& st, const RawKey& c
   }
   if (first || move) st.m_run = mx;
   const float base = (st.m_run == -__builtin_huge_valf()) ? 0.f : st.m_run;
-  // A operands of P V: P_hi and P_lo of keys 4g..4g+3 (head j); the sum
-  // takes the same two halves
+  // A operands of P V: P_hi and P_lo of keys 4g..4g+3 (head j).  hi + lo
+  // holds each weight to ~2^-22, so the sum takes the float32 weights.
   f16x4 ph, pl;
   float psum = 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float pr = exp2_loop(x[r] - base);
     const _Float16 h = (_Float16)pr;
-    const _Float16 l = (_Float16)(pr - (float)h);
     ph[r] = h;
-    pl[r] = l;
-    psum += (float)h + (float)l;
+    pl[r] = (_Float16)(pr - (float)h);
+    psum += pr;
   }
   st.l_run += psum;   // this lane's keys only; the four lanes of head j are summed at the end
 
-  // ---- 4. P V: keys 4g .. 4g+3 of channels 8j .. 8j+7 from LDS -------------
-  uint4 v[4];
+  // ---- 4. P V: B operands straight from the key rows in LDS ----------------
+  // A transposed read (ds_read_b64_tr_b16) hands lane (i, g) channel
+  // 16 n + i of keys 4g .. 4g+3 when lanes 4 r + c of its 16-lane group point
+  // at key 4g + r, channels 16 n + 4c .. + 3 (8 bytes of one row).
+  const uint8_t* vrow = krow + (4 * g + (j >> 2)) * AT_KPITCH + 8 * (j & 3);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) v[kk] = *reinterpret_cast<const uint4*>(krow + (4 * g + kk) * AT_KPITCH + 16 * j);
-  const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
-  const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
-  const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
-  const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // channel pair (2i, 2i+1) of the 8: N-tiles 2i and 2i+1, each against the
-    // hi and then the lo weights
-    const f16x2 a0 = bits_f16x2(__builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u));
-    const f16x2 a1 = bits_f16x2(__builtin_amdgcn_perm(w3[i], w2[i], 0x05040100u));
-    const f16x2 b0 = bits_f16x2(__builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u));
-    const f16x2 b1 = bits_f16x2(__builtin_amdgcn_perm(w3[i], w2[i], 0x07060302u));
-    const f16x4 blo = {a0[0], a0[1], a1[0], a1[1]};
-    const f16x4 bhi = {b0[0], b0[1], b1[0], b1[1]};
-    st.acc_o[2 * i] = mfma_f16_16x16x16(ph, blo, st.acc_o[2 * i]);
-    st.acc_o[2 * i + 1] = mfma_f16_16x16x16(ph, bhi, st.acc_o[2 * i + 1]);
-    st.acc_o[2 * i] = mfma_f16_16x16x16(pl, blo, st.acc_o[2 * i]);
-    st.acc_o[2 * i + 1] = mfma_f16_16x16x16(pl, bhi, st.acc_o[2 * i + 1]);
+  for (int n = 0; n < 8; ++n) {
+    const f16x4 b = lds_read_tr16(vrow + 32 * n);
+    st.acc_o[n] = mfma_f16_16x16x16(ph, b, st.acc_o[n]);
+    st.acc_o[n] = mfma_f16_16x16x16(pl, b, st.acc_o[n]);
   }
 }
 
@@ -437,19 +434,17 @@ __device__ __forceinline__ void attn_finish(Lds& lds, AttnState& st, const AttnA
     for (int r = 0; r < 4; ++r) inv[r] = lsum[r] > 0.f ? 1.0f / lsum[r] : 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float4* dst = reinterpret_cast<float4*>(a.out + (qi * HEADS + 4 * g + r) * D + AT_QCH * w + 8 * j);
-      const f32x4* o = st.acc_o;
-      dst[0] = make_float4(o[0][r] * inv[r], o[1][r] * inv[r], o[2][r] * inv[r], o[3][r] * inv[r]);
-      dst[1] = make_float4(o[4][r] * inv[r], o[5][r] * inv[r], o[6][r] * inv[r], o[7][r] * inv[r]);
+      float* dst = a.out + (qi * HEADS + 4 * g + r) * D + AT_QCH * w + j;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) dst[16 * n] = st.acc_o[n][r] * inv[r];
     }
   } else {
     const int64_t ps = qi * a.n_splits + split;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float4* dst = reinterpret_cast<float4*>(a.part_o + (ps * HEADS + 4 * g + r) * D + AT_QCH * w + 8 * j);
-      const f32x4* o = st.acc_o;
-      dst[0] = make_float4(o[0][r], o[1][r], o[2][r], o[3][r]);
-      dst[1] = make_float4(o[4][r], o[5][r], o[6][r], o[7][r]);
+      float* dst = a.part_o + (ps * HEADS + 4 * g + r) * D + AT_QCH * w + j;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) dst[16 * n] = st.acc_o[n][r];
     }
     if (w == 0 && lane < 16) {
       a.part_ml[(ps * 2 + 0) * HEADS + j] = st.m_run;
