@@ -213,6 +213,17 @@ __device__ __forceinline__ f16x4 lds_read_tr16(const uint8_t* p) {
   return __builtin_bit_cast(f16x4, v);
 }
 
+// fp16(p0 - hi.x) | fp16(p1 - hi.y) << 16: the lo halves of a hi / lo split
+// of two weights whose hi halves are hi, one mixed-precision FMA each
+// (v_fma_mix*: source 0 is an fp16 half of hi, the others float32).
+__device__ __forceinline__ uint32_t split_lo(f16x2 hi, float p0, float p1) {
+  const uint32_t h = __builtin_bit_cast(uint32_t, hi);
+  uint32_t lo;
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(lo) : "v"(h), "v"(p0));
+  asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(lo) : "v"(h), "v"(p1));
+  return lo;
+}
+
 // 2^x on the transcendental unit alone (v_exp_f32, ~1 ulp): the loop's
 // arguments are <= AT_RESCALE or -inf (-> 0), and a weight that underflows to
 // 0 is below anything the fp32 sums could hold, so the denormal range
@@ -313,7 +324,7 @@ __device__ __forceinline__ void attn_tile(int tk, AttnState& st, const RawKey& c
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[r] = ((vmask >> (4 * g + r)) & 1u) ? x[r] : -__builtin_huge_valf();
   }
-  float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  float mx = fmax_nn(fmax_nn(x[0], x[1]), fmax_nn(x[2], x[3]));
   mx = max_xor32(max_xor16(mx));
   const bool first = (st.m_run == -__builtin_huge_valf());
   const bool move = !first && (mx > st.m_run + AT_RESCALE);
@@ -333,16 +344,16 @@ __device__ __forceinline__ void attn_tile(int tk, AttnState& st, const RawKey& c
   const float base = (st.m_run == -__builtin_huge_valf()) ? 0.f : st.m_run;
   // A operands of P V: P_hi and P_lo of keys 4g..4g+3 (head j).  hi + lo
   // holds each weight to ~2^-22, so the sum takes the float32 weights.
-  f16x4 ph, pl;
+  float pr[4];
   float psum = 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float pr = exp2_loop(x[r] - base);
-    const _Float16 h = (_Float16)pr;
-    ph[r] = h;
-    pl[r] = (_Float16)(pr - (float)h);
-    psum += pr;
+    pr[r] = exp2_loop(x[r] - base);
+    psum += pr[r];
   }
+  const f16x2 h01 = {(_Float16)pr[0], (_Float16)pr[1]}, h23 = {(_Float16)pr[2], (_Float16)pr[3]};
+  const f16x4 ph = {h01[0], h01[1], h23[0], h23[1]};
+  const f16x4 pl = __builtin_bit_cast(f16x4, make_uint2(split_lo(h01, pr[0], pr[1]), split_lo(h23, pr[2], pr[3])));
   st.l_run += psum;   // this lane's keys only; the four lanes of head j are summed at the end
 
   // ---- 4. P V: B operands straight from the key rows in LDS ----------------

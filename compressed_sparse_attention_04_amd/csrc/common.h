@@ -157,13 +157,17 @@ __device__ __forceinline__ float sum_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// max(a, b) for non-NaN floats as gfx950's v_maximum3_f32 (IEEE maximum,
+// NaN-propagating): fmaxf would first quiet both inputs (two more
+// instructions).
+__device__ __forceinline__ float fmax_nn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float max_xor16(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 // Max over each aligned group of 8 lanes, in every lane of the group (DPP:
 // quad_perm xor 1, xor 2, then row_half_mirror, which pairs the two quads).
