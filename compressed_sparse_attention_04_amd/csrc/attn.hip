@@ -151,15 +151,18 @@ __device__ __forceinline__ uint4 or4(uint4 x, uint4 y) {
 }
 __device__ __forceinline__ RawKey load_slot(const QueryView& v, const AttnArgs& a, int t, bool live, int j, int g,
                                             int w, int32_t id) {
-  const int slot = t * AT_TILE + j;
-  const bool ent = live && slot < a.k && id >= 0 && id < a.kv_rows;
-  const int wi = slot - a.k;
-  const bool win = live && wi >= 0 && wi < NWIN && v.p - (NWIN - 1) + wi >= 0;
-  int row = v.wbase + wi;
-  row = row >= v.win_cap ? row - v.win_cap : row;
+  // 32-bit throughout: kv_rows < 2^23, win_cap < 2^22.  An entry slot has
+  // wi < 0; the unsigned compares take id < 0 and wi < 0 as out of range.
+  const int wi = t * AT_TILE + j - a.k;
+  const bool ent = live && wi < 0 && (uint32_t)id < (uint32_t)a.kv_rows;
+  const bool win = live && (uint32_t)wi < (uint32_t)NWIN && wi >= (NWIN - 1) - v.p;
+  // ring row of window token wi: wbase + wi < 2 win_cap, and when it is
+  // below win_cap the wrapped difference is the larger
+  const uint32_t row0 = (uint32_t)(v.wbase + wi);
+  const uint32_t row = __builtin_elementwise_min(row0, row0 - (uint32_t)v.win_cap);
   const uint32_t oc = ent ? (uint32_t)id * CODE_BYTES + 64u * w + 16u * g : AT_OOB;
   const uint32_t os = ent ? (uint32_t)id * SCALE_BYTES + 8u * w + 2u * g : AT_OOB;
-  const uint32_t ow = win ? (uint32_t)row * D + AT_QCH * w + 32u * g : AT_OOB;
+  const uint32_t ow = win ? row * D + AT_QCH * w + 32u * g : AT_OOB;
   const uint4 c = load_b128(v.codes, oc);
   const uint32_t sc = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(v.scales, os, 0, 0);
   const uint4 wa = load_b128(v.win, ow), wb = load_b128(v.win, ow + 16u);
@@ -286,15 +289,15 @@ template <int TK>
 __device__ __forceinline__ f32x4 tile_qk(const RawKey& cur, const f16x8 (&qh)[4], const f16x8 (&ql)[4],
                                          uint8_t* krow, int j, int g) {
   __builtin_amdgcn_wave_barrier();   // the previous tile's LDS reads come first
-  f32x4 sh = {0.f, 0.f, 0.f, 0.f}, sl = {0.f, 0.f, 0.f, 0.f};
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const f16x8 av = key_slice<TK>(cur, s);
     *reinterpret_cast<f16x8*>(krow + j * AT_KPITCH + 64 * g + 16 * s) = av;
-    sh = mfma_f16_16x16x32(av, qh[s], sh);
-    sl = mfma_f16_16x16x32(av, ql[s], sl);
+    sc = mfma_f16_16x16x32(av, qh[s], sc);
+    sc = mfma_f16_16x16x32(av, ql[s], sc);
   }
-  return f32x4{sh[0] + sl[0], sh[1] + sl[1], sh[2] + sl[2], sh[3] + sl[3]};
+  return sc;
 }
 
 // Steps 2-4 of one tile for this wave.  krow: the wave's LDS key rows; sbuf:
@@ -345,12 +348,9 @@ __device__ __forceinline__ void attn_tile(int tk, AttnState& st, const RawKey& c
   // A operands of P V: P_hi and P_lo of keys 4g..4g+3 (head j).  hi + lo
   // holds each weight to ~2^-22, so the sum takes the float32 weights.
   float pr[4];
-  float psum = 0.f;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    pr[r] = exp2_loop(x[r] - base);
-    psum += pr[r];
-  }
+  for (int r = 0; r < 4; ++r) pr[r] = exp2_loop(x[r] - base);
+  const float psum = (pr[0] + pr[1]) + (pr[2] + pr[3]);
   const f16x2 h01 = {(_Float16)pr[0], (_Float16)pr[1]}, h23 = {(_Float16)pr[2], (_Float16)pr[3]};
   const f16x4 ph = {h01[0], h01[1], h23[0], h23[1]};
   const f16x4 pl = __builtin_bit_cast(f16x4, make_uint2(split_lo(h01, pr[0], pr[1]), split_lo(h23, pr[2], pr[3])));
