@@ -542,7 +542,7 @@ struct PairLds {
   f32x4 s[NP][AT_WAVES][2][64];   // partial S^T fragments (tile 0, tile 1) per wave
   f16x8 p[NP][2][64];             // P of every pair as A operands: hi, lo
   float pmax[NP][HEADS];          // head maxima of each pair
-  float psum[NP][HEADS];          // head sums of each pair's P (hi + lo)
+  float psum[NP][HEADS];          // head sums of each pair's weights
 };
 
 // Row i < 16 of QK tile h of a pair is pair key (i >> 2) + 4 (2 (i & 3) + h).
@@ -730,14 +730,14 @@ __global__ __launch_bounds__(AT_THREADS) void attn_pair_kernel(AttnArgs a) {
   for (int p = 0; p < NP; ++p) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      f32x4 sh = {0.f, 0.f, 0.f, 0.f}, sl = {0.f, 0.f, 0.f, 0.f};
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const f16x8 av = p < E ? entry_slice(rk[p][h], s) : window_slice(rk[p][h], s);
-        sh = mfma_f16_16x16x32(av, qh[s], sh);
-        sl = mfma_f16_16x16x32(av, ql[s], sl);
+        sc = mfma_f16_16x16x32(av, qh[s], sc);
+        sc = mfma_f16_16x16x32(av, ql[s], sc);
       }
-      lds.s[p][w][h][lane] = f32x4{sh[0] + sl[0], sh[1] + sl[1], sh[2] + sl[2], sh[3] + sl[3]};
+      lds.s[p][w][h][lane] = sc;
     }
   }
   __syncthreads();
@@ -765,12 +765,10 @@ __global__ __launch_bounds__(AT_THREADS) void attn_pair_kernel(AttnArgs a) {
       }
       // x[m][kk] (tile kk >> 2, row 4 g + (kk & 3)) is pair key
       // pair_v_key(g, kk), whose presence is bit kk of the pair's vbits
-      float mx = -__builtin_huge_valf();
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        x[m][kk] = ((vb_p >> kk) & 1u) ? x[m][kk] : -__builtin_huge_valf();
-        mx = fmaxf(mx, x[m][kk]);
-      }
+      for (int kk = 0; kk < 8; ++kk) x[m][kk] = ((vb_p >> kk) & 1u) ? x[m][kk] : -__builtin_huge_valf();
+      float mx = fmax_nn(fmax_nn(fmax_nn(x[m][0], x[m][1]), fmax_nn(x[m][2], x[m][3])),
+                         fmax_nn(fmax_nn(x[m][4], x[m][5]), fmax_nn(x[m][6], x[m][7])));
       mx = max_xor32(max_xor16(mx));
       if (g == 0) lds.pmax[p][j] = mx;
     }
@@ -780,23 +778,26 @@ __global__ __launch_bounds__(AT_THREADS) void attn_pair_kernel(AttnArgs a) {
   // ---- 4. P of the wave's pairs against the block's head maxima --------------------
   float M = lds.pmax[0][j];
 #pragma unroll
-  for (int p = 1; p < NP; ++p) M = fmaxf(M, lds.pmax[p][j]);
+  for (int p = 1; p < NP; ++p) M = fmax_nn(M, lds.pmax[p][j]);
   const float base = (M == -__builtin_huge_valf()) ? 0.f : M;
 #pragma unroll
   for (int m = 0; m < MINE; ++m) {
     const int p = w + AT_WAVES * m;
     if (p < NP) {
-      f16x8 ph, pl;
-      float psum = 0.f;
+      float pr[8];   // <= 1; 0 for an absent key
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const float pr = exp2_loop(x[m][kk] - base);   // <= 1; 0 for an absent key
-        const _Float16 hv = (_Float16)pr;
-        const _Float16 lv = (_Float16)(pr - (float)hv);
-        ph[kk] = hv;
-        pl[kk] = lv;
-        psum += (float)hv + (float)lv;
+      for (int kk = 0; kk < 8; ++kk) pr[kk] = exp2_loop(x[m][kk] - base);
+      f16x2 hv[4];
+      uint32_t lv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hv[i] = f16x2{(_Float16)pr[2 * i], (_Float16)pr[2 * i + 1]};
+        lv[i] = split_lo(hv[i], pr[2 * i], pr[2 * i + 1]);
       }
+      const f16x8 ph = {hv[0][0], hv[0][1], hv[1][0], hv[1][1], hv[2][0], hv[2][1], hv[3][0], hv[3][1]};
+      const f16x8 pl = __builtin_bit_cast(f16x8, make_uint4(lv[0], lv[1], lv[2], lv[3]));
+      // the float32 weights, which P_hi + P_lo match to ~2^-22
+      float psum = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
       psum = sum_xor32(sum_xor16(psum));
       lds.p[p][0][lane] = ph;
       lds.p[p][1][lane] = pl;
@@ -830,7 +831,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_pair_kernel(AttnArgs a) {
 #pragma unroll
     for (int p = 1; p < NP; ++p) {
       L += lds.psum[p][h];
-      Mh = fmaxf(Mh, lds.pmax[p][h]);
+      Mh = fmax_nn(Mh, lds.pmax[p][h]);
     }
     lsum[r] = L;
     mrow[r] = Mh;
