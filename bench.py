@@ -174,9 +174,10 @@ FUSED_MAX_BLOCKS, FUSED_MAX_POOL, FUSED_MAX_K = 32768, 4096, 1024
 GATHER_DECODE_QUERIES, GATHER_DECODE_SCORES, GATHER_PREFILL_SCORES = 512, 1 << 22, 1 << 29
 
 
-def dense_score_call(wl, st):
+def dense_score_call(wl, st, write_scores=True):
     """The Full layer's dense indexer launch, with the step's own inputs and
-    the outputs the step's launch writes."""
+    the outputs the step's launch writes (write_scores=False: the same launch
+    with the block maxima only, which is what the scoring alone costs)."""
     import torch
     import workloads as W
     from compressed_sparse_attention_04_amd import ops
@@ -188,14 +189,18 @@ def dense_score_call(wl, st):
     fused = nblk <= FUSED_MAX_BLOCKS and nb <= FUSED_MAX_POOL and W.TOP_K <= FUSED_MAX_K and nb >= W.TOP_K
     gather = fused and ((Q < GATHER_DECODE_QUERIES and Q * nc <= GATHER_DECODE_SCORES) or
                         (Q >= GATHER_DECODE_QUERIES and Q * nc <= GATHER_PREFILL_SCORES))
-    scores = torch.empty((Q, nc), dtype=torch.float32, device="cuda") if (gather or not fused) else None
+    want = (gather or not fused) and (write_scores or not fused)
+    scores = torch.empty((Q, nc), dtype=torch.float32, device="cuda") if want else None
     bm = torch.empty((Q, nblk), dtype=torch.float32, device="cuda") if (fused or cfg.build_pool) else None
     lib = ops._lib.load()
     args = (ops._p(t["q_fp8"][li]), ops._p(t["w_idx"][li]), ops._p(t["q_pos"]), cfg.n_seq, st.q_per_seq,
             ops._p(t["k_fp8"]), t["k_fp8"].shape[1], nc, None, 0,
             None if scores is None else ops._p(scores), None if bm is None else ops._p(bm))
 
+    outs = (scores, bm)   # held by fn: the launches write them
+
     def fn():
+        assert outs is not None
         rc = lib.csa_index_score(*args, ops._stream())
         if rc:
             raise RuntimeError(lib.csa_last_error().decode())
@@ -307,6 +312,13 @@ def measure_config(cid, steps, warmup, use_graph, kernel_reps):
         res["indexer_gbps"] = per / (kms * 1e-3) / 1e9
     else:
         res["indexer_tflops"] = indexer_flops(cfg) / (kms * 1e-3) / 1e12
+        if out_bytes > cfg.n_queries * ((st.n_entries + 7) // 8) * 4:
+            # the step's launch also writes every score for the selection's
+            # gather; the block-maxima-only launch of the same kernel gives
+            # the scoring rate on its own
+            del fn
+            fn, _ = dense_score_call(wl, st, write_scores=False)
+            res["indexer_tflops_block_max_only"] = indexer_flops(cfg) / (time_kernel(fn, kernel_reps) * 1e-3) / 1e12
     del insts, runs, wl, st
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -568,6 +580,8 @@ def main():
                     "flops_per_launch": indexer_flops(cfg),
                     "avg_launch_ms": round(main_res["indexer_ms"], 4),
                     "frac_of_f8_peak": round(achieved / F8_PEAK_TFLOPS, 4)}
+        if "indexer_tflops_block_max_only" in main_res:
+            roofline["tflops_block_max_only"] = round(main_res["indexer_tflops_block_max_only"], 1)
     value, unit = main_res["tokens_per_s"], "tokens/s"
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": unit, "n_gpus": 1, "steps": args.steps,
@@ -611,6 +625,8 @@ def main():
                 e["indexer_frac_f16_peak"] = round(r["indexer_tflops"] / F16_PEAK_TFLOPS, 4)
                 e["indexer_frac_f16_probe"] = round(r["indexer_tflops"] / pk["mfma_f16_tflops"], 4)
                 e["indexer_frac_f8_peak"] = round(r["indexer_tflops"] / F8_PEAK_TFLOPS, 4)
+                if "indexer_tflops_block_max_only" in r:
+                    e["indexer_tflops_block_max_only"] = round(r["indexer_tflops_block_max_only"], 1)
             else:
                 e["indexer_gbps"] = round(r["indexer_gbps"], 1)
             sec[r["workload"]] = e

@@ -153,16 +153,26 @@ __device__ __forceinline__ RawKey load_slot(const QueryView& v, const AttnArgs& 
                                             int w, int32_t id) {
   // 32-bit throughout: kv_rows < 2^23, win_cap < 2^22.  An entry slot has
   // wi < 0; the unsigned compares take id < 0 and wi < 0 as out of range.
+  // The tile's kind is the same in every lane: a tile of entries skips the
+  // window offsets and a tile of window tokens the entry offsets (a scalar
+  // branch around arithmetic only; the loads below are unconditional).
   const int wi = t * AT_TILE + j - a.k;
-  const bool ent = live && wi < 0 && (uint32_t)id < (uint32_t)a.kv_rows;
-  const bool win = live && (uint32_t)wi < (uint32_t)NWIN && wi >= (NWIN - 1) - v.p;
-  // ring row of window token wi: wbase + wi < 2 win_cap, and when it is
-  // below win_cap the wrapped difference is the larger
-  const uint32_t row0 = (uint32_t)(v.wbase + wi);
-  const uint32_t row = __builtin_elementwise_min(row0, row0 - (uint32_t)v.win_cap);
-  const uint32_t oc = ent ? (uint32_t)id * CODE_BYTES + 64u * w + 16u * g : AT_OOB;
-  const uint32_t os = ent ? (uint32_t)id * SCALE_BYTES + 8u * w + 2u * g : AT_OOB;
-  const uint32_t ow = win ? row * D + AT_QCH * w + 32u * g : AT_OOB;
+  const int tk = tile_kind(t, a.k);
+  bool ent = false, win = false;
+  uint32_t oc = AT_OOB, os = AT_OOB, ow = AT_OOB;
+  if (tk != TK_WINDOW) {
+    ent = live && wi < 0 && (uint32_t)id < (uint32_t)a.kv_rows;
+    oc = ent ? (uint32_t)id * CODE_BYTES + 64u * w + 16u * g : AT_OOB;
+    os = ent ? (uint32_t)id * SCALE_BYTES + 8u * w + 2u * g : AT_OOB;
+  }
+  if (tk != TK_ENTRY) {
+    win = live && (uint32_t)wi < (uint32_t)NWIN && wi >= (NWIN - 1) - v.p;
+    // ring row of window token wi: wbase + wi < 2 win_cap, and when it is
+    // below win_cap the wrapped difference is the larger
+    const uint32_t row0 = (uint32_t)(v.wbase + wi);
+    const uint32_t row = __builtin_elementwise_min(row0, row0 - (uint32_t)v.win_cap);
+    ow = win ? row * D + AT_QCH * w + 32u * g : AT_OOB;
+  }
   const uint4 c = load_b128(v.codes, oc);
   const uint32_t sc = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(v.scales, os, 0, 0);
   const uint4 wa = load_b128(v.win, ow), wb = load_b128(v.win, ow + 16u);
