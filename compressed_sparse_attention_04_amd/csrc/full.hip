@@ -168,11 +168,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void fu
   const int64_t q = blockIdx.y;
   const int NB = a.NB, K = a.K;
 
-  // ---- split selection with a pool: block x = 0 selects the pool (for the
-  // Reindex layers), block x = 1 the top_k best blocks straight from all the
-  // maxima (the same blocks as the best of the pool: the pool holds the NB
-  // best blocks under the same order), so neither waits for the other.
-  if (a.top_out && NB > K) {
+  // ---- split selection with a pool (gridDim.x == 2): block x = 0 selects the
+  // pool (for the Reindex layers), block x = 1 the top_k best blocks straight
+  // from all the maxima (the same blocks as the best of the pool: the pool
+  // holds the NB best blocks under the same order), so neither waits for the
+  // other.  Block 1 then hands the blocks to full_rescore_kernel (top_out),
+  // or, when the scan wrote every score, goes on to phases B and C itself.
+  if (gridDim.x == 2) {
     const int pw = 64 * PER * wv + lane;
     uint32_t key[PER];
     load_keys<PER>(a.block_max + q * a.nblk, pw, (int)a.nblk, key);
@@ -182,18 +184,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void fu
       });
       if (a.pool_out)
         for (int j = (int)n_pool + tid; j < NB; j += NT) a.pool_out[q * NB + j] = -1;
-    } else {
+      return;
+    }
+    if (a.top_out) {
       const uint32_t n_top = block_select<NT, PER>(s, key, (uint32_t)K, [&](int p, uint32_t, uint32_t slot) {
         a.top_out[q * K + slot] = p;
       });
       for (int j = (int)n_top + tid; j < K; j += NT) a.top_out[q * K + j] = -1;
       if (tid == 0) a.ticket[q] = 0;
+      return;
     }
-    return;
-  }
-
+    const uint32_t n_top = block_select<NT, PER>(s, key, (uint32_t)K, [&](int p, uint32_t, uint32_t slot) {
+      top[slot] = p;
+    });
+    for (int j = (int)n_top + tid; j < K; j += NT) top[j] = -1;
+  } else {
   // ---- A. pool, and the top_k blocks ------------------------------------------
-  {
     const int pw = 64 * PER * wv + lane;
     const float* row = a.block_max + q * a.nblk;
     {
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void fu
     }
   }
   __syncthreads();
-  if (a.top_out) {   // split selection: the chosen blocks go to full_rescore_kernel
+  if (a.top_out) {   // (one block per query) the chosen blocks go to full_rescore_kernel
     for (int j = tid; j < K; j += NT) a.top_out[q * K + j] = top[j];
     if (tid == 0) a.ticket[q] = 0;
     return;
@@ -395,8 +401,9 @@ hipError_t launch_full_select(const float* block_max, int64_t nblk, int64_t Q, i
     a.ticket = reinterpret_cast<int32_t*>(p + full_split_top_bytes(Q, k));
     a.sc_out = reinterpret_cast<float*>(p + full_split_top_bytes(Q, k) + full_split_ticket_bytes(Q));
   }
-  // split selection with a pool: two blocks per query (pool, best blocks)
-  const dim3 grid(split_ws && nb > k ? 2 : 1, (unsigned)Q);
+  // decode batches with a pool: two blocks per query (pool, best blocks),
+  // whether the best blocks are then rescored or their scores gathered
+  const dim3 grid(nb > k && (split_ws || (scores && Q < 512)) ? 2 : 1, (unsigned)Q);
   // many queries: 512-thread blocks, two per compute unit (top_k <= 512,
   // nblk <= 16,384); a few queries: 1,024 threads, the shortest block
   if (Q >= 512 && k <= 512 && nblk <= 512 * 32) {

@@ -111,13 +111,15 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
       0x00020000);
   const int ncols_i = (int)ncols;                     // <= 8 x 65,536
   const int cw = (int)c_wave;
-  // Lanes 0-15 own output column cw + 16 f + lane of fragment f: byte offset
-  // vo0 + 64 f.  A column at or past ncols is past the view's records and its
-  // store is dropped (the range check covers the instruction's immediate
-  // offset, where the constant 64 f goes); the other lanes' offset stays past
-  // the records for every f.
-  const uint32_t vo0 = lane < 16 ? (uint32_t)(cw + lane) * 4u : OOB;
+  // The group's four fragments (64 consecutive columns) go out as one store
+  // with every lane: fragment u's scores sit in lanes 0-31 after the head
+  // sums, rows 0 and 1 take fragments 0 and 1 and one v_permlane32_swap
+  // brings fragments 2 and 3 into rows 2 and 3, so lane l holds column l.
+  static_assert(SQ_UNROLL == 4, "one store per group of four fragments");
+  const uint32_t vo0 = (uint32_t)(cw + lane) * 4u;
   auto compute_group = [&](int grp, const uint4 (&v)[SQ_UNROLL][2]) {
+    float sc[SQ_UNROLL];
+    uint64_t valid = 0;
 #pragma unroll
     for (int u = 0; u < SQ_UNROLL; ++u) {
       const int f = grp * SQ_UNROLL + u;
@@ -125,15 +127,21 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
       stage[lane] = v[u][0];
       stage[64 + lane] = v[u][1];
       __builtin_amdgcn_wave_barrier();   // stores before the transposed reads (LDS keeps wave order)
-      const f32x4 acc = frag_mma(afrag, to_frag(read_staged(stage, lane)));
-      const float sc = head_sum(acc, w4);
-      // valid when the column's offset in its pool block (lane % 8) is below
-      // that block's visible count: bit lane of a wave-uniform mask built
-      // from the two halves' counts (<= 8) on the scalar unit
+      sc[u] = head_sum(frag_mma(afrag, to_frag(read_staged(stage, lane))), w4);
+      // column c of fragment u is valid when its offset in its pool block
+      // (c % 8) is below that block's visible count: bits 16 u .. of a
+      // wave-uniform mask built from the halves' counts (<= 8) on the scalar unit
       const uint32_t m16 = ((1u << half_cnt(2 * f)) - 1u) | (((1u << half_cnt(2 * f + 1)) - 1u) << 8);
-      const float v_out = __builtin_amdgcn_inverse_ballot_w64((uint64_t)m16) ? sc : -__builtin_huge_valf();
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v_out), srs, vo0 + 64u * (uint32_t)f, 0, 0);
+      valid |= (uint64_t)m16 << (16 * u);
     }
+    const bool odd_row = (lane & 16) != 0;
+    const float v01 = odd_row ? sc[1] : sc[0], v23 = odd_row ? sc[3] : sc[2];
+    const float s64 = __uint_as_float(
+        __builtin_amdgcn_permlane32_swap(__float_as_uint(v01), __float_as_uint(v23), false, false)[0]);
+    const float v_out = __builtin_amdgcn_inverse_ballot_w64(valid) ? s64 : -__builtin_huge_valf();
+    // a column at or past ncols is past the view's records and its store is
+    // dropped (the range check covers the immediate offset, where 256 grp goes)
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v_out), srs, vo0 + 256u * (uint32_t)grp, 0, 0);
   };
   if (nv == 0) {
     // nothing visible: every column is -inf, and no key row may be read (the
@@ -219,22 +227,38 @@ __global__ __launch_bounds__(256) void score_scan_kernel(ScoreArgs a, int64_t nc
       }
     }
   };
+  // Four consecutive fragments (64 consecutive columns) go out together: the
+  // head sums leave fragment u's scores in lanes 0-31 (16-lane rows 0 and 1
+  // alike), so rows 0 and 1 take fragments u, u + 1 and one
+  // v_permlane32_swap brings fragments u + 2, u + 3 into rows 2 and 3; lane l
+  // then holds column l of the 64, and one store instruction with every lane
+  // (and one block-max step over the 64) replaces four with 16 lanes each.
+  // Fewer store instructions leave more of the memory counter to the key
+  // loads in flight.
+  static_assert(SC_GROUP % 4 == 0 && NFRAG % 4 == 0, "fragments go out in fours within a chunk");
   auto compute_group = [&](int grp, const uint4 (&v)[SC_GROUP][2]) {
+    const bool odd_row = (lane & 16) != 0;
 #pragma unroll
-    for (int u = 0; u < SC_GROUP; ++u) {
-      __builtin_amdgcn_wave_barrier();   // the previous fragment's staged reads come first
-      stage[lane] = v[u][0];
-      stage[64 + lane] = v[u][1];
-      __builtin_amdgcn_wave_barrier();   // stores before the transposed reads (LDS keeps wave order)
-      const f32x4 acc = frag_mma(afrag, to_frag(read_staged(stage, lane)));
-      const float sc = head_sum(acc, w4);
-      const int64_t col = frag_col(grp * SC_GROUP + u) + (lane & 15);
-      const float v_out = (col < ncols && col < nv) ? sc : -__builtin_huge_valf();
+    for (int u0 = 0; u0 < SC_GROUP; u0 += 4) {
+      float sc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_wave_barrier();   // the previous fragment's staged reads come first
+        stage[lane] = v[u0 + i][0];
+        stage[64 + lane] = v[u0 + i][1];
+        __builtin_amdgcn_wave_barrier();   // stores before the transposed reads (LDS keeps wave order)
+        sc[i] = head_sum(frag_mma(afrag, to_frag(read_staged(stage, lane))), w4);
+      }
+      const float v01 = odd_row ? sc[1] : sc[0], v23 = odd_row ? sc[3] : sc[2];
+      const float s64 = __uint_as_float(
+          __builtin_amdgcn_permlane32_swap(__float_as_uint(v01), __float_as_uint(v23), false, false)[0]);
+      const int64_t col = frag_col(grp * SC_GROUP + u0) + lane;
+      const float v_out = (col < ncols && col < nv) ? s64 : -__builtin_huge_valf();
       const float m_out = score_max8(v_out);
-      // lanes 0-15 own the scores, lanes 0 and 8 the block maxima; other
-      // lanes (and a missing output) store out of range, which is dropped
-      const uint32_t vo_s = (lane < 16 && col < ncols) ? (uint32_t)col * 4u : OOB;
-      const uint32_t vo_b = (lane < 16 && (lane & 7) == 0 && (col >> 3) < nblk) ? (uint32_t)(col >> 3) * 4u : OOB;
+      // lanes 0, 8, .. own the block maxima; a missing output stores out of
+      // range, which is dropped
+      const uint32_t vo_s = col < ncols ? (uint32_t)col * 4u : OOB;
+      const uint32_t vo_b = ((lane & 7) == 0 && (col >> 3) < nblk) ? (uint32_t)(col >> 3) * 4u : OOB;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v_out), srs, vo_s, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_out), brs, vo_b, 0, 0);
     }
