@@ -92,10 +92,11 @@ LayerPlan plan_layer(int32_t mode, const csa_layer_args* a) {
     // The scan can also write every score, so that the fused selection
     // gathers the chosen blocks' scores instead of rescoring their 512 KiB
     // of keys per query.  Small decode batches: one block per query
-    // rescoring is ~17 us of latency, but the score stores are 64-byte
-    // pieces that cost the HBM-bound decode scan far more than their bytes
-    // (32 x 1M entries: +28 us against -12 us of selection; 64 x 128K: -9 us
-    // per step), so only batches with at most 2^22 scores take this path.
+    // rescoring is ~17 us of latency, but writing the scores beside the
+    // HBM-bound decode scan costs it more than their bytes (32 x 1M entries,
+    // 32 MiB of scores in whole 256-byte stores: step 0.365 against 0.349 ms
+    // with the rescoring; 64 x 128K: -9 us per step), so only batches with at
+    // most 2^22 scores take this path.
     // Prefill chunks: the MFMA-bound tile scan absorbs the stores, and the
     // rescoring re-reads 512 KiB of keys per query (2,048 queries at 32K:
     // step 0.352 -> 0.303 ms; 4,096 at 256K, 1.1 GB of scores: 2.918 ->
