@@ -64,8 +64,7 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
   if (lane < 2 * NFRAG && c_wave + 8 * lane < ncols)
     my_blk = a.pool[q * a.n_pool_blocks + ((c_wave + 8 * lane) >> 3)];
   // Half i = one pool block of 8 columns.  Lane i keeps the number of its
-  // visible entries (cnt) and the block to read (row 0's block when it has
-  // none, so every load reads existing rows); every half reads them back as
+  // visible entries (cnt) and its block; every half reads them back as
   // wave-uniform values.  32-bit: entries < 2^30.
   // (a block id outside the visible entries, or a bogus one from the caller,
   // has no visible entry; the test comes before the multiply, so 8 * id
@@ -77,21 +76,19 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
   const int my_blkc = my_cnt > 0 ? my_blk : 0;
   // one word per half (block id < 2^27 above the count), one readlane each
   const int my_pack = (my_blkc << 4) | my_cnt;
-  struct Half { int cnt; const uint8_t* base; };
   auto half_cnt = [&](int i) { return __builtin_amdgcn_readlane(my_pack, i) & 15; };
-  auto half_info = [&](int i) {
+  // a buffer view of half i's visible rows (built on the scalar unit): rows
+  // at or past the count read past the view and get zeros, so the lane's
+  // offset needs no per-half selection and no 64-bit address
+  auto half_view = [&](int i) {
     const int pk = __builtin_amdgcn_readlane(my_pack, i);
-    Half hf;
-    hf.cnt = pk & 15;
-    hf.base = kbase + (int64_t)(pk >> 4) * (8 * ID);
-    return hf;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)(pk >> 4) * (8 * ID)), (short)0,
+                                             (pk & 15) * ID, 0x00020000);
   };
   // lane's byte offsets inside a half: row lane / 8, whole-line chunk of half h
-  // (row 0 when that row is not a visible entry)
   const int lrow_k = lane >> 3;
   const uint32_t off_row[2] = {(uint32_t)(lrow_k * ID + 16 * stage_chunk(lane, 0)),
                                (uint32_t)(lrow_k * ID + 16 * stage_chunk(lane, 1))};
-  const uint32_t off_zero[2] = {(uint32_t)(16 * stage_chunk(lane, 0)), (uint32_t)(16 * stage_chunk(lane, 1))};
   // half h of fragment f: one whole-line load of 8 rows (lane / 8 picks the row)
   auto load_group = [&](int grp, uint4 (&v)[SQ_UNROLL][2]) {
 #pragma unroll
@@ -99,8 +96,8 @@ __global__ __launch_bounds__(256) void score_pool_kernel(ScoreArgs a, int64_t nc
       const int f = grp * SQ_UNROLL + u;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const Half hf = half_info(2 * f + h);
-        v[u][h] = load16<false>(hf.base + (lrow_k < hf.cnt ? off_row[h] : off_zero[h]));
+        const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(half_view(2 * f + h), off_row[h], 0, 0);
+        v[u][h] = make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
       }
     }
   };
