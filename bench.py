@@ -197,13 +197,11 @@ def dense_score_call(wl, st, write_scores=True):
             ops._p(t["k_fp8"]), t["k_fp8"].shape[1], nc, None, 0,
             None if scores is None else ops._p(scores), None if bm is None else ops._p(bm))
 
-    outs = (scores, bm)   # held by fn: the launches write them
-
     def fn():
-        assert outs is not None
         rc = lib.csa_index_score(*args, ops._stream())
         if rc:
             raise RuntimeError(lib.csa_last_error().decode())
+    fn.outputs = (scores, bm)   # the launches write them: they live as long as fn
     out_bytes = (0 if scores is None else Q * nc * 4) + (0 if bm is None else Q * nblk * 4)
     return fn, out_bytes
 
