@@ -207,10 +207,18 @@ __global__ __launch_bounds__(256) void score_scan_kernel(ScoreArgs a, int64_t nc
   const int64_t n_chunks = (ncols + SQ_COLS - 1) / SQ_COLS;
   const int64_t my_chunks = blockIdx.x < n_chunks ? (n_chunks - 1 - blockIdx.x) / gridDim.x + 1 : 0;
   const int n_groups = (int)(my_chunks * (NFRAG / SC_GROUP));
-  // first column of fragment g of this wave's stream
+  // first column of fragment g of this wave's stream.  With 8-fragment
+  // groups (several chunks per block) each wave reads its own quarter of the
+  // chunk; with 4-fragment groups (one chunk per block) the four waves take
+  // the chunk's 64-column groups in turn, so the block's loads in flight sit
+  // side by side (1-2 % faster there, ~1 % slower with 8-fragment groups).
   auto frag_col = [&](int g) {
     const int64_t chunk = blockIdx.x + (int64_t)gridDim.x * (g / NFRAG);
-    return chunk * SQ_COLS + wave * (SQ_COLS / 4) + 16 * (g % NFRAG);
+    const int gi = g % NFRAG;
+    if constexpr (SC_GROUP == 4)
+      return chunk * SQ_COLS + ((gi / SC_GROUP) * 4 + wave) * (SC_GROUP * 16) + 16 * (gi % SC_GROUP);
+    else
+      return chunk * SQ_COLS + wave * (SQ_COLS / 4) + 16 * gi;
   };
   auto load_group = [&](int grp, uint4 (&v)[SC_GROUP][2]) {
 #pragma unroll
