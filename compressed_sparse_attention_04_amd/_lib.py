@@ -30,7 +30,7 @@ class CsaLayerArgs(ctypes.Structure):
         ("q_pos", c_void_p), ("q_attn", c_void_p), ("q_idx", c_void_p), ("w_idx", c_void_p),
         ("sm_scale", c_f32), ("top_k", c_i32), ("build_pool", c_i32), ("n_pool_blocks", c_i32),
         ("pool_blocks", c_void_p), ("idx", c_void_p), ("out", c_void_p),
-        ("ws", c_void_p), ("ws_bytes", c_size),
+        ("ws", c_void_p), ("ws_bytes", c_size), ("attn_after", c_void_p),
     ]
 
 

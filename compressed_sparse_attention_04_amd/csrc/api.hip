@@ -530,6 +530,10 @@ static csa_status check_layer(const char* fn, int32_t mode, const csa_layer_args
 }
 
 static csa_status run_attention(const char* fn, const csa_layer_args* a, const LayerPlan& p, hipStream_t st) {
+  if (a->attn_after) {
+    csa_status r = hip_status(hipStreamWaitEvent(st, a->attn_after, 0), fn);
+    if (r != CSA_OK) return r;
+  }
   void* aws = reinterpret_cast<char*>(a->ws) + p.off_attn;
   return hip_status(launch_sparse_attn(a->q_attn, a->q_pos, a->n_seq, a->q_per_seq, a->codes, a->scales,
                                        a->kv_rows, a->idx, a->top_k, a->win, a->win_cap, a->sm_scale,

@@ -455,6 +455,13 @@ class LayerCall:
         self.args.ws = None if ws is None else ws.data_ptr()
         self.args.ws_bytes = 0 if ws is None else ws.numel()
 
+    def set_attn_after(self, event):
+        """Make the layer's attention (not its scoring and selection) wait for
+        ``event`` (a torch.cuda.Event recorded on another stream), or for
+        nothing with None.  The event object is kept alive with the call."""
+        self.attn_event = event
+        self.args.attn_after = None if event is None else ctypes.c_void_p(event.cuda_event)
+
     def __call__(self, stream=None):
         name = {MODE_FULL: "csa_layer_full", MODE_REINDEX: "csa_layer_reindex",
                 MODE_REUSE: "csa_layer_reuse"}[self.mode]

@@ -359,6 +359,13 @@ csa_status csa_sparse_attn_noalloc(const float* q, const int32_t* q_pos, int64_t
  *   All three then run csa_sparse_attn with q_attn -> out.
  * Field meanings follow the entry points above.  Workspace:
  *   csa_layer_workspace_size(mode, args) with mode CSA_MODE_*.
+ * attn_after (optional, NULL for none): an event the layer's attention waits
+ *   for on `stream` (hipStreamWaitEvent) before it starts; the scoring and
+ *   selection do not wait.  A step uses it to compress and store its new
+ *   entries on a second stream while the Full layer scores and selects, since
+ *   only the attention reads the cache rows and window that the compression
+ *   writes ("DeepSeek-V4.1 架构解析" §02, §03).  The event is not owned by the
+ *   library; an error from the wait is returned as CSA_ERR_HIP.
  */
 enum { CSA_MODE_FULL = 0, CSA_MODE_REINDEX = 1, CSA_MODE_REUSE = 2 };
 
@@ -389,6 +396,7 @@ typedef struct csa_layer_args {
   float* out;              /* [Q, 16, 512] */
   void* ws;
   size_t ws_bytes;
+  hipEvent_t attn_after;   /* optional: the attention waits for this event */
 } csa_layer_args;
 
 size_t csa_layer_workspace_size(int32_t mode, const csa_layer_args* a);
