@@ -458,7 +458,10 @@ class LayerCall:
     def set_attn_after(self, event):
         """Make the layer's attention (not its scoring and selection) wait for
         ``event`` (a torch.cuda.Event recorded on another stream), or for
-        nothing with None.  The event object is kept alive with the call."""
+        nothing with None.  The event object is kept alive with the call.  An
+        event gets its HIP handle when first recorded, so record it first."""
+        if event is not None and not event.cuda_event:
+            raise ValueError("attn_after: record the event before passing it")
         self.attn_event = event
         self.args.attn_after = None if event is None else ctypes.c_void_p(event.cuda_event)
 
