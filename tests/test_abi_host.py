@@ -187,3 +187,17 @@ def test_window_rebuild_validation(lib):
     assert f(P + 4, 2, 128, 128 * 512, P, P, 128, None) == ALIGN       # x not 16-byte aligned
     assert f(None, 2, 128, 128 * 512, P, P, 128, None) != 0            # null pointer
     assert f(P, 0, 128, 128 * 512, P, P, 128, None) == 0               # nothing to do
+
+
+def test_attn_after_needs_a_recorded_event():
+    """An unrecorded torch event has no HIP handle yet; passing it would make
+    the layer's attention wait for nothing, so the binding refuses it."""
+    import torch
+    from compressed_sparse_attention_04_amd import ops
+
+    call = ops.LayerCall.__new__(ops.LayerCall)
+    call.args = _lib.CsaLayerArgs()
+    with pytest.raises(ValueError):
+        call.set_attn_after(torch.cuda.Event())
+    call.set_attn_after(None)
+    assert call.args.attn_after is None
