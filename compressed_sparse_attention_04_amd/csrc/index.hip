@@ -177,8 +177,11 @@ constexpr int SC_BLOCKS = 2048;   // ~four rounds of two 4-wave blocks per CU (2
 
 // SC_GROUP: 8 fragments when a block streams several chunks (4 measured 2%
 // slower there: fewer bytes in flight per wave), 4 when it has one chunk
-// (two groups of 8 would leave nothing to overlap).
-template <int SC_GROUP>
+// (two groups of 8 would leave nothing to overlap).  COLS: the chunk; a scan
+// too small to give 256 blocks of 1,024 columns (one short sequence) takes
+// chunks of 256 columns instead, one group per wave, so its blocks do not
+// run four groups one after another.
+template <int SC_GROUP, int COLS = SQ_COLS>
 __global__ __launch_bounds__(256) void score_scan_kernel(ScoreArgs a, int64_t ncols) {
   __shared__ uint4 stage_all[4][128];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(256) void score_scan_kernel(ScoreArgs a, int64_t nc
   for (int r = 0; r < 4; ++r) w4[r] = (lane < 32) ? a.w[q * IH + 4 * (lane >> 4) + r] : 0.f;
   const uint8_t* kbase = a.k_fp8 + seq * a.k_rows * ID;
   const int64_t nblk = (ncols + 7) >> 3;
-  constexpr int NFRAG = SQ_COLS / 4 / 16;   // fragments of a wave per chunk
+  constexpr int NFRAG = COLS / 4 / 16;   // fragments of a wave per chunk
   // outputs through buffer stores: no branch around a store, so the compiler
   // can count the memory operations in flight (stores count with the loads)
   constexpr uint32_t OOB = 0x80000000u;
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(256) void score_scan_kernel(ScoreArgs a, int64_t nc
   const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
       a.block_max ? (void*)(a.block_max + q * nblk) : (void*)any_out, (short)0, a.block_max ? (int)(nblk * 4) : 0,
       0x00020000);
-  const int64_t n_chunks = (ncols + SQ_COLS - 1) / SQ_COLS;
+  const int64_t n_chunks = (ncols + COLS - 1) / COLS;
   const int64_t my_chunks = blockIdx.x < n_chunks ? (n_chunks - 1 - blockIdx.x) / gridDim.x + 1 : 0;
   const int n_groups = (int)(my_chunks * (NFRAG / SC_GROUP));
   // first column of fragment g of this wave's stream.  With 8-fragment
@@ -216,9 +219,9 @@ __global__ __launch_bounds__(256) void score_scan_kernel(ScoreArgs a, int64_t nc
     const int64_t chunk = blockIdx.x + (int64_t)gridDim.x * (g / NFRAG);
     const int gi = g % NFRAG;
     if constexpr (SC_GROUP == 4)
-      return chunk * SQ_COLS + ((gi / SC_GROUP) * 4 + wave) * (SC_GROUP * 16) + 16 * (gi % SC_GROUP);
+      return chunk * COLS + ((gi / SC_GROUP) * 4 + wave) * (SC_GROUP * 16) + 16 * (gi % SC_GROUP);
     else
-      return chunk * SQ_COLS + wave * (SQ_COLS / 4) + 16 * gi;
+      return chunk * COLS + wave * (COLS / 4) + 16 * gi;
   };
   auto load_group = [&](int grp, uint4 (&v)[SC_GROUP][2]) {
 #pragma unroll
@@ -492,8 +495,15 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t st) {
     per_q = (n_chunks + chunks_per_block - 1) / chunks_per_block;
     dim3 grid((unsigned)per_q, (unsigned)Q);
     if (ncols >= ((int64_t)1 << 29)) return hipErrorInvalidValue;   // 32-bit buffer offsets
-    if (chunks_per_block >= 2) hipLaunchKernelGGL(score_scan_kernel<8>, grid, dim3(256), 0, st, a, ncols);
-    else hipLaunchKernelGGL(score_scan_kernel<4>, grid, dim3(256), 0, st, a, ncols);
+    if (Q * n_chunks < 256) {
+      constexpr int SMALL = 256;
+      const dim3 g2((unsigned)((ncols + SMALL - 1) / SMALL), (unsigned)Q);
+      hipLaunchKernelGGL((score_scan_kernel<4, SMALL>), g2, dim3(256), 0, st, a, ncols);
+    } else if (chunks_per_block >= 2) {
+      hipLaunchKernelGGL(score_scan_kernel<8>, grid, dim3(256), 0, st, a, ncols);
+    } else {
+      hipLaunchKernelGGL(score_scan_kernel<4>, grid, dim3(256), 0, st, a, ncols);
+    }
   }
   return hipGetLastError();
 }
